@@ -1,0 +1,720 @@
+/*
+ * hq_oracle.c -- plain, slow CPU reference of the HyperQuant per-tile codec.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the package smoke check and
+ * the benchmark's CPU-baseline leg; never by the product path.  It shares no
+ * code with the HIP library.  Source citations use the short names defined in
+ * hq_oracle.h ([HQ-explainer], [HQ-abstract], [Philox], [SPLAG]).
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no -ffast-math, no -march):
+ * every fp32 operation below is one IEEE-754 binary32 operation rounded to
+ * nearest-even, in the order written.  Where floating point decides an integer
+ * (a lattice code), the HIP path takes the same decision in the same precision
+ * and order, which is what makes codes and bitstreams comparable bit for bit.
+ */
+#include "hq_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define N 128                 /* tile length [HQ-explainer, Methodology 1] */
+#define KMAX 22               /* largest Rice parameter (reading: |u| < 2^20) */
+#define RANGE_LIMIT 1048576.0f /* 2^20: codes stay below 2^21 */
+#define M_LIMIT (1u << 22)    /* largest zigzag symbol a valid stream holds */
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x32-10 [Philox]: ten rounds of two 32x32->64 multiplies with the   */
+/* published multipliers, the key bumped by the published Weyl constants.    */
+/* ------------------------------------------------------------------------ */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    uint64_t p0 = (uint64_t)M0 * c0;
+    uint64_t p1 = (uint64_t)M1 * c2;
+    uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    k0 += W0; k1 += W1;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Counter tags (reading): the sign vector uses counter (0,0,0,"SIGN"); the
+ * dither block j of tile id T uses counter (j, lo32(T), hi32(T), "DITH"). */
+#define TAG_SIGN 0x5349474Eu
+#define TAG_DITH 0x44495448u
+
+/* D of RHT_n(x) = H_n D x [HQ-explainer, Methodology 1]: one random sign per
+ * coordinate, shared by every tile of a plan (reading: the "cheap +-1 sign
+ * diagonal" per-layer rotation of Methodology 4 is this D). */
+void orc_signs(uint64_t seed, float s[128]) {
+  uint32_t ctr[4] = {0u, 0u, 0u, TAG_SIGN};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t r[4];
+  orc_philox4x32_10(ctr, key, r);
+  for (int i = 0; i < N; ++i) s[i] = ((r[i >> 5] >> (i & 31)) & 1u) ? -1.0f : 1.0f;
+}
+
+/* H_n of Methodology 1: the Walsh-Hadamard matrix in Sylvester order,
+ * applied by the textbook butterfly, smallest stride first. */
+void orc_fwht128(float v[128]) {
+  for (int h = 1; h < N; h <<= 1) {
+    for (int i = 0; i < N; ++i) {
+      if (i & h) continue;
+      float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+}
+
+/* The orthonormal scale 1/sqrt(n) and the lattice scale alpha of
+ * Methodology 2 ("integer implementation ... scale alpha") are folded into one
+ * fp32 constant each way, computed in double and rounded once. */
+void orc_scales(float alpha, float *c_enc, float *c_dec) {
+  *c_enc = (float)(1.0 / ((double)alpha * sqrt(128.0)));
+  *c_dec = (float)((double)alpha / sqrt(128.0));
+}
+
+void orc_rht_forward(const float x[128], const float s[128], float c_enc, float u[128]) {
+  float v[N];
+  for (int i = 0; i < N; ++i) v[i] = s[i] * x[i];
+  orc_fwht128(v);
+  for (int i = 0; i < N; ++i) u[i] = v[i] * c_enc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Nearest points [HQ-explainer, Methodology 2; SPLAG ch. 20]               */
+/* Integer embeddings (reading): Z; D4 = {x in Z^4 : sum even};             */
+/* E8 as 2E8 = {x in Z^8 : all x_i of one parity, sum = 0 mod 4}            */
+/* (the E^8_int subset Z^8 of Methodology 2); A2 as the checkerboard        */
+/* {(i,j) : i = j mod 2} whose real point is (i, j*sqrt3).                  */
+/* ------------------------------------------------------------------------ */
+static const float S3 = 1.7320508075688772f;        /* fp32(sqrt 3) */
+static const float K3 = 0.28867513459481287f;       /* fp32(1/(2 sqrt 3)) */
+
+static int lat_dim(int lat) {
+  switch (lat) {
+    case ORC_Z: return 1;
+    case ORC_A2: return 2;
+    case ORC_D4: return 4;
+    case ORC_E8: return 8;
+    default: return 0;
+  }
+}
+
+static void nearest_z(const float *u, int32_t *x) { x[0] = (int32_t)rintf(u[0]); }
+
+/* D4: round every coordinate; if the sum is odd, re-round the coordinate with
+ * the largest rounding error (first such index) the other way. */
+static void nearest_d4(const float *u, int32_t *x) {
+  float f[4];
+  int32_t sum = 0;
+  for (int i = 0; i < 4; ++i) { f[i] = rintf(u[i]); sum += (int32_t)f[i]; }
+  if (sum & 1) {
+    int j = 0;
+    float worst = fabsf(u[0] - f[0]);
+    for (int i = 1; i < 4; ++i) {
+      float e = fabsf(u[i] - f[i]);
+      if (e > worst) { worst = e; j = i; }
+    }
+    f[j] += (u[j] - f[j] >= 0.0f) ? 1.0f : -1.0f;
+  }
+  for (int i = 0; i < 4; ++i) x[i] = (int32_t)f[i];
+}
+
+/* 2E8 = 2D8 u (2D8 + 1).  Even candidate: nearest even integers e_i, parity
+ * fixed on the coordinate with the largest |u_i - e_i|.  Odd candidate:
+ * nearest odd integers o_i, parity fixed on the coordinate with the largest
+ * |u_i - o_i| = 1 - |u_i - e_i|, i.e. the smallest a_i.  With a_i = |u_i - e_i|
+ * (exact in fp32) the squared distances satisfy
+ *   (D_even - D_odd)/2 = (sum a_i - 4) + [even fix] 2(1 - max a) - [odd fix] 2 min a,
+ * which is evaluated in fp32 in exactly this order; even wins ties. */
+static void nearest_e8(const float *u, int32_t *x) {
+  float ye[8], yo[8], a[8];
+  int32_t sye = 0, syo = 0;
+  for (int i = 0; i < 8; ++i) {
+    float h = u[i] * 0.5f;
+    ye[i] = rintf(h);
+    yo[i] = floorf(h);
+    a[i] = fabsf(u[i] - 2.0f * ye[i]);
+    sye += (int32_t)ye[i];
+    syo += (int32_t)yo[i];
+  }
+  float S = a[0];
+  for (int i = 1; i < 8; ++i) S = S + a[i];
+  int jmax = 0, jmin = 0;
+  for (int i = 1; i < 8; ++i) {
+    if (a[i] > a[jmax]) jmax = i;
+    if (a[i] < a[jmin]) jmin = i;
+  }
+  int pe = sye & 1, po = syo & 1;
+  float delta = S - 4.0f;
+  if (pe) delta = delta + 2.0f * (1.0f - a[jmax]);
+  if (po) delta = delta - 2.0f * a[jmin];
+  int32_t c[8];
+  if (delta <= 0.0f) {
+    for (int i = 0; i < 8; ++i) c[i] = 2 * (int32_t)ye[i];
+    if (pe) c[jmax] += (u[jmax] - (float)c[jmax] >= 0.0f) ? 2 : -2;
+  } else {
+    for (int i = 0; i < 8; ++i) c[i] = 2 * (int32_t)yo[i] + 1;
+    if (po) c[jmin] += (u[jmin] - (float)c[jmin] >= 0.0f) ? 2 : -2;
+  }
+  for (int i = 0; i < 8; ++i) x[i] = c[i];
+}
+
+/* A2: the real lattice {(i, j sqrt3) : i = j mod 2} is the union of two
+ * rectangular cosets, rounded independently; the closer one wins (ties even). */
+static float a2_dist(const float *u, int32_t i, int32_t j) {
+  float e0 = u[0] - (float)i;
+  float t = (float)j * S3;
+  float e1 = u[1] - t;
+  return e0 * e0 + e1 * e1;
+}
+
+static void nearest_a2(const float *u, int32_t *x) {
+  float w0 = u[0] * 0.5f, w1 = u[1] * K3;
+  int32_t ie = 2 * (int32_t)rintf(w0), je = 2 * (int32_t)rintf(w1);
+  int32_t io = 2 * (int32_t)floorf(w0) + 1, jo = 2 * (int32_t)floorf(w1) + 1;
+  float de = a2_dist(u, ie, je), dd = a2_dist(u, io, jo);
+  if (de <= dd) { x[0] = ie; x[1] = je; }
+  else { x[0] = io; x[1] = jo; }
+}
+
+void orc_nearest(int lat, const float *u, int32_t *x) {
+  switch (lat) {
+    case ORC_Z: nearest_z(u, x); break;
+    case ORC_A2: nearest_a2(u, x); break;
+    case ORC_D4: nearest_d4(u, x); break;
+    case ORC_E8: nearest_e8(u, x); break;
+    default: break;
+  }
+}
+
+void orc_nearest_many(int lat, uint64_t n_vectors, const float *u, int32_t *x) {
+  int d = lat_dim(lat);
+  for (uint64_t r = 0; r < n_vectors; ++r) orc_nearest(lat, &u[r * (uint64_t)d], &x[r * (uint64_t)d]);
+}
+
+void orc_embed(int lat, const int32_t *x, float *p) {
+  int d = lat_dim(lat);
+  if (lat == ORC_A2) {
+    p[0] = (float)x[0];
+    p[1] = (float)x[1] * S3;
+    return;
+  }
+  for (int i = 0; i < d; ++i) p[i] = (float)x[i];
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bit-stripping [HQ-explainer, Methodology 3]: the membership constraints   */
+/* fix log2(index) bits of every code vector; they are removed before        */
+/* coding.  E8: the common parity b (kept as one raw bit), then the halves   */
+/* y_i = (x_i - b)/2 whose sum is even, so y_7's low bit is dropped.  D4:    */
+/* x_3's low bit equals the parity of x_0+x_1+x_2.  A2: i's low bit equals   */
+/* j's; i (real step 2 once stripped) and j (real step sqrt3) then have      */
+/* nearly equal spread, so one Rice parameter fits both.  (Shifts below are  */
+/* arithmetic, i.e. floor division.)                                         */
+/* ------------------------------------------------------------------------ */
+void orc_strip(int lat, const int32_t *x, int32_t *sym, int *raw_bit) {
+  *raw_bit = 0;
+  switch (lat) {
+    case ORC_Z: sym[0] = x[0]; break;
+    case ORC_A2: sym[0] = (x[0] - (x[1] & 1)) >> 1; sym[1] = x[1]; break;
+    case ORC_D4: {
+      int32_t p = (x[0] + x[1] + x[2]) & 1;
+      sym[0] = x[0]; sym[1] = x[1]; sym[2] = x[2];
+      sym[3] = (x[3] - p) >> 1;
+      break;
+    }
+    case ORC_E8: {
+      int32_t b = x[0] & 1, y[8], p = 0;
+      for (int i = 0; i < 8; ++i) y[i] = (x[i] - b) >> 1;
+      for (int i = 0; i < 7; ++i) p += y[i];
+      p &= 1;
+      for (int i = 0; i < 7; ++i) sym[i] = y[i];
+      sym[7] = (y[7] - p) >> 1;
+      *raw_bit = b;
+      break;
+    }
+    default: break;
+  }
+}
+
+void orc_unstrip(int lat, const int32_t *sym, int raw_bit, int32_t *x) {
+  switch (lat) {
+    case ORC_Z: x[0] = sym[0]; break;
+    case ORC_A2: x[0] = 2 * sym[0] + (sym[1] & 1); x[1] = sym[1]; break;
+    case ORC_D4: {
+      int32_t p = (sym[0] + sym[1] + sym[2]) & 1;
+      x[0] = sym[0]; x[1] = sym[1]; x[2] = sym[2];
+      x[3] = 2 * sym[3] + p;
+      break;
+    }
+    case ORC_E8: {
+      int32_t y[8], p = 0;
+      for (int i = 0; i < 7; ++i) { y[i] = sym[i]; p += sym[i]; }
+      p &= 1;
+      y[7] = 2 * sym[7] + p;
+      for (int i = 0; i < 8; ++i) x[i] = 2 * y[i] + raw_bit;
+      break;
+    }
+    default: break;
+  }
+}
+
+/* Signed to unsigned for Rice coding (reading: zigzag). */
+uint32_t orc_zigzag(int32_t v) { return v >= 0 ? 2u * (uint32_t)v : 2u * (uint32_t)(-(int64_t)v) - 1u; }
+int32_t orc_unzigzag(uint32_t m) { return (m & 1u) ? -(int32_t)((m + 1u) >> 1) : (int32_t)(m >> 1); }
+
+/* Rice coding [HQ-explainer, Methodology 3]: symbol m costs a k-bit remainder
+ * plus a unary quotient (m >> k zeros and a terminating one).  One k per tile,
+ * the smallest minimiser of the tile length (reading). */
+uint64_t orc_rice_len(const uint32_t m[128], int k, int raw_bits) {
+  uint64_t L = (uint64_t)raw_bits + (uint64_t)N * (uint64_t)(1 + k);
+  for (int i = 0; i < N; ++i) L += (uint64_t)(m[i] >> k);
+  return L;
+}
+
+int orc_rice_kstar(const uint32_t m[128], int raw_bits) {
+  int best = 0;
+  uint64_t bestL = orc_rice_len(m, 0, raw_bits);
+  for (int k = 1; k <= KMAX; ++k) {
+    uint64_t L = orc_rice_len(m, k, raw_bits);
+    if (L < bestL) { bestL = L; best = k; }
+  }
+  return best;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Subtractive dither [HQ-explainer, Methodology 4]: U ~ Uniform(V(Lambda)). */
+/* Construction (reading): tau uniform over one period of an integer         */
+/* sublattice (4Z^8 in 2E8, 2Z^4 in D4, 2Z x 2sqrt3 Z in A2, Z), then        */
+/* d = tau - Q(tau), which is uniform over the Voronoi cell.  Uniforms are   */
+/* 24-bit: f = (r >> 8) * 2^-24 from Philox block j = coordinate / 4.        */
+/* ------------------------------------------------------------------------ */
+void orc_dither(int lat, uint64_t seed, uint64_t tile_id, float d[128]) {
+  float f[N];
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  for (uint32_t j = 0; j < N / 4; ++j) {
+    uint32_t ctr[4] = {j, (uint32_t)tile_id, (uint32_t)(tile_id >> 32), TAG_DITH};
+    uint32_t r[4];
+    orc_philox4x32_10(ctr, key, r);
+    for (int c = 0; c < 4; ++c) f[4 * j + c] = (float)(r[c] >> 8) * 0x1p-24f;
+  }
+  int dim = lat_dim(lat);
+  for (int v = 0; v < N / dim; ++v) {
+    float tau[8], p[8];
+    int32_t q[8];
+    for (int c = 0; c < dim; ++c) {
+      float fv = f[v * dim + c];
+      switch (lat) {
+        case ORC_Z: tau[c] = fv; break;
+        case ORC_D4: tau[c] = 2.0f * fv; break;
+        case ORC_E8: tau[c] = 4.0f * fv; break;
+        case ORC_A2: tau[c] = (c == 0) ? 2.0f * fv : fv * (2.0f * S3); break;
+        default: tau[c] = 0.0f; break;
+      }
+    }
+    orc_nearest(lat, tau, q);
+    orc_embed(lat, q, p);
+    for (int c = 0; c < dim; ++c) d[v * dim + c] = tau[c] - p[c];
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tile quantiser: RHT -> (dither) -> nearest point, range-checked.          */
+/* ------------------------------------------------------------------------ */
+static float load_elem(const void *x, int dtype, uint64_t i) {
+  if (dtype == ORC_BF16) {
+    uint32_t b = (uint32_t)((const uint16_t *)x)[i] << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return f;
+  }
+  return ((const float *)x)[i];
+}
+
+static int quantize_tile_s(int lat, uint64_t seed, const float s[128], float c_enc,
+                           const float x[128], int dithered, uint64_t tile_id,
+                           int32_t codes[128]) {
+  for (int i = 0; i < N; ++i)
+    if (!isfinite(x[i])) return ORC_ERR_NONFINITE;
+  float u[N];
+  orc_rht_forward(x, s, c_enc, u);
+  if (dithered) {
+    float d[N];
+    orc_dither(lat, seed, tile_id, d);
+    for (int i = 0; i < N; ++i) u[i] = u[i] + d[i];
+  }
+  for (int i = 0; i < N; ++i)
+    if (!(fabsf(u[i]) < RANGE_LIMIT)) return ORC_ERR_RANGE;
+  int dim = lat_dim(lat);
+  for (int v = 0; v < N / dim; ++v) orc_nearest(lat, &u[v * dim], &codes[v * dim]);
+  return ORC_OK;
+}
+
+int orc_quantize_tile(int lat, uint64_t seed, float alpha, const float x[128],
+                      int dithered, uint64_t tile_id, int32_t codes[128]) {
+  if (lat_dim(lat) == 0 || !(alpha > 0.0f) || !isfinite(alpha)) return ORC_ERR_ARG;
+  float s[N], c_enc, c_dec;
+  orc_signs(seed, s);
+  orc_scales(alpha, &c_enc, &c_dec);
+  return quantize_tile_s(lat, seed, s, c_enc, x, dithered, tile_id, codes);
+}
+
+/* Codes of a tile -> zigzag symbols (vector-major) and raw bits. */
+static int tile_symbols(int lat, const int32_t codes[128], uint32_t m[128], uint32_t *raw) {
+  int dim = lat_dim(lat);
+  *raw = 0;
+  for (int v = 0; v < N / dim; ++v) {
+    int32_t sym[8];
+    int rb;
+    orc_strip(lat, &codes[v * dim], sym, &rb);
+    for (int c = 0; c < dim; ++c) m[v * dim + c] = orc_zigzag(sym[c]);
+    if (lat == ORC_E8) *raw |= (uint32_t)rb << v;
+  }
+  return lat == ORC_E8 ? 16 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stream layout (reading; parity unpinned by the pages):                    */
+/*   record of tile t at bits [off[t], off[t+1]):                            */
+/*     [raw bits (E8: bit v = coset bit of vector v)]                        */
+/*     [128 remainders of k bits, symbol order, each LSB first]              */
+/*     [128 unary quotients: q zeros then a one, symbol order]               */
+/*   stream bit P is bit (P & 31) of uint32 word P >> 5; records abut.       */
+/* ------------------------------------------------------------------------ */
+static void put_bit(uint32_t *w, uint64_t pos) { w[pos >> 5] |= 1u << (pos & 31); }
+static int get_bit(const uint32_t *w, uint64_t pos) { return (int)((w[pos >> 5] >> (pos & 31)) & 1u); }
+
+static void write_record(uint32_t *words, uint64_t off, int raw_bits, uint32_t raw,
+                         const uint32_t m[128], int k) {
+  uint64_t p = off;
+  for (int b = 0; b < raw_bits; ++b, ++p)
+    if ((raw >> b) & 1u) put_bit(words, p);
+  for (int i = 0; i < N; ++i)
+    for (int b = 0; b < k; ++b, ++p)
+      if ((m[i] >> b) & 1u) put_bit(words, p);
+  for (int i = 0; i < N; ++i) {
+    p += m[i] >> k;
+    put_bit(words, p);
+    ++p;
+  }
+}
+
+uint64_t orc_write_record_codes(int lat, const int32_t codes[128], uint32_t *words,
+                                uint64_t off, int *k_out) {
+  uint32_t m[N], raw;
+  int raw_bits = tile_symbols(lat, codes, m, &raw);
+  int kt = orc_rice_kstar(m, raw_bits);
+  write_record(words, off, raw_bits, raw, m, kt);
+  *k_out = kt;
+  return orc_rice_len(m, kt, raw_bits);
+}
+
+int orc_encode(int lat, uint64_t seed, float alpha, const void *x, int dtype,
+               uint64_t n_tiles, int dithered, uint64_t tile_base,
+               uint32_t *words, uint64_t cap_words, uint64_t *offsets, uint8_t *k) {
+  if (lat_dim(lat) == 0 || !(alpha > 0.0f) || !isfinite(alpha)) return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
+  float s[N], c_enc, c_dec;
+  orc_signs(seed, s);
+  orc_scales(alpha, &c_enc, &c_dec);
+  int status = ORC_OK;
+  uint64_t off = 0, zeroed = 0; /* words [0, zeroed) have been cleared */
+  offsets[0] = 0;
+  for (uint64_t t = 0; t < n_tiles; ++t) {
+    float xt[N];
+    int32_t codes[N];
+    uint32_t m[N], raw;
+    for (int i = 0; i < N; ++i) xt[i] = load_elem(x, dtype, t * N + (uint64_t)i);
+    int st = quantize_tile_s(lat, seed, s, c_enc, xt, dithered, tile_base + t, codes);
+    if (st != ORC_OK) return st;
+    int raw_bits = tile_symbols(lat, codes, m, &raw);
+    int kt = orc_rice_kstar(m, raw_bits);
+    uint64_t L = orc_rice_len(m, kt, raw_bits);
+    k[t] = (uint8_t)kt;
+    uint64_t end = off + L;
+    if (status == ORC_OK && (end + 31) / 32 <= cap_words) {
+      uint64_t wend = (end + 31) / 32;
+      for (; zeroed < wend; ++zeroed) words[zeroed] = 0u;
+      write_record(words, off, raw_bits, raw, m, kt);
+    } else {
+      status = ORC_ERR_CAPACITY;
+    }
+    off = end;
+    offsets[t + 1] = off;
+  }
+  return status;
+}
+
+int orc_total_bits(int lat, uint64_t seed, float alpha, const void *x, int dtype,
+                   uint64_t n_tiles, int dithered, uint64_t tile_base, uint64_t *bits) {
+  if (lat_dim(lat) == 0 || !(alpha > 0.0f) || !isfinite(alpha)) return ORC_ERR_ARG;
+  float s[N], c_enc, c_dec;
+  orc_signs(seed, s);
+  orc_scales(alpha, &c_enc, &c_dec);
+  uint64_t total = 0;
+  for (uint64_t t = 0; t < n_tiles; ++t) {
+    float xt[N];
+    int32_t codes[N];
+    uint32_t m[N], raw;
+    for (int i = 0; i < N; ++i) xt[i] = load_elem(x, dtype, t * N + (uint64_t)i);
+    int st = quantize_tile_s(lat, seed, s, c_enc, xt, dithered, tile_base + t, codes);
+    if (st != ORC_OK) return st;
+    int raw_bits = tile_symbols(lat, codes, m, &raw);
+    total += orc_rice_len(m, orc_rice_kstar(m, raw_bits), raw_bits);
+  }
+  *bits = total;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decoder: parse the record, invert strip and zigzag, dequantise, inverse   */
+/* RHT (H is symmetric with H H = nI, so the inverse is the same butterfly   */
+/* followed by c_dec and D).                                                  */
+/* A record is corrupt when k > 22, when it is longer than the longest valid */
+/* record, when its unary section holds fewer than 128 ones before the end,  */
+/* when the 128th one is not its last bit, or when a symbol reaches 2^22.    */
+/* ------------------------------------------------------------------------ */
+int orc_parse_tile(int lat, const uint32_t *words, uint64_t off, uint64_t end, int k,
+                   int32_t codes[128]) {
+  int dim = lat_dim(lat);
+  if (dim == 0) return ORC_ERR_ARG;
+  int raw_bits = lat == ORC_E8 ? 16 : 0;
+  if (k < 0 || k > KMAX) return ORC_ERR_CORRUPT;
+  if (end < off) return ORC_ERR_CORRUPT;
+  uint64_t L = end - off;
+  if (L > (uint64_t)raw_bits + (uint64_t)N * (KMAX + 1)) return ORC_ERR_CORRUPT;
+  if (L < (uint64_t)raw_bits + (uint64_t)N * (uint64_t)(k + 1)) return ORC_ERR_CORRUPT;
+  uint64_t p = off;
+  uint32_t raw = 0, m[N];
+  for (int b = 0; b < raw_bits; ++b, ++p) raw |= (uint32_t)get_bit(words, p) << b;
+  for (int i = 0; i < N; ++i) {
+    uint32_t r = 0;
+    for (int b = 0; b < k; ++b, ++p) r |= (uint32_t)get_bit(words, p) << b;
+    m[i] = r;
+  }
+  for (int i = 0; i < N; ++i) {
+    uint64_t q = 0;
+    while (p < end && !get_bit(words, p)) { ++q; ++p; }
+    if (p >= end) return ORC_ERR_CORRUPT;
+    ++p;
+    uint64_t mv = (q << k) | m[i];
+    if (mv >= M_LIMIT) return ORC_ERR_CORRUPT;
+    m[i] = (uint32_t)mv;
+  }
+  if (p != end) return ORC_ERR_CORRUPT;
+  for (int v = 0; v < N / dim; ++v) {
+    int32_t sym[8];
+    for (int c = 0; c < dim; ++c) sym[c] = orc_unzigzag(m[v * dim + c]);
+    orc_unstrip(lat, sym, lat == ORC_E8 ? (int)((raw >> v) & 1u) : 0, &codes[v * dim]);
+  }
+  return ORC_OK;
+}
+
+static void dequant_codes(int lat, uint64_t seed, const int32_t codes[128], int dithered,
+                          uint64_t tile_id, float uh[128]) {
+  int dim = lat_dim(lat);
+  for (int v = 0; v < N / dim; ++v) orc_embed(lat, &codes[v * dim], &uh[v * dim]);
+  if (dithered) {
+    float d[N];
+    orc_dither(lat, seed, tile_id, d);
+    for (int i = 0; i < N; ++i) uh[i] = uh[i] - d[i];
+  }
+}
+
+int orc_dequant_rotated(int lat, uint64_t seed, const uint32_t *words, uint64_t off,
+                        uint64_t end, int k, int dithered, uint64_t tile_id, float uh[128]) {
+  int32_t codes[N];
+  int st = orc_parse_tile(lat, words, off, end, k, codes);
+  if (st != ORC_OK) return st;
+  dequant_codes(lat, seed, codes, dithered, tile_id, uh);
+  return ORC_OK;
+}
+
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu)) return (uint16_t)((b >> 16) | 0x40u);
+  uint32_t bias = 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)((b + bias) >> 16);
+}
+
+int orc_decode(int lat, uint64_t seed, float alpha, const uint32_t *words,
+               const uint64_t *offsets, const uint8_t *k, uint64_t n_tiles,
+               int dithered, uint64_t tile_base, void *y, int dtype) {
+  if (lat_dim(lat) == 0 || !(alpha > 0.0f) || !isfinite(alpha)) return ORC_ERR_ARG;
+  if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
+  float s[N], c_enc, c_dec;
+  orc_signs(seed, s);
+  orc_scales(alpha, &c_enc, &c_dec);
+  int status = ORC_OK;
+  for (uint64_t t = 0; t < n_tiles; ++t) {
+    int32_t codes[N];
+    float v[N];
+    int st = orc_parse_tile(lat, words, offsets[t], offsets[t + 1], (int)k[t], codes);
+    if (st != ORC_OK) {
+      status = st;
+      for (int i = 0; i < N; ++i) v[i] = 0.0f;
+    } else {
+      dequant_codes(lat, seed, codes, dithered, tile_base + t, v);
+      orc_fwht128(v);
+      for (int i = 0; i < N; ++i) v[i] = s[i] * (v[i] * c_dec);
+    }
+    for (int i = 0; i < N; ++i) {
+      if (dtype == ORC_BF16) ((uint16_t *)y)[t * N + (uint64_t)i] = f32_to_bf16_rne(v[i]);
+      else ((float *)y)[t * N + (uint64_t)i] = v[i];
+    }
+  }
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention scores against compressed keys, in fp64:                        */
+/* q . k_hat = q . (D H u_hat c_dec) = c_dec <H D q, u_hat>  (H symmetric).  */
+/* ------------------------------------------------------------------------ */
+static void fwht128_f64(double v[128]) {
+  for (int h = 1; h < N; h <<= 1)
+    for (int i = 0; i < N; ++i) {
+      if (i & h) continue;
+      double a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+}
+
+int orc_kv_scores(int lat, uint64_t seed, float alpha, const uint32_t *words,
+                  const uint64_t *offsets, const uint8_t *k, uint32_t n_heads,
+                  uint64_t tiles_per_head, uint64_t tile_base, const float *q,
+                  uint32_t qph, double *scores) {
+  if (lat_dim(lat) == 0 || !(alpha > 0.0f) || qph == 0) return ORC_ERR_ARG;
+  float s[N], c_enc, c_dec;
+  orc_signs(seed, s);
+  orc_scales(alpha, &c_enc, &c_dec);
+  uint32_t nq = n_heads * qph;
+  double *qt = (double *)malloc(sizeof(double) * (size_t)nq * N);
+  if (!qt) return ORC_ERR_ARG;
+  for (uint32_t r = 0; r < nq; ++r) {
+    for (int i = 0; i < N; ++i) qt[(size_t)r * N + i] = (double)s[i] * (double)q[(size_t)r * N + i];
+    fwht128_f64(&qt[(size_t)r * N]);
+  }
+  int status = ORC_OK;
+  for (uint32_t h = 0; h < n_heads; ++h) {
+    for (uint64_t j = 0; j < tiles_per_head; ++j) {
+      uint64_t t = (uint64_t)h * tiles_per_head + j;
+      int32_t codes[N];
+      double uh[N];
+      int st = orc_parse_tile(lat, words, offsets[t], offsets[t + 1], (int)k[t], codes);
+      if (st != ORC_OK) {
+        status = st;
+        for (int i = 0; i < N; ++i) uh[i] = 0.0;
+      } else {
+        int dim = lat_dim(lat);
+        float p[N], d[N];
+        for (int v = 0; v < N / dim; ++v) orc_embed(lat, &codes[v * dim], &p[v * dim]);
+        orc_dither(lat, seed, tile_base + t, d); /* keys are always dithered */
+        for (int i = 0; i < N; ++i) uh[i] = (double)p[i] - (double)d[i];
+      }
+      for (uint32_t g = 0; g < qph; ++g) {
+        const double *qr = &qt[((size_t)h * qph + g) * N];
+        double acc = 0.0;
+        for (int i = 0; i < N; ++i) acc += qr[i] * uh[i];
+        scores[((size_t)h * qph + g) * tiles_per_head + j] = (double)c_dec * acc;
+      }
+    }
+  }
+  free(qt);
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rate calibration [HQ-explainer, Methodology 3: achieved rate within about */
+/* 0.01 bps of the target].  Mechanism (reading): start from the             */
+/* high-resolution estimate alpha0 = sqrt(2 pi e) sigma / (nu 2^R), with     */
+/* sigma the RMS of the tensor and nu the per-dimension cell edge of the     */
+/* embedding (Z 1, A2 sqrt(2 sqrt3), D4 2^(1/4), 2E8 2); bracket the target  */
+/* in log2(alpha) with steps of 4, then bisect on the exact payload rate     */
+/* until it is within 0.002 bps, at most 40 times.  The fp32 alpha with the  */
+/* closest rate wins; ties go to the larger alpha.                           */
+/* ------------------------------------------------------------------------ */
+static double rate_at(int lat, uint64_t seed, float a, const void *x, int dtype,
+                      uint64_t n_tiles, int dithered, uint64_t tile_base, int *st) {
+  uint64_t bits = 0;
+  *st = orc_total_bits(lat, seed, a, x, dtype, n_tiles, dithered, tile_base, &bits);
+  if (*st == ORC_ERR_RANGE) return INFINITY; /* step too fine: treat as too many bits */
+  return (double)bits / ((double)n_tiles * (double)N);
+}
+
+int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,
+                  uint64_t n_tiles, int dithered, uint64_t tile_base,
+                  float *alpha_out, double *bps_out, int *iters_out) {
+  if (lat_dim(lat) == 0 || n_tiles == 0 || !(bps > 0.0f)) return ORC_ERR_ARG;
+  double ss = 0.0;
+  uint64_t n = n_tiles * (uint64_t)N;
+  for (uint64_t i = 0; i < n; ++i) {
+    double v = (double)load_elem(x, dtype, i);
+    if (!isfinite(v)) return ORC_ERR_NONFINITE;
+    ss += v * v;
+  }
+  double sigma = sqrt(ss / (double)n);
+  if (!(sigma > 0.0)) return ORC_ERR_ARG;
+  static const double nu[4] = {1.0, 1.8612097182041991 /* sqrt(2 sqrt3) */,
+                               1.1892071150027210 /* 2^(1/4) */, 2.0};
+  double a0 = sqrt(2.0 * M_PI * M_E) * sigma / (nu[lat] * pow(2.0, (double)bps));
+  double target = (double)bps;
+  double lo = log2(a0) - 4.0, hi = log2(a0) + 4.0;
+  int st, iters = 0;
+  float best_a = 0.0f;
+  double best_r = 0.0, best_err = INFINITY;
+#define CONSIDER(A, R)                                                        \
+  do {                                                                        \
+    double e_ = fabs((R) - target);                                           \
+    if (e_ < best_err || (e_ == best_err && (A) > best_a)) {                  \
+      best_err = e_; best_a = (A); best_r = (R);                              \
+    }                                                                         \
+  } while (0)
+  for (int g = 0; g < 16; ++g) { /* lo must give a rate >= target */
+    float a = (float)exp2(lo);
+    double r = rate_at(lat, seed, a, x, dtype, n_tiles, dithered, tile_base, &st);
+    ++iters;
+    if (st != ORC_OK && st != ORC_ERR_RANGE) return st;
+    if (st == ORC_OK) CONSIDER(a, r);
+    if (r >= target) break;
+    lo -= 4.0;
+  }
+  for (int g = 0; g < 16; ++g) { /* hi must give a rate <= target */
+    float a = (float)exp2(hi);
+    double r = rate_at(lat, seed, a, x, dtype, n_tiles, dithered, tile_base, &st);
+    ++iters;
+    if (st != ORC_OK && st != ORC_ERR_RANGE) return st;
+    if (st == ORC_OK) CONSIDER(a, r);
+    if (r <= target) break;
+    hi += 4.0;
+  }
+  for (int it = 0; it < 40 && best_err > 0.002; ++it) {
+    double mid = 0.5 * (lo + hi);
+    float a = (float)exp2(mid);
+    double r = rate_at(lat, seed, a, x, dtype, n_tiles, dithered, tile_base, &st);
+    ++iters;
+    if (st != ORC_OK && st != ORC_ERR_RANGE) return st;
+    if (st == ORC_OK) CONSIDER(a, r);
+    if (r > target) lo = mid;
+    else hi = mid;
+  }
+#undef CONSIDER
+  if (!(best_a > 0.0f)) return ORC_ERR_RANGE;
+  *alpha_out = best_a;
+  *bps_out = best_r;
+  if (iters_out) *iters_out = iters;
+  return ORC_OK;
+}

@@ -1,0 +1,242 @@
+"""Pins of the oracle's whole-tensor codec (encode, decode, dither, rate, scores).
+
+Against the HyperQuant explainer (technical summary, Methodology 1-4):
+  * decode(encode(x)) stays within the lattice covering radius (times alpha)
+    of x, because the RHT is orthogonal and the nearest point is within the
+    covering radius of every input;
+  * the stream is lossless: parsed codes equal the quantiser's codes and the
+    offsets are the Rice lengths;
+  * with subtractive dither U ~ Uniform(V(Lambda)), the reconstruction error is
+    uniform over the Voronoi cell, so the MSE per scalar is alpha^2 G V^(2/d)
+    exactly in expectation, and every fixed vector's inner products are
+    unbiased (Methodology 4, Appendix A of the paper);
+  * the achieved rate lands within 0.01 bps of the target (Methodology 3);
+  * the fused score equals q . k_hat of the decoded key.
+"""
+import numpy as np
+import pytest
+
+from test_oracle_lattice import G_CLOSED, SQ3, members
+
+SEED = 0x5EED0001
+DIMS = {0: 1, 1: 2, 2: 4, 3: 8}
+VOL = {0: 1.0, 1: 2.0 * SQ3, 2: 2.0, 3: 256.0}
+# squared covering radius per vector of each embedding
+RCOV2 = {0: 0.25, 1: 4.0 / 3.0, 2: 1.0, 3: 4.0}
+
+
+def bf16_bits(x):
+    """fp32 -> bf16 bit patterns, round to nearest even (numpy, test side)."""
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def bf16_to_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def gaussian_tiles(rng, n_tiles, sigma=0.02, outliers=0.01, mult=20.0):
+    x = rng.standard_normal((n_tiles, 128)) * sigma
+    mask = rng.random((n_tiles, 128)) < outliers
+    x[mask] *= mult
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("lat", [0, 1, 2, 3])
+def test_round_trip_within_covering_radius(orc, lat):
+    rng = np.random.default_rng(900 + lat)
+    x = gaussian_tiles(rng, 256)
+    alpha = 0.004
+    st, words, off, k = orc.encode(lat, SEED, alpha, x)
+    assert st == 0
+    st, y = orc.decode(lat, SEED, alpha, words, off, k)
+    assert st == 0
+    y = y.reshape(x.shape)
+    bound = np.sqrt(RCOV2[lat] * 128 / DIMS[lat]) * alpha
+    err = np.linalg.norm(y.astype(np.float64) - x, axis=1)
+    assert np.all(err <= bound * (1 + 1e-5) + 1e-6 * np.linalg.norm(x, axis=1))
+    # and the error is well below the input: the codec is not returning zeros
+    assert err.mean() < 0.2 * np.linalg.norm(x, axis=1).mean()
+
+
+@pytest.mark.parametrize("lat", [0, 1, 2, 3])
+def test_stream_is_lossless_and_offsets_are_rice_lengths(orc, lat):
+    rng = np.random.default_rng(950 + lat)
+    x = gaussian_tiles(rng, 97)  # not a multiple of anything
+    alpha = 0.003
+    st, words, off, k = orc.encode(lat, SEED, alpha, x)
+    assert st == 0 and off[0] == 0 and np.all(np.diff(off.astype(np.int64)) > 0)
+    total = int(off[-1])
+    assert words.size == (total + 31) // 32
+    if total % 32:
+        assert int(words[-1]) >> (total % 32) == 0  # trailing bits are zero
+    st, tb = orc.total_bits(lat, SEED, alpha, x)
+    assert st == 0 and tb == total
+    for t in range(x.shape[0]):
+        st, codes = orc.quantize_tile(lat, SEED, alpha, x[t])
+        assert st == 0 and np.all(members(lat, codes.reshape(-1, DIMS[lat])))
+        st, parsed = orc.parse_tile(lat, words, int(off[t]), int(off[t + 1]), int(k[t]))
+        assert st == 0 and np.array_equal(parsed, codes)
+
+
+def test_bf16_input_and_output(orc):
+    rng = np.random.default_rng(960)
+    xf = gaussian_tiles(rng, 64)
+    xb = bf16_bits(xf)
+    alpha = 0.003
+    st1, w1, o1, k1 = orc.encode(3, SEED, alpha, xb)
+    st2, w2, o2, k2 = orc.encode(3, SEED, alpha, bf16_to_f32(xb))
+    assert st1 == st2 == 0 and np.array_equal(w1, w2) and np.array_equal(o1, o2)
+    st, yf = orc.decode(3, SEED, alpha, w1, o1, k1)
+    st, yb = orc.decode(3, SEED, alpha, w1, o1, k1, out_dtype=1)
+    assert np.array_equal(yb, bf16_bits(yf))
+
+
+def test_empty_and_error_statuses(orc):
+    alpha = 0.003
+    st, w, off, k = orc.encode(3, SEED, alpha, np.zeros((0, 128), np.float32))
+    assert st == 0 and off.tolist() == [0]
+    x = np.zeros((4, 128), np.float32)
+    x[2, 5] = np.nan
+    assert orc.encode(3, SEED, alpha, x)[0] == orc.ERR_NONFINITE
+    x[2, 5] = np.inf
+    assert orc.encode(3, SEED, alpha, x)[0] == orc.ERR_NONFINITE
+    x[2, 5] = 1e6  # |u| >= 2^20 after scaling by 1/(alpha sqrt n)
+    assert orc.encode(3, SEED, alpha, x)[0] == orc.ERR_RANGE
+    x[2, 5] = 0.01
+    st, w, off, k = orc.encode(3, SEED, alpha, x)
+    assert st == 0
+    need = (int(off[-1]) + 31) // 32
+    assert orc.encode(3, SEED, alpha, x, cap_words=need - 1)[0] == orc.ERR_CAPACITY
+    assert orc.encode(3, SEED, alpha, x, cap_words=need)[0] == 0
+    assert orc.encode(3, SEED, -1.0, x)[0] == orc.ERR_ARG
+
+
+def test_corrupt_records_are_detected(orc):
+    rng = np.random.default_rng(970)
+    x = gaussian_tiles(rng, 8)
+    st, w, off, k = orc.encode(3, SEED, 0.003, x)
+    o0, o1 = int(off[0]), int(off[1])
+    assert orc.parse_tile(3, w, o0, o1, int(k[0]))[0] == 0
+    assert orc.parse_tile(3, w, o0, o1 - 1, int(k[0]))[0] == orc.ERR_CORRUPT  # short
+    assert orc.parse_tile(3, w, o0, o1 + 1, int(k[0]))[0] == orc.ERR_CORRUPT  # trailing bit
+    assert orc.parse_tile(3, w, o0, o1, 23)[0] == orc.ERR_CORRUPT  # k out of range
+    assert orc.parse_tile(3, w, o0, o0 + 5000, int(k[0]))[0] == orc.ERR_CORRUPT  # too long
+    w2 = w.copy()
+    w2[(o1 - 1) >> 5] ^= 1 << ((o1 - 1) & 31)  # drop the last terminating one
+    assert orc.parse_tile(3, w2, o0, o1, int(k[0]))[0] == orc.ERR_CORRUPT
+    koff = k.copy()
+    koff[1] = (int(k[1]) + 1) % 23
+    st, _ = orc.decode(3, SEED, 0.003, w, off, koff)
+    assert st == orc.ERR_CORRUPT
+
+
+# --------------------------------------------------------------------------- #
+# dither (Methodology 4)
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("lat", [0, 1, 2, 3])
+def test_dither_is_uniform_over_the_voronoi_cell(orc, lat):
+    d = DIMS[lat]
+    ds = np.concatenate([orc.dither(lat, 77, t) for t in range(4000)]).reshape(-1, d)
+    # inside the cell: the origin is (one of) the nearest lattice points
+    q = orc.nearest(lat, ds)
+    inside = np.all(q == 0, axis=1)
+    assert inside.mean() > 0.999
+    # mean zero and second moment G V^(2/d) per scalar
+    n = ds.shape[0]
+    assert np.all(np.abs(ds.mean(0)) < 5 * ds.std(0) / np.sqrt(n))
+    m2 = np.sum(ds.astype(np.float64) ** 2, axis=1) / d
+    want = G_CLOSED[lat] * VOL[lat] ** (2.0 / d)
+    assert abs(m2.mean() - want) < 5 * m2.std() / np.sqrt(n)
+
+
+@pytest.mark.parametrize("lat", [0, 2, 3])
+def test_dithered_distortion_closed_form(orc, lat):
+    """Crypto lemma: with subtractive dither the error is uniform over V, so
+    the per-scalar MSE is alpha^2 G V^(2/d), whatever the input."""
+    rng = np.random.default_rng(1000 + lat)
+    x = (rng.standard_normal((3000, 128)) * 0.7).astype(np.float32)
+    alpha = 0.05
+    st, w, off, k = orc.encode(lat, SEED, alpha, x, dithered=True, tile_base=12345)
+    assert st == 0
+    st, y = orc.decode(lat, SEED, alpha, w, off, k, dithered=True, tile_base=12345)
+    assert st == 0
+    e2 = np.mean((y.reshape(x.shape).astype(np.float64) - x) ** 2, axis=1) / alpha**2
+    want = G_CLOSED[lat] * VOL[lat] ** (2.0 / DIMS[lat])
+    assert abs(e2.mean() - want) < 5 * e2.std() / np.sqrt(e2.size)
+
+
+def test_kv_inner_products_unbiased_per_vector(orc):
+    """10^6 copies of one fixed key, each quantised with its own dither (tile id):
+    mean(q . k_hat - q . k) is zero within 4.5 standard errors (Methodology 4).
+    Negative control: without dither every copy has the same nonzero error."""
+    rng = np.random.default_rng(1100)
+    kvec = (rng.standard_normal(128) * 1.0).astype(np.float32)
+    kvec[[3, 70]] *= 50.0  # an outlier channel pair, as in the KV workloads
+    q = rng.standard_normal(128)
+    n = 1_000_000
+    x = np.broadcast_to(kvec, (n, 128)).copy()
+    alpha = 0.9
+    st, w, off, k = orc.encode(2, SEED, alpha, x, dithered=True, tile_base=0)
+    assert st == 0
+    st, y = orc.decode(2, SEED, alpha, w, off, k, dithered=True, tile_base=0)
+    assert st == 0
+    err = y.reshape(n, 128).astype(np.float64) @ q - float(kvec.astype(np.float64) @ q)
+    z = err.mean() / (err.std() / np.sqrt(n))
+    assert abs(z) < 4.5, z
+    # negative control
+    nd = 1000
+    st, w, off, k = orc.encode(2, SEED, alpha, x[:nd], dithered=False)
+    st, y = orc.decode(2, SEED, alpha, w, off, k, dithered=False)
+    err0 = y.reshape(nd, 128).astype(np.float64) @ q - float(kvec.astype(np.float64) @ q)
+    assert np.all(err0 == err0[0]) and abs(err0[0]) > 0
+
+
+# --------------------------------------------------------------------------- #
+# rate (Methodology 3) and scores
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("lat,bps", [(3, 4.0), (3, 3.0), (3, 1.7), (2, 2.0), (1, 3.0), (0, 5.0)])
+def test_calibrated_rate_within_target(orc, lat, bps):
+    rng = np.random.default_rng(1200 + lat)
+    x = gaussian_tiles(rng, 512)
+    st, alpha, rate, iters = orc.calibrate(lat, SEED, bps, x)
+    assert st == 0
+    assert abs(rate - bps) <= 0.01  # the pages' claim
+    assert abs(rate - bps) <= 0.002  # this codec's stopping rule
+    st, tb = orc.total_bits(lat, SEED, alpha, x)
+    assert tb / x.size == rate
+
+
+def test_rate_follows_high_resolution_entropy(orc):
+    """R ~ h(X) - log2(nu alpha) per scalar, h = 0.5 log2(2 pi e sigma^2), plus
+    a Rice overhead of about 0.1 bit (Rice is matched to geometric, not
+    Gaussian, symbols); a wrong scale or a dropped term breaks this."""
+    rng = np.random.default_rng(1300)
+    sigma = 0.02
+    x = (rng.standard_normal((1024, 128)) * sigma).astype(np.float32)
+    nu = {0: 1.0, 1: np.sqrt(2 * SQ3), 2: 2 ** 0.25, 3: 2.0}
+    for lat in (0, 1, 2, 3):
+        for bits in (4.0, 5.0):
+            alpha = np.sqrt(2 * np.pi * np.e) * sigma / (nu[lat] * 2**bits)
+            st, tb = orc.total_bits(lat, SEED, float(alpha), x)
+            assert st == 0
+            over = tb / x.size - bits
+            assert 0.0 < over < 0.2, (lat, bits, over)
+
+
+def test_scores_equal_query_dot_decoded_key(orc):
+    rng = np.random.default_rng(1400)
+    H, S, qph = 2, 40, 4
+    kx = rng.standard_normal((H * S, 128)).astype(np.float32)
+    q = rng.standard_normal((H * qph, 128)).astype(np.float32)
+    alpha = 0.4
+    for lat in (3, 2):
+        st, w, off, k = orc.encode(lat, SEED, alpha, kx, dithered=True, tile_base=500)
+        st, sc = orc.kv_scores(lat, SEED, alpha, w, off, k, H, S, 500, q, qph)
+        assert st == 0
+        st, y = orc.decode(lat, SEED, alpha, w, off, k, dithered=True, tile_base=500)
+        khat = y.reshape(H, S, 128).astype(np.float64)
+        want = np.einsum("hgi,hsi->hgs", q.reshape(H, qph, 128).astype(np.float64), khat).reshape(H * qph, S)
+        scale = np.linalg.norm(q, axis=1)[:, None] * np.linalg.norm(khat.reshape(H * S, 128), axis=1).reshape(H, S).repeat(qph, 0)
+        assert np.all(np.abs(sc - want) <= 1e-5 * scale)
