@@ -1,0 +1,176 @@
+"""Benchmark of the HyperQuant E8 weight codec on one MI355X.
+
+Workload: the 4096 x 4096 bf16 weight (Student-t(4) entries, per-row sigma
+LogUniform(0.005, 0.05)), E8 lattice at 4 bits per scalar, alpha from
+hq_calibrate (untimed).  One step = hq_encode followed by hq_decode (bf16 out)
+of the whole tensor, i.e. every step of the weight codec's hot path.  Inputs
+are resident in HBM; ten buffer sets are rotated so that no step finds its
+data in the 256 MB last-level cache.
+
+value = 2 x bf16 tensor bytes / step time: each of encode and decode moves the
+bf16 tensor once, so this is the mean codec throughput in "GB/s (bf16 in)".
+The roofline object is for the slower of the two kernels, with algorithmic
+bytes = bf16 tensor + payload + offsets (8 B/tile) + k (1 B/tile).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--bps", type=float, default=4.0)
+    ap.add_argument("--sets", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def cpu_baseline(x_host_bits, alpha, seed, reps):
+    """The oracle (single-threaded C) on the same tensor: encode + decode."""
+    import numpy as np  # noqa: F401
+    from oracle import oracle as O
+    O.lib()
+    n_bytes = x_host_bits.size * 2
+    t_total = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        st, w, off, k = O.encode(O.E8, seed, alpha, x_host_bits)
+        st2, y = O.decode(O.E8, seed, alpha, w, off, k, out_dtype=O.BF16)
+        t_total += time.perf_counter() - t0
+        assert st == 0 and st2 == 0
+    return {"value": round(2.0 * n_bytes * reps / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"whole 4096x4096 bf16 tensor, encode+decode, {reps} repetitions, "
+                      f"{t_total:.1f} s single-threaded"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import lattice_vq_entropy_amd as hq
+    from lattice_vq_entropy_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    seed = W.PLAN_SEED
+    x0 = W.c2(dev)
+    n_el = x0.numel()
+    n_tiles = n_el // 128
+    plan = hq.Plan("E8", args.bps, seed)
+    ws = plan.workspace(n_tiles)
+    alpha, bps_cal = plan.calibrate(x0, ws)
+
+    sets = []
+    for i in range(args.sets):
+        x = x0 if i == 0 else x0.clone()
+        out = hq.alloc_stream(plan, n_tiles, dev)
+        y = torch.empty(n_el, dtype=torch.bfloat16, device=dev)
+        sets.append((x, out, y))
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        x, out, y = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        enc = hq.encode(plan, x, ws, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+        hq.decode(plan, enc, ws, out=y)
+        if ev is not None:
+            ev[2].record(stream)
+        return enc
+
+    for i in range(args.warmup):
+        step(i)
+    hq.check(ws)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    hq.check(ws)
+
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+
+    # stream size of this tensor (all sets hold the same data)
+    enc = sets[0][1]
+    total_bits = int(enc[1][-1].item())
+    payload_bytes = total_bits / 8.0
+    side_bytes = 8.0 * (n_tiles + 1) + n_tiles
+    bf16_bytes = 2.0 * n_el
+    alg_bytes = bf16_bytes + payload_bytes + side_bytes
+    enc_gbs = alg_bytes / (enc_ms * 1e-3) / 1e9
+    dec_gbs = alg_bytes / (dec_ms * 1e-3) / 1e9
+    dominant = "encode" if enc_ms >= dec_ms else "decode"
+    achieved = min(enc_gbs, dec_gbs)
+
+    line = {
+        "metric": "encode/decode GB/s (bf16 in) + % HBM roofline, E8 at 4 bps, 1xMI355X",
+        "value": round(2.0 * bf16_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "weight codec: bf16 4096x4096, Student-t(4) x per-row LogUniform(0.005,0.05) sigma, "
+                        "tiles of 128 along rows, E8 lattice",
+            "bps_target": args.bps,
+            "bps_achieved": round(total_bits / n_el, 5),
+            "alpha": alpha,
+            "input_sets_rotated": args.sets,
+            "step": "hq_encode + hq_decode (bf16 out)",
+        },
+        "encode": {"ms": round(enc_ms, 5), "GBps_bf16_in": round(bf16_bytes / (enc_ms * 1e-3) / 1e9, 1),
+                   "GBps_algorithmic": round(enc_gbs, 1), "hbm_frac": round(enc_gbs / HBM_PEAK_GBS, 4)},
+        "decode": {"ms": round(dec_ms, 5), "GBps_bf16_in": round(bf16_bytes / (dec_ms * 1e-3) / 1e9, 1),
+                   "GBps_algorithmic": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": int(alg_bytes),
+        },
+    }
+    if not args.no_cpu_baseline:
+        xb = x0.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+        line["cpu_baseline"] = cpu_baseline(xb, alpha, seed, args.cpu_reps)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,140 @@
+/*
+ * hq.h -- C ABI of libhq, the HyperQuant per-tile lattice codec for MI355X
+ * (gfx950).
+ *
+ * The operation is the data-free post-training codec of "HyperQuant: A
+ * Rate-Distortion-Optimal Quantization Pipeline for Large Language and
+ * Diffusion Models" (gist.science explainer pages, technical summary,
+ * Methodology 1-4; the paper's abstract page, items (i)-(iv)):
+ *   encode: per 128-wide tile, the randomized Hadamard transform
+ *           u = H_n D x / (alpha sqrt n)                       (Methodology 1)
+ *           nearest point of u in the integer embedding of E8, D4, A2 or Z
+ *                                                               (Methodology 2)
+ *           bit-stripping of the membership-fixed bits, Rice coding of the
+ *           remaining symbols with one k per tile                (Methodology 3)
+ *           for KV: subtractive dither U ~ Uniform(V(lattice)) added before
+ *           and subtracted after quantisation                    (Methodology 4)
+ *   decode: the inverse of each step.
+ *
+ * Conventions (all entry points):
+ *   - Pointers named x, y, words, offsets, k, q, scores and ws are DEVICE
+ *     pointers owned by the caller, 16-byte aligned.  The library never
+ *     allocates device memory.  `stream` is a hipStream_t (NULL = null stream).
+ *   - Calls are asynchronous on `stream` except hq_calibrate and
+ *     hq_status_sync, which synchronise it.
+ *   - Argument errors return synchronously (HQ_ERR_ARG, HQ_ERR_NOALPHA).
+ *     Data errors found on the device (non-finite input, range, capacity,
+ *     corrupt stream) are recorded in the workspace and returned by
+ *     hq_status_sync; the outputs of the failing call are then unspecified.
+ *     When several data errors occur, the lowest code is reported.
+ *   - Workspace: a device buffer of hq_workspace_bytes() bytes, zero-filled
+ *     by the caller once before its first use.  One workspace must not be
+ *     used by two calls that can run concurrently (e.g. on two streams).
+ *   - Tensors are row-major; every 128 consecutive elements form one tile
+ *     (weights: tiles along rows; KV [B, H, S, 128]: one tile per vector).
+ *   - Stream layout: record of tile t at bits [offsets[t], offsets[t+1]):
+ *     [E8 only: 16 raw coset bits, bit v for lattice vector v]
+ *     [128 Rice remainders of k[t] bits, symbol order, LSB first]
+ *     [128 unary quotients, q zeros then a one].
+ *     Stream bit P is bit P%32 of 32-bit word P/32; records abut; offsets[0]
+ *     = 0; the unused bits of the last word are zero; words beyond it are
+ *     not written.  The stream is not self-describing: decoding needs the
+ *     same plan (lattice, seed, alpha).
+ */
+#ifndef HQ_H
+#define HQ_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { HQ_Z = 0, HQ_A2 = 1, HQ_D4 = 2, HQ_E8 = 3 } hq_lattice;
+typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
+typedef enum {
+  HQ_OK = 0,
+  HQ_ERR_ARG = 1,        /* bad argument (null pointer, tile != 128, size) */
+  HQ_ERR_NONFINITE = 2,  /* NaN or Inf in the input */
+  HQ_ERR_RANGE = 3,      /* a scaled coordinate reached 2^20: alpha too small */
+  HQ_ERR_CAPACITY = 4,   /* the stream does not fit cap_words */
+  HQ_ERR_CORRUPT = 5,    /* a record does not parse (decode) */
+  HQ_ERR_DEVICE = 6,     /* a HIP runtime call failed */
+  HQ_ERR_NOALPHA = 7     /* the plan has no alpha yet */
+} hq_status;
+
+typedef struct hq_plan_s* hq_plan_t;
+
+/* Create a plan [Methodology 1-2]: lattice, tile length (must be 128), target
+ * rate in bits per scalar (used by hq_calibrate), seed of the random signs of
+ * D and of the dither stream.  alpha is unset until hq_plan_set_alpha or
+ * hq_calibrate.  The plan is host memory owned by the library. */
+hq_status hq_plan(hq_lattice lattice, int tile, float bps, uint64_t seed, hq_plan_t* out);
+
+/* Fix the lattice scale alpha (> 0, finite) [Methodology 2]. */
+hq_status hq_plan_set_alpha(hq_plan_t plan, float alpha);
+
+/* Read back alpha and the fp32 scale constants c_enc = 1/(alpha sqrt 128),
+ * c_dec = alpha/sqrt 128 (any output pointer may be NULL). */
+hq_status hq_plan_get(hq_plan_t plan, float* alpha, float* c_enc, float* c_dec);
+
+void hq_plan_destroy(hq_plan_t plan);
+
+/* Workspace bytes for calls on up to n_tiles tiles. */
+size_t hq_workspace_bytes(hq_plan_t plan, uint64_t n_tiles);
+
+/* Words that always suffice for the stream of n_tiles tiles (the longest
+ * record is 16 + 128*23 bits for E8, 128*23 otherwise). */
+uint64_t hq_encode_bound_words(hq_plan_t plan, uint64_t n_tiles);
+
+/* Rate calibration [Methodology 3: the achieved rate lands within about 0.01
+ * bps of the target]: bisection on log2(alpha) for the payload rate of x,
+ * stopping within 0.002 bps (at most 40 steps after bracketing).  Sets the
+ * plan's alpha.  dithered/tile_base select the KV dither stream.  Synchronous. */
+hq_status hq_calibrate(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles,
+                       int dithered, uint64_t tile_base, void* ws, void* stream,
+                       float* alpha_out, double* bps_out);
+
+/* Encode n_tiles tiles of x (fp32 or bf16) [Methodology 1-3].
+ * words: cap_words uint32 (see hq_encode_bound_words); offsets: n_tiles+1
+ * uint64 bit offsets; k: n_tiles uint8 Rice parameters. */
+hq_status hq_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles,
+                    uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k,
+                    void* ws, void* stream);
+
+/* Decode n_tiles tiles into y (fp32 or bf16).  n_words bounds the reads of
+ * words. */
+hq_status hq_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
+                    const uint64_t* offsets, const uint8_t* k, uint64_t n_tiles, void* y,
+                    hq_dtype out_dtype, void* ws, void* stream);
+
+/* KV variants with subtractive dither [Methodology 4]: the dither of tile t
+ * is drawn from (seed, tile_base + t) by Philox4x32-10, so appended tokens
+ * keep their own stream. */
+hq_status hq_kv_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles,
+                       uint64_t tile_base, uint32_t* words, uint64_t cap_words,
+                       uint64_t* offsets, uint8_t* k, void* ws, void* stream);
+hq_status hq_kv_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
+                       const uint64_t* offsets, const uint8_t* k, uint64_t n_tiles,
+                       uint64_t tile_base, void* y, hq_dtype out_dtype, void* ws, void* stream);
+
+/* Attention scores against dithered compressed keys, without materialising
+ * them: scores[(h*qph + g)*tiles_per_head + s] = q_{h,g} . k_hat_{h,s}
+ * = c_dec <H D q_{h,g}, u_hat_{h,s}> for the keys of n_heads heads stored as
+ * tiles h*tiles_per_head + s of one encode (tile ids tile_base + that).
+ * q: fp32 [n_heads*qph][128]; scores: fp32.  qph <= 16. */
+hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
+                       const uint64_t* offsets, const uint8_t* k, uint32_t n_heads,
+                       uint64_t tiles_per_head, uint64_t tile_base, const float* q,
+                       uint32_t qph, float* scores, void* ws, void* stream);
+
+/* Synchronise stream, return the lowest data error recorded in ws since the
+ * last call, and clear it. */
+hq_status hq_status_sync(void* ws, void* stream);
+
+const char* hq_status_str(hq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

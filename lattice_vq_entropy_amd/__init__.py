@@ -1,0 +1,240 @@
+"""Python binding of libhq, the HyperQuant per-tile lattice codec for MI355X.
+
+Argument marshalling only: every step of the codec runs in the HIP kernels of
+``libhq.so`` (built by ``lattice_vq_entropy_amd/build.py``), called through its
+C ABI (``include/hq.h``).  PyTorch supplies device memory and the stream.
+The binding raises if the library is missing; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch  # noqa: F401  (loads the HIP runtime libhq links against)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhq.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "hq.h")
+
+Z, A2, D4, E8 = 0, 1, 2, 3
+LATTICES = {"Z": Z, "A2": A2, "D4": D4, "E8": E8}
+F32, BF16 = 0, 1
+OK, ERR_ARG, ERR_NONFINITE, ERR_RANGE, ERR_CAPACITY, ERR_CORRUPT, ERR_DEVICE, ERR_NOALPHA = range(8)
+TILE = 128
+
+
+class HQError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"libhq: {status_str(code)} (code {code}){': ' + what if what else ''}")
+
+
+_lib = None
+_p, _u64, _u32, _f, _i = C.c_void_p, C.c_uint64, C.c_uint32, C.c_float, C.c_int
+
+_SIGNATURES = {
+    "hq_plan": (_i, [_i, _i, _f, _u64, C.POINTER(_p)]),
+    "hq_plan_set_alpha": (_i, [_p, _f]),
+    "hq_plan_get": (_i, [_p, C.POINTER(_f), C.POINTER(_f), C.POINTER(_f)]),
+    "hq_plan_destroy": (None, [_p]),
+    "hq_workspace_bytes": (C.c_size_t, [_p, _u64]),
+    "hq_encode_bound_words": (_u64, [_p, _u64]),
+    "hq_calibrate": (_i, [_p, _p, _i, _u64, _i, _u64, _p, _p, C.POINTER(_f), C.POINTER(C.c_double)]),
+    "hq_encode": (_i, [_p, _p, _i, _u64, _p, _u64, _p, _p, _p, _p]),
+    "hq_decode": (_i, [_p, _p, _u64, _p, _p, _u64, _p, _i, _p, _p]),
+    "hq_kv_encode": (_i, [_p, _p, _i, _u64, _u64, _p, _u64, _p, _p, _p, _p]),
+    "hq_kv_decode": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _i, _p, _p]),
+    "hq_kv_scores": (_i, [_p, _p, _u64, _p, _p, _u32, _u64, _u64, _p, _u32, _p, _p, _p]),
+    "hq_status_sync": (_i, [_p, _p]),
+    "hq_status_str": (C.c_char_p, [_i]),
+}
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/hq.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(hq_\w+)\s*\(", text, re.M)))
+
+
+def lib():
+    """The loaded libhq (ctypes), raising when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python lattice_vq_entropy_amd/build.py` (no fallback exists)")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(code: int) -> str:
+    try:
+        return lib().hq_status_str(code).decode()
+    except Exception:  # library missing
+        return f"status {code}"
+
+
+def _check(code: int, what: str = ""):
+    if code != OK:
+        raise HQError(code, what)
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dptr(t: torch.Tensor | None):
+    if t is None:
+        return C.c_void_p(0)
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("expected a contiguous device tensor")
+    return C.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("input must be float32 or bfloat16")
+
+
+def _n_tiles(t: torch.Tensor) -> int:
+    if t.numel() % TILE:
+        raise ValueError("the number of elements must be a multiple of 128")
+    return t.numel() // TILE
+
+
+class Plan:
+    """hq_plan: lattice, target bps, seed; alpha set by set_alpha or calibrate."""
+
+    def __init__(self, lattice, bps: float, seed: int, tile: int = TILE):
+        lat = LATTICES[lattice] if isinstance(lattice, str) else int(lattice)
+        h = C.c_void_p(0)
+        _check(lib().hq_plan(lat, tile, float(bps), int(seed), C.byref(h)), "hq_plan")
+        self._h = h
+        self.lattice, self.bps, self.seed = lat, float(bps), int(seed)
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.hq_plan_destroy(self._h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def set_alpha(self, alpha: float):
+        _check(lib().hq_plan_set_alpha(self._h, float(alpha)), "hq_plan_set_alpha")
+        return self
+
+    def get(self):
+        a, ce, cd = C.c_float(0), C.c_float(0), C.c_float(0)
+        _check(lib().hq_plan_get(self._h, C.byref(a), C.byref(ce), C.byref(cd)), "hq_plan_get")
+        return a.value, ce.value, cd.value
+
+    @property
+    def alpha(self) -> float:
+        return self.get()[0]
+
+    def workspace_bytes(self, n_tiles: int) -> int:
+        return int(lib().hq_workspace_bytes(self._h, n_tiles))
+
+    def bound_words(self, n_tiles: int) -> int:
+        return int(lib().hq_encode_bound_words(self._h, n_tiles))
+
+    def workspace(self, n_tiles: int, device="cuda") -> torch.Tensor:
+        """A zero-filled workspace (the zero fill is required once)."""
+        return torch.zeros(self.workspace_bytes(n_tiles), dtype=torch.uint8, device=device)
+
+    def calibrate(self, x: torch.Tensor, ws: torch.Tensor, dithered: bool = False, tile_base: int = 0,
+                  stream=None):
+        a, r = C.c_float(0), C.c_double(0)
+        _check(lib().hq_calibrate(self._h, _dptr(x), _dtype_code(x), _n_tiles(x), int(dithered), tile_base,
+                                  _dptr(ws), _stream(stream), C.byref(a), C.byref(r)), "hq_calibrate")
+        return a.value, r.value
+
+
+class Encoded:
+    """Bitstream, per-tile bit offsets and Rice parameters of one encode."""
+
+    def __init__(self, words, offsets, k, n_tiles, tile_base=0, dithered=False):
+        self.words, self.offsets, self.k = words, offsets, k
+        self.n_tiles, self.tile_base, self.dithered = n_tiles, tile_base, dithered
+
+    def total_bits(self) -> int:
+        return int(self.offsets[-1].item())
+
+    def used_words(self) -> int:
+        return (self.total_bits() + 31) // 32
+
+
+def alloc_stream(plan: Plan, n_tiles: int, device="cuda"):
+    words = torch.empty(max(plan.bound_words(n_tiles), 1), dtype=torch.int32, device=device)
+    offsets = torch.empty(n_tiles + 1, dtype=torch.int64, device=device)
+    k = torch.empty(max(n_tiles, 1), dtype=torch.uint8, device=device)
+    return words, offsets, k
+
+
+def encode(plan: Plan, x: torch.Tensor, ws: torch.Tensor, out=None, dithered: bool = False,
+           tile_base: int = 0, cap_words: int | None = None, stream=None) -> Encoded:
+    """hq_encode / hq_kv_encode (asynchronous; check hq_status_sync for data errors)."""
+    n = _n_tiles(x)
+    words, offsets, k = out if out is not None else alloc_stream(plan, n, x.device)
+    cap = words.numel() if cap_words is None else cap_words
+    if dithered:
+        rc = lib().hq_kv_encode(plan.handle, _dptr(x), _dtype_code(x), n, tile_base, _dptr(words), cap,
+                                _dptr(offsets), _dptr(k), _dptr(ws), _stream(stream))
+    else:
+        rc = lib().hq_encode(plan.handle, _dptr(x), _dtype_code(x), n, _dptr(words), cap, _dptr(offsets),
+                             _dptr(k), _dptr(ws), _stream(stream))
+    _check(rc, "encode")
+    return Encoded(words, offsets, k, n, tile_base, dithered)
+
+
+def decode(plan: Plan, enc: Encoded, ws: torch.Tensor, out: torch.Tensor | None = None,
+           out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """hq_decode / hq_kv_decode into a [n_tiles*128] tensor."""
+    n = enc.n_tiles
+    y = out if out is not None else torch.empty(n * TILE, dtype=out_dtype, device=enc.words.device)
+    code = _dtype_code(y)
+    if enc.dithered:
+        rc = lib().hq_kv_decode(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets),
+                                _dptr(enc.k), n, enc.tile_base, _dptr(y), code, _dptr(ws), _stream(stream))
+    else:
+        rc = lib().hq_decode(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),
+                             n, _dptr(y), code, _dptr(ws), _stream(stream))
+    _check(rc, "decode")
+    return y
+
+
+def kv_scores(plan: Plan, enc: Encoded, n_heads: int, tiles_per_head: int, q: torch.Tensor, qph: int,
+              ws: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """hq_kv_scores: fp32 [n_heads*qph, tiles_per_head] = q . k_hat without materialising k_hat."""
+    if q.dtype != torch.float32 or q.numel() != n_heads * qph * TILE:
+        raise ValueError("q must be fp32 [n_heads*qph, 128]")
+    s = out if out is not None else torch.empty(n_heads * qph, tiles_per_head, dtype=torch.float32,
+                                                device=q.device)
+    rc = lib().hq_kv_scores(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),
+                            n_heads, tiles_per_head, enc.tile_base, _dptr(q), qph, _dptr(s), _dptr(ws),
+                            _stream(stream))
+    _check(rc, "kv_scores")
+    return s
+
+
+def status_sync(ws: torch.Tensor, stream=None) -> int:
+    """hq_status_sync: synchronise and return (and clear) the recorded data error."""
+    return int(lib().hq_status_sync(_dptr(ws), _stream(stream)))
+
+
+def check(ws: torch.Tensor, stream=None):
+    _check(status_sync(ws, stream), "device status")

@@ -1,0 +1,70 @@
+"""Build libhq.so (HIP, gfx950) in-tree.
+
+The library links the HIP runtime that PyTorch ships, so that a process that
+also uses torch for device memory and streams has exactly one HIP runtime.
+Device code is built with -ffp-contract=off (no FMA contraction: the fp32
+decisions that pick lattice codes follow a fixed operation order) and without
+packed fp32 instructions.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libhq.so")
+SOURCES = ["hq_kernels.hip", "hq_api.hip"]
+HEADERS = ["hq_device.h", "hq_kernels.h", "hq_ws.h"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+DEVICE_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+]
+
+
+def torch_lib_dir() -> str:
+    import importlib.util
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.origin:
+        raise RuntimeError("torch is required for its HIP runtime")
+    return os.path.join(os.path.dirname(spec.origin), "lib")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libhq.so; always rebuilds."""
+    objs = []
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    for src in SOURCES:
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
+        cmd = [HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed on {src}")
+        objs.append(obj)
+    tlib = torch_lib_dir()
+    tmp = LIB + ".tmp"
+    cmd = ["/opt/rocm/llvm/bin/clang++", "-shared", "-fPIC", "-o", tmp, *objs,
+           os.path.join(tlib, "libamdhip64.so"), f"-Wl,-rpath,{tlib}", "-Wl,--no-undefined",
+           "-Wl,-z,defs"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link of libhq.so failed")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

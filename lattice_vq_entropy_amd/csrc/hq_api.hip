@@ -1,0 +1,335 @@
+// hq_api.hip -- host side of libhq: plans, argument checks, kernel launches,
+// status, and rate calibration.  See include/hq.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/hq.h"
+#include "hq_kernels.h"
+#include "hq_ws.h"
+
+struct hq_plan_s {
+  int lattice;
+  float bps;
+  uint64_t seed;
+  bool has_alpha;
+  float alpha, c_enc, c_dec;
+  uint32_t sgn[4];
+};
+
+namespace {
+
+constexpr uint32_t kTagSign = 0x5349474Eu;  // "SIGN"
+
+// Philox4x32-10 [Salmon et al., SC'11] on the host, for the sign vector of D.
+void philox_host(uint32_t c[4], uint32_t k0, uint32_t k1) {
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = (uint32_t)p1;
+    c[2] = n2;
+    c[3] = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+int raw_bits(int lat) { return lat == HQ_E8 ? 16 : 0; }
+uint64_t max_record_bits(int lat) { return (uint64_t)raw_bits(lat) + 128ull * 23ull; }
+
+bool lattice_ok(int lat) { return lat >= HQ_Z && lat <= HQ_E8; }
+
+hq_status dev_err(hipError_t e) { return e == hipSuccess ? HQ_OK : HQ_ERR_DEVICE; }
+
+void fill_common(const hq_plan_s* p, uint32_t sgn[4], uint32_t& k0, uint32_t& k1) {
+  for (int i = 0; i < 4; ++i) sgn[i] = p->sgn[i];
+  k0 = (uint32_t)p->seed;
+  k1 = (uint32_t)(p->seed >> 32);
+}
+
+hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, bool dither,
+                      uint64_t tile_base, uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k,
+                      void* ws, void* stream, bool len_only) {
+  if (!plan) return HQ_ERR_ARG;
+  if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_ARG;
+  if (!ws) return HQ_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (!len_only && !offsets) return HQ_ERR_ARG;
+  if (n_tiles == 0) {
+    if (len_only) return HQ_OK;
+    return dev_err(hipMemsetAsync(offsets, 0, sizeof(uint64_t), st));
+  }
+  if (!x) return HQ_ERR_ARG;
+  if (!len_only && (!words || !k)) return HQ_ERR_ARG;
+  if (((uintptr_t)x & 15u) != 0) return HQ_ERR_ARG;
+  // descriptors hold 38-bit bit counts; chunk tickets are 32-bit
+  if (n_tiles > (hq::kDescValueMask / max_record_bits(plan->lattice))) return HQ_ERR_ARG;
+  hq::EncArgs a{};
+  a.x = x;
+  a.n_tiles = n_tiles;
+  a.words = words;
+  a.cap_words = cap_words;
+  a.offsets = offsets;
+  a.kout = k;
+  fill_common(plan, a.sgn, a.key0, a.key1);
+  a.c_enc = plan->c_enc;
+  a.tile_base = tile_base;
+  a.ws = (hq::WsHeader*)ws;
+  const uint64_t chunks = hq::ws_chunks(n_tiles);
+  a.desc = (uint64_t*)((char*)ws + sizeof(hq::WsHeader));
+  a.tail = a.desc + chunks;
+  a.n_chunks = (uint32_t)chunks;
+  return dev_err(hq::launch_encode(plan->lattice, dither, dtype == HQ_BF16, len_only, a, st));
+}
+
+hq_status decode_impl(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets,
+                      const uint8_t* k, uint64_t n_tiles, bool dither, uint64_t tile_base, void* y,
+                      hq_dtype out_dtype, void* ws, void* stream) {
+  if (!plan) return HQ_ERR_ARG;
+  if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (out_dtype != HQ_F32 && out_dtype != HQ_BF16) return HQ_ERR_ARG;
+  if (n_tiles == 0) return HQ_OK;
+  if (!words || !offsets || !k || !y || !ws) return HQ_ERR_ARG;
+  if (((uintptr_t)y & 15u) != 0) return HQ_ERR_ARG;
+  hq::DecArgs a{};
+  a.words = words;
+  a.n_words = n_words;
+  a.offsets = offsets;
+  a.kin = k;
+  a.n_tiles = n_tiles;
+  a.y = y;
+  fill_common(plan, a.sgn, a.key0, a.key1);
+  a.c_dec = plan->c_dec;
+  a.tile_base = tile_base;
+  a.ws = (hq::WsHeader*)ws;
+  const dim3 grid((uint32_t)hq::ws_chunks(n_tiles));
+  return dev_err(hq::launch_decode(plan->lattice, dither, out_dtype == HQ_BF16 ? hq::kOutBf16 : hq::kOutF32, a,
+                                   grid, (hipStream_t)stream));
+}
+
+// Payload rate of x at alpha a on the device (bits per scalar); +inf when the
+// step is too fine for the 2^20 code range.
+hq_status rate_at(hq_plan_s* p, float a, const void* x, hq_dtype dtype, uint64_t n_tiles, bool dither,
+                  uint64_t tile_base, void* ws, hipStream_t st, double* rate) {
+  hq_plan_s q = *p;
+  q.has_alpha = true;
+  q.alpha = a;
+  q.c_enc = (float)(1.0 / ((double)a * std::sqrt(128.0)));
+  q.c_dec = (float)((double)a / std::sqrt(128.0));
+  hq::WsHeader* h = (hq::WsHeader*)ws;
+  if (hipMemsetAsync(&h->bits, 0, sizeof(h->bits), st) != hipSuccess) return HQ_ERR_DEVICE;
+  hq_status s = encode_impl(&q, x, dtype, n_tiles, dither, tile_base, nullptr, 0, nullptr, nullptr, ws, st, true);
+  if (s != HQ_OK) return s;
+  unsigned long long bits = 0;
+  if (hipMemcpyAsync(&bits, &h->bits, sizeof(bits), hipMemcpyDeviceToHost, st) != hipSuccess) return HQ_ERR_DEVICE;
+  s = hq_status_sync(ws, st);
+  if (s == HQ_ERR_RANGE) {
+    *rate = INFINITY;
+    return HQ_ERR_RANGE;
+  }
+  if (s != HQ_OK) return s;
+  *rate = (double)bits / ((double)n_tiles * 128.0);
+  return HQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hq_status hq_plan(hq_lattice lattice, int tile, float bps, uint64_t seed, hq_plan_t* out) {
+  if (!out) return HQ_ERR_ARG;
+  *out = nullptr;
+  if (!lattice_ok(lattice) || tile != 128 || !(bps > 0.0f) || !std::isfinite(bps)) return HQ_ERR_ARG;
+  hq_plan_s* p = new (std::nothrow) hq_plan_s{};
+  if (!p) return HQ_ERR_ARG;
+  p->lattice = lattice;
+  p->bps = bps;
+  p->seed = seed;
+  uint32_t c[4] = {0u, 0u, 0u, kTagSign};
+  philox_host(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  for (int i = 0; i < 4; ++i) p->sgn[i] = c[i];
+  *out = p;
+  return HQ_OK;
+}
+
+hq_status hq_plan_set_alpha(hq_plan_t plan, float alpha) {
+  if (!plan || !(alpha > 0.0f) || !std::isfinite(alpha)) return HQ_ERR_ARG;
+  plan->alpha = alpha;
+  plan->c_enc = (float)(1.0 / ((double)alpha * std::sqrt(128.0)));
+  plan->c_dec = (float)((double)alpha / std::sqrt(128.0));
+  plan->has_alpha = true;
+  return HQ_OK;
+}
+
+hq_status hq_plan_get(hq_plan_t plan, float* alpha, float* c_enc, float* c_dec) {
+  if (!plan) return HQ_ERR_ARG;
+  if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (alpha) *alpha = plan->alpha;
+  if (c_enc) *c_enc = plan->c_enc;
+  if (c_dec) *c_dec = plan->c_dec;
+  return HQ_OK;
+}
+
+void hq_plan_destroy(hq_plan_t plan) { delete plan; }
+
+size_t hq_workspace_bytes(hq_plan_t, uint64_t n_tiles) { return (size_t)hq::ws_bytes(n_tiles); }
+
+uint64_t hq_encode_bound_words(hq_plan_t plan, uint64_t n_tiles) {
+  const int lat = plan ? plan->lattice : HQ_E8;
+  return (n_tiles * max_record_bits(lat) + 31) / 32;
+}
+
+hq_status hq_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint32_t* words,
+                    uint64_t cap_words, uint64_t* offsets, uint8_t* k, void* ws, void* stream) {
+  return encode_impl(plan, x, dtype, n_tiles, false, 0, words, cap_words, offsets, k, ws, stream, false);
+}
+
+hq_status hq_kv_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint64_t tile_base,
+                       uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k, void* ws, void* stream) {
+  return encode_impl(plan, x, dtype, n_tiles, true, tile_base, words, cap_words, offsets, k, ws, stream, false);
+}
+
+hq_status hq_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets,
+                    const uint8_t* k, uint64_t n_tiles, void* y, hq_dtype out_dtype, void* ws, void* stream) {
+  return decode_impl(plan, words, n_words, offsets, k, n_tiles, false, 0, y, out_dtype, ws, stream);
+}
+
+hq_status hq_kv_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets,
+                       const uint8_t* k, uint64_t n_tiles, uint64_t tile_base, void* y, hq_dtype out_dtype,
+                       void* ws, void* stream) {
+  return decode_impl(plan, words, n_words, offsets, k, n_tiles, true, tile_base, y, out_dtype, ws, stream);
+}
+
+hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets,
+                       const uint8_t* k, uint32_t n_heads, uint64_t tiles_per_head, uint64_t tile_base,
+                       const float* q, uint32_t qph, float* scores, void* ws, void* stream) {
+  if (!plan) return HQ_ERR_ARG;
+  if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (qph == 0 || qph > 16) return HQ_ERR_ARG;
+  if (n_heads == 0 || tiles_per_head == 0) return HQ_OK;
+  if (!words || !offsets || !k || !q || !scores || !ws) return HQ_ERR_ARG;
+  const uint64_t cph = (tiles_per_head + hq::kChunkTiles - 1) / hq::kChunkTiles;
+  if (cph > 0x7FFFFFFFull || n_heads > 65535u) return HQ_ERR_ARG;
+  hq::DecArgs a{};
+  a.words = words;
+  a.n_words = n_words;
+  a.offsets = offsets;
+  a.kin = k;
+  a.n_tiles = (uint64_t)n_heads * tiles_per_head;
+  fill_common(plan, a.sgn, a.key0, a.key1);
+  a.c_dec = plan->c_dec;
+  a.tile_base = tile_base;
+  a.ws = (hq::WsHeader*)ws;
+  a.q = q;
+  a.scores = scores;
+  a.qph = qph;
+  a.tiles_per_head = tiles_per_head;
+  return dev_err(hq::launch_decode(plan->lattice, true, hq::kOutScores, a, dim3((uint32_t)cph, n_heads),
+                                   (hipStream_t)stream));
+}
+
+hq_status hq_status_sync(void* ws, void* stream) {
+  if (!ws) return HQ_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  hq::WsHeader* h = (hq::WsHeader*)ws;
+  uint32_t bits = 0;
+  if (hipMemcpyAsync(&bits, &h->status, sizeof(bits), hipMemcpyDeviceToHost, st) != hipSuccess) return HQ_ERR_DEVICE;
+  if (hipStreamSynchronize(st) != hipSuccess) return HQ_ERR_DEVICE;
+  if (bits == 0) return HQ_OK;
+  if (hipMemsetAsync(&h->status, 0, sizeof(uint32_t), st) != hipSuccess) return HQ_ERR_DEVICE;
+  if (hipStreamSynchronize(st) != hipSuccess) return HQ_ERR_DEVICE;
+  for (int c = 1; c < 32; ++c)
+    if (bits & (1u << c)) return (hq_status)c;
+  return HQ_ERR_DEVICE;
+}
+
+const char* hq_status_str(hq_status s) {
+  switch (s) {
+    case HQ_OK: return "ok";
+    case HQ_ERR_ARG: return "invalid argument";
+    case HQ_ERR_NONFINITE: return "non-finite input";
+    case HQ_ERR_RANGE: return "scaled coordinate out of range (alpha too small)";
+    case HQ_ERR_CAPACITY: return "stream exceeds the word capacity";
+    case HQ_ERR_CORRUPT: return "corrupt stream";
+    case HQ_ERR_DEVICE: return "HIP runtime error";
+    case HQ_ERR_NOALPHA: return "plan has no alpha";
+  }
+  return "unknown status";
+}
+
+// Bisection [reading of Methodology 3]: start from the high-resolution
+// estimate alpha0 = sqrt(2 pi e) sigma / (nu 2^R) (sigma the RMS of x, nu the
+// per-dimension cell edge of the embedding), bracket the target in log2 alpha
+// from floor(log2 alpha0) -/+ 4 in steps of 4, then bisect on the exact payload
+// rate until within 0.002 bps, at most 40 times.  Each trial alpha is
+// fp32(2^mid); the closest rate wins, ties to the larger alpha.
+hq_status hq_calibrate(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, int dithered,
+                       uint64_t tile_base, void* ws, void* stream, float* alpha_out, double* bps_out) {
+  if (!plan || !x || !ws || n_tiles == 0) return HQ_ERR_ARG;
+  if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  hq::WsHeader* h = (hq::WsHeader*)ws;
+  const uint64_t n = n_tiles * 128ull;
+  if (hipMemsetAsync(&h->sumsq, 0, sizeof(double), st) != hipSuccess) return HQ_ERR_DEVICE;
+  if (hq::launch_sumsq(x, dtype == HQ_BF16, n, &h->sumsq, st) != hipSuccess) return HQ_ERR_DEVICE;
+  double ss = 0.0;
+  if (hipMemcpyAsync(&ss, &h->sumsq, sizeof(double), hipMemcpyDeviceToHost, st) != hipSuccess) return HQ_ERR_DEVICE;
+  if (hipStreamSynchronize(st) != hipSuccess) return HQ_ERR_DEVICE;
+  if (!std::isfinite(ss)) return HQ_ERR_NONFINITE;
+  const double sigma = std::sqrt(ss / (double)n);
+  if (!(sigma > 0.0)) return HQ_ERR_ARG;
+  static const double nu[4] = {1.0, 1.8612097182041991, 1.1892071150027210, 2.0};
+  const double a0 = std::sqrt(2.0 * M_PI * M_E) * sigma / (nu[plan->lattice] * std::pow(2.0, (double)plan->bps));
+  const double target = (double)plan->bps;
+  double lo = std::floor(std::log2(a0)) - 4.0, hi = std::floor(std::log2(a0)) + 4.0;
+  float best_a = 0.0f;
+  double best_r = 0.0, best_err = INFINITY;
+  auto consider = [&](float a, double r) {
+    const double e = std::fabs(r - target);
+    if (e < best_err || (e == best_err && a > best_a)) {
+      best_err = e;
+      best_a = a;
+      best_r = r;
+    }
+  };
+  double r = 0.0;
+  for (int g = 0; g < 16; ++g) {
+    const float a = (float)std::exp2(lo);
+    const hq_status s = rate_at(plan, a, x, dtype, n_tiles, dithered != 0, tile_base, ws, st, &r);
+    if (s != HQ_OK && s != HQ_ERR_RANGE) return s;
+    if (s == HQ_OK) consider(a, r);
+    if (r >= target) break;
+    lo -= 4.0;
+  }
+  for (int g = 0; g < 16; ++g) {
+    const float a = (float)std::exp2(hi);
+    const hq_status s = rate_at(plan, a, x, dtype, n_tiles, dithered != 0, tile_base, ws, st, &r);
+    if (s != HQ_OK && s != HQ_ERR_RANGE) return s;
+    if (s == HQ_OK) consider(a, r);
+    if (r <= target) break;
+    hi += 4.0;
+  }
+  for (int it = 0; it < 40 && best_err > 0.002; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    const float a = (float)std::exp2(mid);
+    const hq_status s = rate_at(plan, a, x, dtype, n_tiles, dithered != 0, tile_base, ws, st, &r);
+    if (s != HQ_OK && s != HQ_ERR_RANGE) return s;
+    if (s == HQ_OK) consider(a, r);
+    if (r > target) lo = mid;
+    else hi = mid;
+  }
+  if (!(best_a > 0.0f)) return HQ_ERR_RANGE;
+  hq_plan_set_alpha(plan, best_a);
+  if (alpha_out) *alpha_out = best_a;
+  if (bps_out) *bps_out = best_r;
+  return HQ_OK;
+}
+
+}  // extern "C"

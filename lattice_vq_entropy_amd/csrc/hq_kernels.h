@@ -1,0 +1,51 @@
+// hq_kernels.h -- kernel argument blocks and launchers (internal to libhq).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hq_ws.h"
+
+namespace hq {
+
+constexpr int kOutF32 = 0, kOutBf16 = 1, kOutScores = 2;
+
+struct EncArgs {
+  const void* x;
+  uint64_t n_tiles;
+  uint32_t* words;
+  uint64_t cap_words;
+  uint64_t* offsets;
+  uint8_t* kout;
+  uint32_t sgn[4];  // bit i of the 128: coordinate i of D is -1
+  float c_enc;
+  uint32_t key0, key1;
+  uint64_t tile_base;
+  WsHeader* ws;
+  uint64_t* desc;
+  uint64_t* tail;  // (epoch << 32) | last 32 bits of each chunk
+  uint32_t n_chunks;
+};
+
+struct DecArgs {
+  const uint32_t* words;
+  uint64_t n_words;
+  const uint64_t* offsets;
+  const uint8_t* kin;
+  uint64_t n_tiles;
+  void* y;
+  uint32_t sgn[4];
+  float c_dec;
+  uint32_t key0, key1;
+  uint64_t tile_base;
+  WsHeader* ws;
+  const float* q;
+  float* scores;
+  uint32_t qph;
+  uint64_t tiles_per_head;
+};
+
+hipError_t launch_encode(int lat, bool dither, bool bf16, bool len_only, const EncArgs& a, hipStream_t st);
+hipError_t launch_decode(int lat, bool dither, int out, const DecArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* out, hipStream_t st);
+
+}  // namespace hq

@@ -643,7 +643,9 @@ int orc_kv_scores(int lat, uint64_t seed, float alpha, const uint32_t *words,
 /* high-resolution estimate alpha0 = sqrt(2 pi e) sigma / (nu 2^R), with     */
 /* sigma the RMS of the tensor and nu the per-dimension cell edge of the     */
 /* embedding (Z 1, A2 sqrt(2 sqrt3), D4 2^(1/4), 2E8 2); bracket the target  */
-/* in log2(alpha) with steps of 4, then bisect on the exact payload rate     */
+/* in log2(alpha) from floor(log2 alpha0) -/+ 4 (an integer, so the bracket  */
+/* does not depend on the rounding of sigma) in steps of 4, then bisect on   */
+/* the exact payload rate                                                    */
 /* until it is within 0.002 bps, at most 40 times.  The fp32 alpha with the  */
 /* closest rate wins; ties go to the larger alpha.                           */
 /* ------------------------------------------------------------------------ */
@@ -672,7 +674,7 @@ int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,
                                1.1892071150027210 /* 2^(1/4) */, 2.0};
   double a0 = sqrt(2.0 * M_PI * M_E) * sigma / (nu[lat] * pow(2.0, (double)bps));
   double target = (double)bps;
-  double lo = log2(a0) - 4.0, hi = log2(a0) + 4.0;
+  double lo = floor(log2(a0)) - 4.0, hi = floor(log2(a0)) + 4.0;
   int st, iters = 0;
   float best_a = 0.0f;
   double best_r = 0.0, best_err = INFINITY;

@@ -1,0 +1,66 @@
+"""Host-side checks of the libhq C ABI (no GPU needed): the library loads,
+exports every function include/hq.h declares, and validates its arguments on
+the host before touching a device."""
+import ctypes as C
+
+import pytest
+
+
+@pytest.fixture(scope="module")
+def hq():
+    import lattice_vq_entropy_amd as hq
+    hq.lib()
+    return hq
+
+
+def test_every_declared_function_is_exported(hq):
+    names = hq.header_functions()
+    assert len(names) >= 14
+    L = hq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_plan_lifecycle_and_constants(hq):
+    p = hq.Plan("E8", 4.0, 0x5EED0001)
+    with pytest.raises(hq.HQError) as e:
+        p.get()
+    assert e.value.code == hq.ERR_NOALPHA
+    p.set_alpha(0.0057)
+    a, ce, cd = p.get()
+    assert a == pytest.approx(0.0057, rel=1e-7)
+    assert ce * a * 128 ** 0.5 == pytest.approx(1.0, rel=1e-6)
+    assert cd / a * 128 ** 0.5 == pytest.approx(1.0, rel=1e-6)
+    # c_enc/c_dec are the same fp32 constants the oracle derives
+    from oracle import oracle as O
+    assert (ce, cd) == O.scales(a)
+
+
+def test_sizes(hq):
+    p = hq.Plan("E8", 4.0, 1)
+    assert p.bound_words(1) == (16 + 128 * 23 + 31) // 32
+    assert p.bound_words(1000) == (1000 * (16 + 128 * 23) + 31) // 32
+    assert hq.Plan("Z", 4.0, 1).bound_words(32) == 32 * 128 * 23 // 32
+    assert p.workspace_bytes(1) >= 256 + 16
+    assert p.workspace_bytes(4096) >= 256 + 128 * 16
+
+
+def test_argument_errors_are_synchronous(hq):
+    L = hq.lib()
+    h = C.c_void_p(0)
+    assert L.hq_plan(7, 128, 4.0, 1, C.byref(h)) == hq.ERR_ARG
+    assert L.hq_plan(3, 64, 4.0, 1, C.byref(h)) == hq.ERR_ARG
+    assert L.hq_plan(3, 128, -1.0, 1, C.byref(h)) == hq.ERR_ARG
+    p = hq.Plan("D4", 2.0, 1)
+    assert L.hq_plan_set_alpha(p.handle, 0.0) == hq.ERR_ARG
+    assert L.hq_plan_set_alpha(p.handle, float("nan")) == hq.ERR_ARG
+    # no alpha yet
+    assert L.hq_encode(p.handle, None, 1, 4, None, 0, None, None, None, None) == hq.ERR_NOALPHA
+    p.set_alpha(0.5)
+    # null workspace / pointers, bad dtype
+    assert L.hq_encode(p.handle, None, 1, 4, None, 0, None, None, None, None) == hq.ERR_ARG
+    assert L.hq_encode(p.handle, None, 5, 4, None, 0, None, None, C.c_void_p(256), None) == hq.ERR_ARG
+    assert L.hq_decode(p.handle, None, 0, None, None, 4, None, 0, None, None) == hq.ERR_ARG
+    assert L.hq_kv_scores(p.handle, None, 0, None, None, 1, 1, 0, None, 17, None, None, None) == hq.ERR_ARG
+    assert L.hq_status_sync(None, None) == hq.ERR_ARG
+    assert hq.status_str(hq.ERR_CORRUPT) == "corrupt stream"

@@ -1,0 +1,253 @@
+"""GPU parity of libhq (through its C ABI) against the oracle.
+
+Bar: bit-exact for the bitstream words, per-tile offsets and Rice parameters,
+and (because both sides use the same fp32 operations in the same order) for
+the fp32 and bf16 reconstructions; fused scores within the fp32 rounding bound
+1e-5 * c_dec * ||H D q|| * ||u_hat|| of the oracle's fp64 value.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0x5EED0001
+NU = {0: 1.0, 1: math.sqrt(2 * math.sqrt(3)), 2: 2 ** 0.25, 3: 2.0}
+
+
+@pytest.fixture(scope="module")
+def hq():
+    import lattice_vq_entropy_amd as hq
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    hq.lib()
+    return hq
+
+
+@pytest.fixture(scope="module")
+def orc():
+    from oracle import oracle as O
+    O.lib()
+    return O
+
+
+def alpha_for(lat, sigma, bps):
+    """High-resolution step for a target rate (no calibration needed)."""
+    return float(np.float32(math.sqrt(2 * math.pi * math.e) * sigma / (NU[lat] * 2.0 ** bps)))
+
+
+def host_input(x: torch.Tensor) -> np.ndarray:
+    x = x.detach().contiguous().cpu()
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    return x.numpy().reshape(-1)
+
+
+def gpu_stream(enc):
+    torch.cuda.synchronize()
+    total = enc.total_bits()
+    words = enc.words.cpu().numpy().view(np.uint32)[: (total + 31) // 32]
+    offsets = enc.offsets.cpu().numpy().view(np.uint64)
+    k = enc.k.cpu().numpy()[: enc.n_tiles]
+    return words, offsets, k
+
+
+def bits_of(words: np.ndarray, start: int, length: int) -> int:
+    w0, w1 = start >> 5, (start + length + 31) >> 5
+    val = int.from_bytes(words[w0:w1].astype("<u4").tobytes(), "little")
+    return (val >> (start & 31)) & ((1 << length) - 1)
+
+
+def as_f32(a: np.ndarray, code: int) -> np.ndarray:
+    return a.view(np.float32) if code == 0 else (a.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def assert_same_values(gpu: np.ndarray, orc_out: np.ndarray, code: int):
+    """Reconstructions must be equal as numbers (every bit but the sign of an
+    exact zero, which IEEE arithmetic leaves to the operation order)."""
+    g, o = as_f32(gpu, code), as_f32(orc_out, code)
+    assert not np.isnan(g).any()
+    bad = np.flatnonzero(g != o)
+    assert bad.size == 0, f"decode differs at {bad[:8]}: {g[bad[:4]]} vs {o[bad[:4]]}"
+    nz = o != 0
+    assert np.array_equal(g.view(np.uint32)[nz], o.view(np.uint32)[nz])
+
+
+def full_parity(hq, orc, lat, x, alpha, dithered=False, tile_base=0, decode=True):
+    """Encode and decode x on the GPU and with the oracle; compare everything."""
+    plan = hq.Plan(lat, 4.0, SEED).set_alpha(alpha)
+    n = x.numel() // 128
+    ws = plan.workspace(n)
+    enc = hq.encode(plan, x, ws, dithered=dithered, tile_base=tile_base)
+    assert hq.status_sync(ws) == hq.OK
+    words, offsets, k = gpu_stream(enc)
+    st, ow, oo, ok = orc.encode(lat, SEED, alpha, host_input(x), dithered=dithered, tile_base=tile_base)
+    assert st == 0
+    assert np.array_equal(offsets, oo), "offsets differ"
+    assert np.array_equal(k, ok), "Rice parameters differ"
+    assert np.array_equal(words, ow), f"words differ at {np.flatnonzero(words != ow)[:8]}"
+    if decode:
+        for dt, code in ((torch.float32, 0), (torch.bfloat16, 1)):
+            y = hq.decode(plan, enc, ws, out_dtype=dt)
+            assert hq.status_sync(ws) == hq.OK
+            st, oy = orc.decode(lat, SEED, alpha, ow, oo, ok, dithered=dithered, tile_base=tile_base,
+                                out_dtype=code)
+            assert st == 0
+            assert_same_values(host_input(y), oy, code)
+    return enc
+
+
+def test_c1_config_bit_exact(hq, orc):
+    """fp32 [4096, 128], E8 at the fixed alpha of the 4-bps operating point."""
+    from lattice_vq_entropy_amd import workloads as W
+    x = W.c1("cpu").cuda()
+    alpha = float(np.float32(math.sqrt(2 * math.pi * math.e) * W.c1_sigma_eff() / (2.0 * 16.0)))
+    full_parity(hq, orc, 3, x, alpha)
+
+
+@pytest.mark.parametrize("lat", [0, 1, 2, 3])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dithered", [False, True])
+def test_lattice_parity_ragged(hq, orc, lat, dtype, dithered):
+    """1000 tiles (not a multiple of the 32-tile chunk) of the c2 distribution."""
+    from lattice_vq_entropy_amd import workloads as W
+    x = W.c2("cpu", rows=250, cols=512, seed=77 + lat).to(dtype).cuda()
+    sigma = float(x.float().pow(2).mean().sqrt())
+    bps = {0: 5.0, 1: 3.0, 2: 2.0, 3: 4.0}[lat]
+    full_parity(hq, orc, lat, x, alpha_for(lat, sigma, bps), dithered=dithered, tile_base=12345 if dithered else 0)
+
+
+@pytest.mark.parametrize("n_tiles", [1, 31, 32, 33, 97])
+def test_small_and_ragged_sizes(hq, orc, n_tiles):
+    g = torch.Generator().manual_seed(n_tiles)
+    x = (torch.randn(n_tiles, 128, generator=g) * 0.3).to(torch.bfloat16).cuda()
+    full_parity(hq, orc, 3, x, alpha_for(3, 0.3, 4.0))
+
+
+def test_wide_dynamic_range_paths(hq, orc):
+    """Tiles whose Rice parameter exceeds 8 and tiles whose lanes hold more
+    than 64 unary bits take the general packing and parsing paths."""
+    import scipy.linalg
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(128, 128, generator=g) * 0.01
+    x[0:32] *= 3000.0          # k > 8 at this alpha
+    # tiles whose transform is one spike (x = D H e_j A): one huge symbol among
+    # zeros gives a lane far more than 64 unary bits
+    H = torch.tensor(scipy.linalg.hadamard(128), dtype=torch.float32)
+    s = torch.tensor(orc.signs(SEED))
+    for i, t in enumerate(range(64, 96)):
+        x[t] = s * H[:, (7 * i) % 128] * (0.05 * (i + 1))
+    x[100] = 0.0               # all-zero tile
+    x[101] = 1e-30             # tiny values
+    x = x.cuda()
+    full_parity(hq, orc, 3, x, 0.002)
+    full_parity(hq, orc, 0, x, 0.002)
+
+
+def test_exact_ties(hq, orc):
+    """Inputs whose RHT lands on half-integers and lattice points exercise the
+    tie rules, which both sides must resolve identically."""
+    x = torch.zeros(64, 128)
+    x[:, 0] = torch.arange(64, dtype=torch.float32) * 0.5
+    x[:32, 1] = 0.25
+    x = x.cuda()
+    for lat in range(4):
+        full_parity(hq, orc, lat, x, float(1.0 / math.sqrt(128.0)))
+
+
+def test_workspace_reuse_and_determinism(hq, orc):
+    from lattice_vq_entropy_amd import workloads as W
+    plan = hq.Plan(3, 4.0, SEED).set_alpha(0.003)
+    big = W.c2("cuda", rows=512, cols=4096, seed=9)
+    small = W.c2("cuda", rows=16, cols=1024, seed=10)
+    ws = plan.workspace(big.numel() // 128)
+    ref_big = gpu_stream(hq.encode(plan, big, ws))
+    ref_small = gpu_stream(hq.encode(plan, small, ws))
+    for i in range(12):
+        x, ref = (big, ref_big) if i % 3 else (small, ref_small)
+        got = gpu_stream(hq.encode(plan, x, ws))
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b)
+    assert hq.status_sync(ws) == hq.OK
+
+
+def test_kv_scores(hq, orc):
+    from lattice_vq_entropy_amd import workloads as W
+    heads, seq, qph = 2, 1000, 4
+    k, _, q = W.c5("cpu", heads=heads, seq=seq, q_per_head=qph, seed=55)
+    alpha = alpha_for(3, float(k.float().pow(2).mean().sqrt()), 1.7)
+    plan = hq.Plan(3, 1.7, SEED).set_alpha(alpha)
+    kd, qd = k.cuda(), q.cuda()
+    ws = plan.workspace(heads * seq)
+    enc = hq.encode(plan, kd, ws, dithered=True, tile_base=777)
+    sc = hq.kv_scores(plan, enc, heads, seq, qd, qph, ws)
+    assert hq.status_sync(ws) == hq.OK
+    # the oracle encodes on its own; the GPU stream is only compared with it
+    st, words, offsets, kk = orc.encode(3, SEED, alpha, host_input(k), dithered=True, tile_base=777)
+    assert st == 0
+    gw, go, gk = gpu_stream(enc)
+    assert np.array_equal(gw, words) and np.array_equal(go, offsets) and np.array_equal(gk, kk)
+    st, osc = orc.kv_scores(3, SEED, alpha, words, offsets, kk, heads, seq, 777, q.numpy(), qph)
+    assert st == 0
+    _, _, c_dec = plan.get()
+    qn = np.linalg.norm(q.numpy().astype(np.float64), axis=1) * math.sqrt(128.0)
+    un = np.zeros(heads * seq)
+    for t in range(heads * seq):
+        st, uh = orc.dequant_rotated(3, SEED, words, int(offsets[t]), int(offsets[t + 1]), int(kk[t]),
+                                     dithered=True, tile_id=777 + t)
+        un[t] = np.linalg.norm(uh.astype(np.float64))
+    bound = 1e-5 * c_dec * qn[:, None] * un.reshape(heads, seq).repeat(qph, 0)
+    err = np.abs(sc.cpu().numpy().astype(np.float64) - osc)
+    assert np.all(err <= bound), float((err / bound).max())
+
+
+@pytest.mark.parametrize("lat,bps,dithered", [(3, 4.0, False), (2, 2.0, True), (1, 3.0, False)])
+def test_calibrate_matches_oracle(hq, orc, lat, bps, dithered):
+    from lattice_vq_entropy_amd import workloads as W
+    x = W.c2("cpu", rows=64, cols=1024, seed=3)
+    plan = hq.Plan(lat, bps, SEED)
+    xd = x.cuda()
+    ws = plan.workspace(x.numel() // 128)
+    a, r = plan.calibrate(xd, ws, dithered=dithered, tile_base=5)
+    st, oa, orate, _ = orc.calibrate(lat, SEED, bps, host_input(x), dithered=dithered, tile_base=5)
+    assert st == 0
+    assert (a, r) == (oa, orate)
+    assert abs(r - bps) <= 0.002
+
+
+def test_error_statuses(hq, orc):
+    plan = hq.Plan(3, 4.0, SEED).set_alpha(0.003)
+    x = (torch.randn(40, 128) * 0.02).cuda()
+    ws = plan.workspace(40)
+    bad = x.clone()
+    bad[17, 3] = float("nan")
+    hq.encode(plan, bad, ws)
+    assert hq.status_sync(ws) == hq.ERR_NONFINITE
+    bad[17, 3] = 1e6
+    hq.encode(plan, bad, ws)
+    assert hq.status_sync(ws) == hq.ERR_RANGE
+    enc = hq.encode(plan, x, ws)
+    assert hq.status_sync(ws) == hq.OK
+    need = enc.used_words()
+    hq.encode(plan, x, ws, cap_words=need - 1)
+    assert hq.status_sync(ws) == hq.ERR_CAPACITY
+    enc = hq.encode(plan, x, ws)  # the workspace still works after errors
+    assert hq.status_sync(ws) == hq.OK
+    words, offsets, k = gpu_stream(enc)
+    st, ow, oo, ok = orc.encode(3, SEED, 0.003, host_input(x))
+    assert np.array_equal(words, ow) and np.array_equal(offsets, oo)
+    # corrupt stream: a wrong Rice parameter, then a truncated record
+    enc.k[5] = (int(enc.k[5].item()) + 1) % 23
+    hq.decode(plan, enc, ws)
+    assert hq.status_sync(ws) == hq.ERR_CORRUPT
+    enc.k[5] = int(ok[5])
+    enc.offsets[6] -= 1
+    hq.decode(plan, enc, ws)
+    assert hq.status_sync(ws) == hq.ERR_CORRUPT
+    enc.offsets[6] += 1
+    hq.decode(plan, enc, ws)
+    assert hq.status_sync(ws) == hq.OK
+    # empty input
+    e0 = hq.encode(plan, torch.empty(0, 128, device="cuda"), ws)
+    assert hq.status_sync(ws) == hq.OK and e0.offsets[0].item() == 0
