@@ -5,7 +5,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <unordered_map>
 
 #include "../../include/hq.h"
 #include "hq_kernels.h"
@@ -47,6 +49,18 @@ bool lattice_ok(int lat) { return lat >= HQ_Z && lat <= HQ_E8; }
 
 hq_status dev_err(hipError_t e) { return e == hipSuccess ? HQ_OK : HQ_ERR_DEVICE; }
 
+// Calls on one workspace are stream-ordered, so the host numbers them: the
+// number tags the look-back words of that call (1 .. 2^24-1, never 0, so a
+// zero-filled workspace never matches).
+uint32_t next_epoch(void* ws) {
+  static std::mutex mu;
+  static std::unordered_map<void*, uint32_t> epochs;
+  std::lock_guard<std::mutex> g(mu);
+  uint32_t& e = epochs[ws];
+  e = e % 0xFFFFFFu + 1u;
+  return e;
+}
+
 void fill_common(const hq_plan_s* p, uint32_t sgn[4], uint32_t& k0, uint32_t& k1) {
   for (int i = 0; i < 4; ++i) sgn[i] = p->sgn[i];
   k0 = (uint32_t)p->seed;
@@ -85,7 +99,9 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   const uint64_t chunks = hq::ws_chunks(n_tiles);
   a.desc = (uint64_t*)((char*)ws + sizeof(hq::WsHeader));
   a.tail = a.desc + chunks;
+  a.partials = (unsigned long long*)a.desc;
   a.n_chunks = (uint32_t)chunks;
+  a.epoch = len_only ? 0u : next_epoch(ws);
   return dev_err(hq::launch_encode(plan->lattice, dither, dtype == HQ_BF16, len_only, a, st));
 }
 
@@ -124,7 +140,6 @@ hq_status rate_at(hq_plan_s* p, float a, const void* x, hq_dtype dtype, uint64_t
   q.c_enc = (float)(1.0 / ((double)a * std::sqrt(128.0)));
   q.c_dec = (float)((double)a / std::sqrt(128.0));
   hq::WsHeader* h = (hq::WsHeader*)ws;
-  if (hipMemsetAsync(&h->bits, 0, sizeof(h->bits), st) != hipSuccess) return HQ_ERR_DEVICE;
   hq_status s = encode_impl(&q, x, dtype, n_tiles, dither, tile_base, nullptr, 0, nullptr, nullptr, ws, st, true);
   if (s != HQ_OK) return s;
   unsigned long long bits = 0;
@@ -277,8 +292,11 @@ hq_status hq_calibrate(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n
   hipStream_t st = (hipStream_t)stream;
   hq::WsHeader* h = (hq::WsHeader*)ws;
   const uint64_t n = n_tiles * 128ull;
-  if (hipMemsetAsync(&h->sumsq, 0, sizeof(double), st) != hipSuccess) return HQ_ERR_DEVICE;
-  if (hq::launch_sumsq(x, dtype == HQ_BF16, n, &h->sumsq, st) != hipSuccess) return HQ_ERR_DEVICE;
+  double* partials = (double*)((char*)ws + sizeof(hq::WsHeader));
+  const uint64_t chunks = hq::ws_chunks(n_tiles);
+  if (hq::launch_sumsq(x, dtype == HQ_BF16, n, partials, (uint32_t)(chunks < 1024 ? chunks : 1024), &h->sumsq, st) !=
+      hipSuccess)
+    return HQ_ERR_DEVICE;
   double ss = 0.0;
   if (hipMemcpyAsync(&ss, &h->sumsq, sizeof(double), hipMemcpyDeviceToHost, st) != hipSuccess) return HQ_ERR_DEVICE;
   if (hipStreamSynchronize(st) != hipSuccess) return HQ_ERR_DEVICE;

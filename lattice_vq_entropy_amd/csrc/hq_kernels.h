@@ -23,7 +23,9 @@ struct EncArgs {
   WsHeader* ws;
   uint64_t* desc;
   uint64_t* tail;  // (epoch << 32) | last 32 bits of each chunk
+  unsigned long long* partials;  // length-only pass: bits per work-group
   uint32_t n_chunks;
+  uint32_t epoch;  // tag of this call's look-back words, 1 .. 2^24-1
 };
 
 struct DecArgs {
@@ -46,6 +48,7 @@ struct DecArgs {
 
 hipError_t launch_encode(int lat, bool dither, bool bf16, bool len_only, const EncArgs& a, hipStream_t st);
 hipError_t launch_decode(int lat, bool dither, int out, const DecArgs& a, dim3 grid, hipStream_t st);
-hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* out, hipStream_t st);
+hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
+                        hipStream_t st);
 
 }  // namespace hq

@@ -108,18 +108,13 @@ __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
     for (int i = 0; i < 8; ++i) smask[i] = ((sbyte >> i) & 1u) << 31;
   }
 
-  uint32_t chunk, epoch = 0;
-  if constexpr (LEN_ONLY) {
-    chunk = blockIdx.x;
-  } else {
-    if (tid == 0) {
-      s_misc[0] = __hip_atomic_fetch_add(&a.ws->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_misc[1] = __hip_atomic_load(&a.ws->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    chunk = s_misc[0];
-    epoch = s_misc[1] % 0xFFFFFFu + 1u;  // 24-bit tag, never 0 (zero-filled words never match)
-  }
+  // Persistent grid: every work-group is resident (cooperative launch) and
+  // walks chunks blockIdx.x, blockIdx.x + gridDim.x, ... in order, so a
+  // chunk's look-back only ever waits on lower chunks that are being or have
+  // been processed.  The epoch tags this call's look-back words.
+  const uint32_t epoch = a.epoch;
+  uint64_t len_acc = 0;
+  for (uint32_t chunk = blockIdx.x; chunk < a.n_chunks; chunk += gridDim.x) {
   const uint64_t t_first = (uint64_t)chunk * kChunkTiles;
 
   uint32_t m[kPasses][8];
@@ -219,9 +214,16 @@ __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
   const uint32_t A = s_lo[kChunkTiles];
 
   if constexpr (LEN_ONLY) {
-    if (tid == 0) atomicAdd(&a.ws->bits, (unsigned long long)A);
-    return;
+    len_acc += A;
   } else {
+    // Publish this chunk's aggregate as soon as it is known, so successors'
+    // look-backs progress while the chunk packs its bits.  Every word
+    // exchanged between work-groups carries the call's epoch, so relaxed
+    // device-scope atomics suffice (no cache-wide release/acquire).
+    const uint64_t ep = (uint64_t)epoch << kDescEpochShift;
+    if (tid == 0)
+      __hip_atomic_store(&a.desc[chunk], (chunk == 0 ? kDescFlagIncl : kDescFlagAgg) | ep | (uint64_t)A,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t nz = ((A + 31u) >> 5) + 2u;
     for (uint32_t i = tid; i < nz; i += 256) s_stage[1 + i] = 0u;
     __syncthreads();
@@ -288,49 +290,54 @@ __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
     }
     __syncthreads();
 
-    // publish the aggregate (with the last 32 bits of the local stream) and
-    // look back for the exclusive prefix; wave 0 only
+    // publish the last 32 bits of the local stream, then look back for the
+    // exclusive prefix (wave 0; 4 descriptors per lane, 256 per round)
     if (wv == 0) {
       uint64_t excl = 0;
-      uint32_t tailv = 0;
-      {
+      if (lane == 0) {
         const uint32_t b = A - 32u;  // A >= 128: every chunk holds a tile
         const uint32_t w = 1 + (b >> 5), sh = b & 31;
-        tailv = sh ? __builtin_amdgcn_alignbit(s_stage[w + 1], s_stage[w], sh) : s_stage[w];
-      }
-      // Every word exchanged between work-groups carries the call's epoch, so
-      // relaxed device-scope atomics suffice: no cache-wide release/acquire.
-      const uint64_t ep = (uint64_t)epoch << kDescEpochShift;
-      if (lane == 0)
+        const uint32_t tailv = sh ? __builtin_amdgcn_alignbit(s_stage[w + 1], s_stage[w], sh) : s_stage[w];
         __hip_atomic_store(&a.tail[chunk], ((uint64_t)epoch << 32) | tailv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (chunk == 0) {
-        if (lane == 0)
-          __hip_atomic_store(&a.desc[0], kDescFlagIncl | ep | (uint64_t)A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        if (lane == 0)
-          __hip_atomic_store(&a.desc[chunk], kDescFlagAgg | ep | (uint64_t)A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        int64_t j = (int64_t)chunk - 1;
+      }
+      if (chunk > 0) {
+        int64_t j = (int64_t)chunk - 1;  // newest descriptor of the window
         while (true) {
-          const int64_t idx = j - lane;
-          uint64_t d = 0;
-          if (idx >= 0) d = __hip_atomic_load(&a.desc[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const uint32_t dep = (uint32_t)(d >> kDescEpochShift) & 0xFFFFFFu;
-          const uint64_t flag = d >> 62;
-          const bool rdy = idx < 0 || (flag != 0 && dep == epoch);
-          const bool isP = idx < 0 || (rdy && flag == 2);
-          const uint64_t bp = __ballot(isP), br = __ballot(rdy);
-          const int fp = bp ? __builtin_ctzll(bp) : 64;
-          const uint64_t need = fp >= 63 ? ~0ull : ((2ull << fp) - 1ull);
+          uint64_t val[4];
+          bool rdy[4], isP[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t idx = j - 4 * lane - q;
+            const uint64_t d = idx >= 0 ? __hip_atomic_load(&a.desc[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+            const uint32_t dep = (uint32_t)(d >> kDescEpochShift) & 0xFFFFFFu;
+            const uint64_t flag = d >> 62;
+            rdy[q] = idx < 0 || (flag != 0 && dep == epoch);
+            isP[q] = idx < 0 || (rdy[q] && flag == 2);
+            val[q] = idx >= 0 ? (d & kDescValueMask) : 0ull;
+          }
+          int qp = 4;  // first inclusive descriptor of this lane (newest first)
+#pragma unroll
+          for (int q = 3; q >= 0; --q) qp = isP[q] ? q : qp;
+          bool lane_rdy = true;
+          uint64_t upto = 0, all4 = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (q <= qp) { lane_rdy &= rdy[q]; upto += val[q]; }
+            all4 += val[q];
+          }
+          const uint64_t bp = __ballot(qp < 4), br = __ballot(lane_rdy);
+          const int fl = bp ? __builtin_ctzll(bp) : 64;
+          const uint64_t need = fl >= 63 ? ~0ull : ((2ull << fl) - 1ull);
           if ((br & need) != need) {
             __builtin_amdgcn_s_sleep(1);
             continue;
           }
-          uint64_t contrib = (lane <= fp && idx >= 0) ? (d & kDescValueMask) : 0ull;
+          uint64_t contrib = lane < fl ? all4 : (lane == fl ? upto : 0ull);
 #pragma unroll
           for (int o = 32; o >= 1; o >>= 1) contrib += __shfl_xor(contrib, o);
           excl += contrib;
-          if (fp < 64) break;
-          j -= 64;
+          if (fl < 64) break;
+          j -= 256;
         }
         if (lane == 0)
           __hip_atomic_store(&a.desc[chunk], kDescFlagIncl | ep | (excl + A), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -371,16 +378,11 @@ __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
       a.words[w] = sh ? __builtin_amdgcn_alignbit(s_stage[1 + i], s_stage[i], 32 - sh) : s_stage[1 + i];
     }
 
-    // The last work-group to finish re-arms the ticket counter and advances
-    // the epoch for the next call (kernel completion publishes the stores).
-    if (tid == 0) {
-      const uint32_t dn = __hip_atomic_fetch_add(&a.ws->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (dn == a.n_chunks - 1) {
-        __hip_atomic_store(&a.ws->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.ws->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.ws->epoch, a.ws->epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+  }
+  __syncthreads();  // the chunk's LDS is reused by the next chunk
+  }
+  if constexpr (LEN_ONLY) {
+    if (tid == 0) a.partials[blockIdx.x] = len_acc;
   }
 }
 
@@ -611,8 +613,10 @@ __global__ __launch_bounds__(256) void decode_k(DecArgs a) {
   }
 }
 
-// Sum of squares (fp64) for the calibration start point.
-__global__ __launch_bounds__(256) void sumsq_k(const void* x, int bf16, uint64_t n, double* out) {
+// Sum of squares (fp64) for the calibration start point: one partial per
+// work-group (no same-address atomics), reduced in a fixed order.
+__global__ __launch_bounds__(256) void sumsq_k(const void* x, int bf16, uint64_t n, double* partials) {
+  __shared__ double s_w[4];
   double acc = 0.0;
   for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (uint64_t)gridDim.x * 256) {
     float f = bf16 ? __builtin_bit_cast(float, (uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16)
@@ -620,18 +624,55 @@ __global__ __launch_bounds__(256) void sumsq_k(const void* x, int bf16, uint64_t
     acc += (double)f * (double)f;
   }
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if ((threadIdx.x & 63) == 0) atomicAdd(out, acc);
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blockIdx.x] = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_k(const T* p, uint32_t n, T* out) {
+  __shared__ T s[256];
+  T acc = 0;
+  for (uint32_t i = threadIdx.x; i < n; i += 256) acc += p[i];
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) s[threadIdx.x] += s[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = s[0];
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Work-groups of a kernel that fit on the device at once.
+template <typename K>
+static uint32_t coresident_blocks(K kernel) {
+  int dev = 0, cus = 0, nb = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 256, 0) != hipSuccess) return 0;
+  return (uint32_t)(nb * cus);
+}
+
 template <int L, bool DITHER, bool BF16>
-static hipError_t launch_encode_t(const EncArgs& a, bool len_only, hipStream_t st) {
-  const uint32_t grid = a.n_chunks;
-  if (len_only) hipLaunchKernelGGL((encode_k<L, DITHER, BF16, true>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((encode_k<L, DITHER, BF16, false>), dim3(grid), dim3(256), 0, st, a);
-  return hipGetLastError();
+static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
+  if (len_only) {
+    auto k = encode_k<L, DITHER, BF16, true>;
+    static uint32_t cap = coresident_blocks(k);
+    const uint32_t grid = a.n_chunks < cap ? a.n_chunks : (cap ? cap : 1u);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(reduce_k<unsigned long long>, dim3(1), dim3(256), 0, st,
+                       (const unsigned long long*)a.partials, grid, &a.ws->bits);
+    return hipGetLastError();
+  }
+  auto k = encode_k<L, DITHER, BF16, false>;
+  static uint32_t cap = coresident_blocks(k);
+  if (cap == 0) return hipErrorInvalidConfiguration;
+  const uint32_t grid = a.n_chunks < cap ? a.n_chunks : cap;
+  void* args[] = {&a};
+  return hipLaunchCooperativeKernel((const void*)k, dim3(grid), dim3(256), args, 0, st);
 }
 
 hipError_t launch_encode(int lat, bool dither, bool bf16, bool len_only, const EncArgs& a, hipStream_t st) {
@@ -665,11 +706,13 @@ hipError_t launch_decode(int lat, bool dither, int out, const DecArgs& a, dim3 g
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* out, hipStream_t st) {
+hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
+                        hipStream_t st) {
   uint64_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > max_blocks) blocks = max_blocks;
   if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(sumsq_k, dim3((uint32_t)blocks), dim3(256), 0, st, x, bf16 ? 1 : 0, n, out);
+  hipLaunchKernelGGL(sumsq_k, dim3((uint32_t)blocks), dim3(256), 0, st, x, bf16 ? 1 : 0, n, partials);
+  hipLaunchKernelGGL(reduce_k<double>, dim3(1), dim3(256), 0, st, (const double*)partials, (uint32_t)blocks, out);
   return hipGetLastError();
 }
 
