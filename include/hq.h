@@ -30,6 +30,10 @@
  *   - Workspace: a device buffer of hq_workspace_bytes() bytes, zero-filled
  *     by the caller once before its first use.  One workspace must not be
  *     used by two calls that can run concurrently (e.g. on two streams).
+ *   - hq_encode has no device-wide wait that depends on scheduling: a
+ *     work-group that waits too long on a predecessor's bit count recomputes
+ *     it.  The environment variable HQ_LOOKBACK_SPINS (default 512) sets how
+ *     long it waits; 0 recomputes at once (a test setting).
  *   - Tensors are row-major; every 128 consecutive elements form one tile
  *     (weights: tiles along rows; KV [B, H, S, 128]: one tile per vector).
  *   - Stream layout: record of tile t at bits [offsets[t], offsets[t+1]):

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -52,6 +53,14 @@ hq_status dev_err(hipError_t e) { return e == hipSuccess ? HQ_OK : HQ_ERR_DEVICE
 // Calls on one workspace are stream-ordered, so the host numbers them: the
 // number tags the look-back words of that call (1 .. 2^24-1, never 0, so a
 // zero-filled workspace never matches).
+// Rounds a work-group waits on an unready predecessor before recomputing its
+// aggregate itself (environment HQ_LOOKBACK_SPINS; 0 forces recomputation).
+uint32_t lookback_spins() {
+  const char* e = std::getenv("HQ_LOOKBACK_SPINS");
+  if (!e || !*e) return 512u;
+  return (uint32_t)std::strtoul(e, nullptr, 10);
+}
+
 uint32_t next_epoch(void* ws) {
   static std::mutex mu;
   static std::unordered_map<void*, uint32_t> epochs;
@@ -102,6 +111,7 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   a.partials = (unsigned long long*)a.desc;
   a.n_chunks = (uint32_t)chunks;
   a.epoch = len_only ? 0u : next_epoch(ws);
+  a.lookback_spins = lookback_spins();
   return dev_err(hq::launch_encode(plan->lattice, dither, dtype == HQ_BF16, len_only, a, st));
 }
 

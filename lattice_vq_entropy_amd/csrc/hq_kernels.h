@@ -26,6 +26,7 @@ struct EncArgs {
   unsigned long long* partials;  // length-only pass: bits per work-group
   uint32_t n_chunks;
   uint32_t epoch;  // tag of this call's look-back words, 1 .. 2^24-1
+  uint32_t lookback_spins;  // rounds before an unready predecessor is recomputed
 };
 
 struct DecArgs {

@@ -84,142 +84,236 @@ __device__ __forceinline__ uint32_t rev4(uint32_t n) {
 // ===========================================================================
 // Encode
 // ===========================================================================
+// Per-lane constants of a plan: butterfly signs, the scale with the lane
+// sign folded in, and the sign bits of D for the lane's 8 coordinates.
+template <bool BF16>
+struct LaneConst {
+  FwhtSigns fs;
+  float scale;
+  uint32_t smask[8];
+  __device__ __forceinline__ LaneConst(const uint32_t sgn[4], int v, float c) {
+    fs = fwht_signs(v);
+    scale = fs.lane_sign * c;
+    const uint32_t sbyte = (sgn[v >> 2] >> ((v & 3) * 8)) & 0xFFu;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        smask[i] = (((sbyte >> (2 * i)) & 1u) << 15) | (((sbyte >> (2 * i + 1)) & 1u) << 31);
+#pragma unroll
+      for (int i = 4; i < 8; ++i) smask[i] = 0;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) smask[i] = ((sbyte >> i) & 1u) << 31;
+    }
+  }
+};
+
+// One tile's symbols as seen by one lane, and the tile's Rice parameter and
+// record length.
+struct TileSyms {
+  uint32_t m[8];  // zigzag symbols of the lane's coordinates
+  uint32_t raw;   // E8 coset bit of the lane's vector
+  uint32_t k;     // Rice parameter of the tile
+  uint32_t L;     // record length of the tile (bits)
+  uint32_t ulen;  // unary bits of the lane's 8 symbols
+};
+
+// RHT -> (dither) -> nearest point -> strip -> zigzag -> Rice k for tile t,
+// held by the 16-lane row of the calling lane.  Every lane of the wave calls
+// it (it uses ballots); invalid tiles yield zero symbols.
+template <int L, bool DITHER, bool BF16>
+__device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF16>& lc, uint64_t t, bool valid,
+                                           int v, int r, int grp, TileSyms& ts) {
+  constexpr uint32_t RAW = Lat<L>::raw;
+  float xv[8];
+  if (valid) {
+    load_lane<BF16>(a.x, t, v, lc.smask, xv);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = 0.0f;
+  }
+  fwht_tile(xv, lc.fs);
+  float u[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = xv[i] * lc.scale;
+  if constexpr (DITHER) {
+    float d[8];
+    dither_lane<L>(a.key0, a.key1, a.tile_base + t, v, d);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = u[i] + d[i];
+  }
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bad |= !(__builtin_fabsf(u[i]) < kRangeLimit);
+  const uint64_t bad_mask = __ballot(bad);
+  if (bad_mask) {
+    const bool tile_bad = ((bad_mask >> (grp * 16)) & 0xFFFFull) != 0;
+    bool nf = false;
+    if (tile_bad && valid) nf = lane_nonfinite<BF16>(a.x, t, v);
+    const bool tile_nf = ((__ballot(nf) >> (grp * 16)) & 0xFFFFull) != 0;
+    if (tile_bad) {
+      if (r == 0 && valid) set_status(a.ws, tile_nf ? 2 : 3);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u[i] = 0.0f;
+    }
+  }
+  int32_t sym[8];
+  quantize_lane<L>(u, sym, ts.raw);
+  uint32_t lsum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ts.m[i] = valid ? zigzag(sym[i]) : 0u;
+    lsum += ts.m[i];
+  }
+  // Rice parameter: the smallest k with S(k) = sum ceil((m >> k)/2) <= 128
+  // minimises the tile length.  From M = sum m: S(k) <= 128 once
+  // M <= 2^(k+7) (at kA) and S(k) > 128 while M >= 3*2^(k+7), so the answer
+  // is one of kA-2, kA-1, kA; S(k) = A_k - A_(k+1) with A_j = sum m >> j.
+  const uint32_t M = row_sum_u32(lsum);
+  const int kA = M <= 128u ? 0 : (32 - __builtin_clz(M - 1u)) - 7;
+  const int c = kA >= 2 ? kA - 2 : 0;
+  uint32_t a0 = 0, a1 = 0, a2 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t tt = ts.m[i] >> c;
+    a0 += tt;
+    a1 += tt >> 1;
+    a2 += tt >> 2;
+  }
+  const uint32_t tot = row_sum_u32(a0 | (a1 << 10) | (a2 << 20));  // A_c <= 512
+  const uint32_t A0 = tot & 1023u, A1 = (tot >> 10) & 1023u, A2 = tot >> 20;
+  uint32_t Ak, ak;
+  if (A0 - A1 <= 128u) { ts.k = c; Ak = A0; ak = a0; }
+  else if (A1 - A2 <= 128u) { ts.k = c + 1; Ak = A1; ak = a1; }
+  else { ts.k = c + 2; Ak = A2; ak = a2; }
+  ts.ulen = ak + 8u;
+  ts.L = valid ? RAW + 128u * (1u + ts.k) + Ak : 0u;
+}
+
+// Assemble one tile's record at local bit tb of the LDS stream s (stream word
+// i at s[1 + i]).  Every lane of the wave calls it (ballot, shuffles); only
+// lanes of valid tiles write.
+template <int L>
+__device__ __forceinline__ void tile_pack(uint32_t* s, uint32_t tb, const TileSyms& ts, int v, int r, int lane,
+                                          int grp, bool valid) {
+  constexpr uint32_t RAW = Lat<L>::raw;
+  const uint32_t k = ts.k;
+  if constexpr (RAW > 0) {
+    const uint64_t bm = __ballot((ts.raw & 1u) != 0);
+    const uint32_t g16 = (uint32_t)(bm >> (grp * 16)) & 0xFFFFu;
+    // bit v of the field is the coset bit of vector v, held by lane v(r)
+    const uint32_t raw16 = (g16 & 0x0F0Fu) | (rev4((g16 >> 4) & 0xFu) << 4) | (rev4((g16 >> 12) & 0xFu) << 12);
+    if (valid && r == 0) lds_or64(s, tb, raw16, 0u);
+  }
+  // exclusive scan of the unary lengths in vector order
+  const uint32_t U = ts.ulen;
+  const int rowbase = lane & ~15;
+  const uint32_t Uv = (uint32_t)__shfl((int)U, rowbase | lane_vector(r));
+  const uint32_t incl = row_scan_u32(Uv);
+  const uint32_t exv = incl - Uv;
+  const uint32_t excl = (uint32_t)__shfl((int)exv, rowbase | lane_vector(r));
+  if (!valid) return;
+  const uint32_t rpos = tb + RAW + 8u * (uint32_t)v * k;
+  if (k != 0) {
+    const uint32_t mask = (1u << k) - 1u;
+    if (k <= 8) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lo |= (ts.m[j] & mask) << (j * k);
+#pragma unroll
+      for (int j = 4; j < 8; ++j) hi |= (ts.m[j] & mask) << ((j - 4) * k);
+      const uint64_t R = (uint64_t)lo | ((uint64_t)hi << (4 * k));
+      lds_or64(s, rpos, (uint32_t)R, (uint32_t)(R >> 32));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lds_or64(s, rpos + j * k, ts.m[j] & mask, 0u);
+    }
+  }
+  const uint32_t upos = tb + RAW + 128u * k + excl;
+  if (U <= 64u) {
+    uint64_t msk = 0;
+    uint32_t pos = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pos += ts.m[j] >> k;
+      msk |= 1ull << pos;
+      pos += 1;
+    }
+    lds_or64(s, upos, (uint32_t)msk, (uint32_t)(msk >> 32));
+  } else {
+    uint32_t pos = upos;
+    for (int j = 0; j < 8; ++j) {
+      pos += ts.m[j] >> k;
+      atomicOr(&s[1 + (pos >> 5)], 1u << (pos & 31));
+      pos += 1;
+    }
+  }
+}
+
+// Exclusive scan of the kChunkTiles lengths in ln[] into lo[0..kChunkTiles]
+// (lo[kChunkTiles] = chunk total); wave 0 only.
+__device__ __forceinline__ void chunk_scan(const uint32_t* ln, uint32_t* lo, int tid, int lane) {
+  uint32_t l = tid < kChunkTiles ? ln[tid] : 0u;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(l, o);
+    if (lane >= o) l += y;
+  }
+  if (tid < kChunkTiles) lo[tid + 1] = l;
+  if (tid == 0) lo[0] = 0;
+}
+
+// Look-back control words (LDS) written by wave 0 for the whole work-group.
+enum : uint32_t { kLbDone = 0, kLbAdvance = 1, kLbRetry = 2, kLbFallback = 3 };
+
+// One chunk per work-group, chunk = blockIdx.x.  The single pass computes the
+// chunk's symbols and lengths, publishes its bit total (aggregate), packs its
+// bits in LDS, publishes its last 32 bits (tail), looks back over the
+// predecessors' descriptors for its exclusive bit offset, then stores.
+//
+// Forward progress needs no assumption about dispatch order or residency:
+// when a predecessor's descriptor stays unready for a.lookback_spins rounds
+// (one round: device-coherent loads of 256 descriptors and a short sleep),
+// the work-group recomputes that chunk's aggregate itself (and its tail if it
+// is the immediate predecessor), as in the "decoupled fallback" single-pass
+// scan.  All inter-work-group words carry the call's epoch, so relaxed
+// device-scope atomics suffice and no same-address atomic is used.
 template <int L, bool DITHER, bool BF16, bool LEN_ONLY>
 __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
-  constexpr uint32_t RAW = Lat<L>::raw;
   __shared__ uint32_t s_stage[kStageWords + 1];
-  __shared__ uint32_t s_len[kChunkTiles];
-  __shared__ uint32_t s_lo[kChunkTiles + 1];
-  __shared__ uint32_t s_k[kChunkTiles];
-  __shared__ uint32_t s_misc[8];
+  __shared__ uint32_t s_tbuf[kMaxRecordWords + 4];  // fallback: one tile's record
+  __shared__ uint32_t s_len[kChunkTiles], s_lo[kChunkTiles + 1], s_k[kChunkTiles];
+  __shared__ uint32_t s_len2[kChunkTiles], s_lo2[kChunkTiles + 1];
+  __shared__ uint32_t s_ctl[4];
+  __shared__ uint64_t s_ctl64[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
   const int v = lane_vector(r);
-  const FwhtSigns fs = fwht_signs(v);
-  const float scale = fs.lane_sign * a.c_enc;
-  const uint32_t sbyte = (a.sgn[v >> 2] >> ((v & 3) * 8)) & 0xFFu;
-  uint32_t smask[8];
-  if constexpr (BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      smask[i] = (((sbyte >> (2 * i)) & 1u) << 15) | (((sbyte >> (2 * i + 1)) & 1u) << 31);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) smask[i] = ((sbyte >> i) & 1u) << 31;
-  }
-
-  // Persistent grid: every work-group is resident (cooperative launch) and
-  // walks chunks blockIdx.x, blockIdx.x + gridDim.x, ... in order, so a
-  // chunk's look-back only ever waits on lower chunks that are being or have
-  // been processed.  The epoch tags this call's look-back words.
+  const LaneConst<BF16> lc(a.sgn, v, a.c_enc);
+  const uint32_t chunk = blockIdx.x;
   const uint32_t epoch = a.epoch;
-  uint64_t len_acc = 0;
-  for (uint32_t chunk = blockIdx.x; chunk < a.n_chunks; chunk += gridDim.x) {
   const uint64_t t_first = (uint64_t)chunk * kChunkTiles;
 
-  uint32_t m[kPasses][8];
-  uint32_t rawv[kPasses];
-  uint32_t kk[kPasses];
-  uint32_t ulen[kPasses];
-
+  TileSyms ts[kPasses];
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int slot = p * 16 + wv * 4 + grp;
     const uint64_t t = t_first + slot;
     const bool valid = t < a.n_tiles;
-    float xv[8];
-    if (valid) {
-      load_lane<BF16>(a.x, t, v, smask, xv);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xv[i] = 0.0f;
-    }
-    fwht_tile(xv, fs);
-    float u[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = xv[i] * scale;
-    if constexpr (DITHER) {
-      float d[8];
-      dither_lane<L>(a.key0, a.key1, a.tile_base + t, v, d);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) u[i] = u[i] + d[i];
-    }
-    bool bad = false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) bad |= !(__builtin_fabsf(u[i]) < kRangeLimit);
-    const uint64_t bad_mask = __ballot(bad);
-    if (bad_mask) {
-      const bool tile_bad = ((bad_mask >> (grp * 16)) & 0xFFFFull) != 0;
-      bool nf = false;
-      if (tile_bad && valid) nf = lane_nonfinite<BF16>(a.x, t, v);
-      const bool tile_nf = ((__ballot(nf) >> (grp * 16)) & 0xFFFFull) != 0;
-      if (tile_bad) {
-        if (r == 0 && valid) set_status(a.ws, tile_nf ? 2 : 3);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) u[i] = 0.0f;
-      }
-    }
-    int32_t sym[8];
-    uint32_t raw;
-    quantize_lane<L>(u, sym, raw);
-    uint32_t lsum = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      m[p][i] = valid ? zigzag(sym[i]) : 0u;
-      lsum += m[p][i];
-    }
-    rawv[p] = raw;
-    // Rice parameter: the smallest k with S(k) = sum ceil((m >> k)/2) <= 128
-    // minimises the tile length.  From M = sum m: S(k) <= 128 once
-    // M <= 2^(k+7) (at kA) and S(k) > 128 while M >= 3*2^(k+7), so the
-    // answer is one of kA-2, kA-1, kA; S(k) = A_k - A_(k+1) with A_j = sum m >> j.
-    const uint32_t M = row_sum_u32(lsum);
-    const int kA = M <= 128u ? 0 : (32 - __builtin_clz(M - 1u)) - 7;
-    const int c = kA >= 2 ? kA - 2 : 0;
-    uint32_t a0 = 0, a1 = 0, a2 = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t tt = m[p][i] >> c;
-      a0 += tt;
-      a1 += tt >> 1;
-      a2 += tt >> 2;
-    }
-    const uint32_t tot = row_sum_u32(a0 | (a1 << 10) | (a2 << 20));  // A_c <= 512
-    const uint32_t A0 = tot & 1023u, A1 = (tot >> 10) & 1023u, A2 = tot >> 20;
-    uint32_t k, Ak, ak;
-    if (A0 - A1 <= 128u) { k = c; Ak = A0; ak = a0; }
-    else if (A1 - A2 <= 128u) { k = c + 1; Ak = A1; ak = a1; }
-    else { k = c + 2; Ak = A2; ak = a2; }
-    kk[p] = k;
-    ulen[p] = ak + 8u;
+    tile_front<L, DITHER, BF16>(a, lc, t, valid, v, r, grp, ts[p]);
     if (r == 0) {
-      s_len[slot] = valid ? RAW + 128u * (1u + k) + Ak : 0u;
-      s_k[slot] = k;
+      s_len[slot] = ts[p].L;
+      s_k[slot] = ts[p].k;
     }
   }
   __syncthreads();
-
-  // work-group exclusive scan of the tile lengths
-  if (tid < 64) {
-    uint32_t l = tid < kChunkTiles ? s_len[tid] : 0u;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(l, o);
-      if (lane >= o) l += y;
-    }
-    if (tid < kChunkTiles) s_lo[tid + 1] = l;
-    if (tid == 0) s_lo[0] = 0;
-  }
+  if (wv == 0) chunk_scan(s_len, s_lo, tid, lane);
   __syncthreads();
   const uint32_t A = s_lo[kChunkTiles];
 
   if constexpr (LEN_ONLY) {
-    len_acc += A;
+    if (tid == 0) a.partials[chunk] = A;
   } else {
-    // Publish this chunk's aggregate as soon as it is known, so successors'
-    // look-backs progress while the chunk packs its bits.  Every word
-    // exchanged between work-groups carries the call's epoch, so relaxed
-    // device-scope atomics suffice (no cache-wide release/acquire).
     const uint64_t ep = (uint64_t)epoch << kDescEpochShift;
     if (tid == 0)
       __hip_atomic_store(&a.desc[chunk], (chunk == 0 ? kDescFlagIncl : kDescFlagAgg) | ep | (uint64_t)A,
@@ -227,138 +321,137 @@ __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
     const uint32_t nz = ((A + 31u) >> 5) + 2u;
     for (uint32_t i = tid; i < nz; i += 256) s_stage[1 + i] = 0u;
     __syncthreads();
-
-    // bit assembly in LDS
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int slot = p * 16 + wv * 4 + grp;
-      const bool valid = t_first + slot < a.n_tiles;
-      const uint32_t tb = s_lo[slot];
-      const uint32_t k = kk[p];
-      if constexpr (RAW > 0) {
-        const uint64_t bm = __ballot((rawv[p] & 1u) != 0);
-        const uint32_t g16 = (uint32_t)(bm >> (grp * 16)) & 0xFFFFu;
-        const uint32_t raw16 = (g16 & 0x0F0Fu) | (rev4((g16 >> 4) & 0xFu) << 4) | (rev4((g16 >> 12) & 0xFu) << 12);
-        if (valid && r == 0 && raw16) atomicOr(&s_stage[1 + (tb >> 5)], raw16 << (tb & 31));
-        if (valid && r == 0 && (tb & 31) > 16 && (raw16 >> (32 - (tb & 31))))
-          atomicOr(&s_stage[2 + (tb >> 5)], raw16 >> (32 - (tb & 31)));
-      }
-      // exclusive scan of the unary lengths in vector order
-      const uint32_t U = ulen[p];
-      const int rowbase = lane & ~15;
-      const uint32_t Uv = (uint32_t)__shfl((int)U, rowbase | lane_vector(r));
-      const uint32_t incl = row_scan_u32(Uv);
-      const uint32_t exv = incl - Uv;
-      const uint32_t excl = (uint32_t)__shfl((int)exv, rowbase | lane_vector(r));
-      if (valid) {
-        const uint32_t rpos = tb + RAW + 8u * (uint32_t)v * k;
-        if (k != 0) {
-          const uint32_t mask = (1u << k) - 1u;
-          if (k <= 8) {
-            uint32_t lo = 0, hi = 0;
+      tile_pack<L>(s_stage, s_lo[slot], ts[p], v, r, lane, grp, t_first + slot < a.n_tiles);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t b = A - 32u;  // A >= 128: every chunk holds a tile
+      const uint32_t w = 1 + (b >> 5), sh = b & 31;
+      const uint32_t tailv = sh ? __builtin_amdgcn_alignbit(s_stage[w + 1], s_stage[w], sh) : s_stage[w];
+      __hip_atomic_store(&a.tail[chunk], ((uint64_t)epoch << 32) | tailv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ctl[1] = 0;  // predecessor tail not yet known
+    }
+
+    // ---- look-back (work-group-wide loop; wave 0 reads 256 descriptors) ----
+    uint64_t excl = 0;
+    int64_t j = (int64_t)chunk - 1;
+    int spins = 0;
+    while (j >= 0) {
+      if (wv == 0) {
+        uint64_t val[4];
+        bool rdy[4], isP[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) lo |= (m[p][j] & mask) << (j * k);
+        for (int q = 0; q < 4; ++q) {
+          const int64_t idx = j - 4 * lane - q;
+          const uint64_t d = idx >= 0 ? __hip_atomic_load(&a.desc[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+          const uint32_t dep = (uint32_t)(d >> kDescEpochShift) & 0xFFFFFFu;
+          const uint64_t flag = d >> 62;
+          rdy[q] = idx < 0 || (flag != 0 && dep == epoch);
+          isP[q] = idx < 0 || (rdy[q] && flag == 2);
+          val[q] = idx >= 0 ? (d & kDescValueMask) : 0ull;
+        }
+        // first stop (inclusive or unready descriptor), newest first
+        int qs = 4;
 #pragma unroll
-            for (int j = 4; j < 8; ++j) hi |= (m[p][j] & mask) << ((j - 4) * k);
-            const uint64_t R = (uint64_t)lo | ((uint64_t)hi << (4 * k));
-            lds_or64(s_stage, rpos, (uint32_t)R, (uint32_t)(R >> 32));
+        for (int q = 3; q >= 0; --q) qs = (isP[q] || !rdy[q]) ? q : qs;
+        uint64_t before = 0, all4 = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q < qs) before += val[q];
+          all4 += val[q];
+        }
+        const uint64_t bs = __ballot(qs < 4);
+        const int fl = bs ? __builtin_ctzll(bs) : 64;
+        uint64_t contrib = lane < fl ? all4 : (lane == fl ? before : 0ull);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) contrib += __shfl_xor(contrib, o);
+        if (lane == (fl < 64 ? fl : 0)) {
+          uint32_t ctl;
+          uint64_t add = contrib;
+          if (fl == 64) {
+            ctl = kLbAdvance;
+          } else if (isP[qs < 4 ? qs : 0] && qs < 4) {
+            ctl = kLbDone;
+            add += val[qs];
           } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) lds_or64(s_stage, rpos + j * k, m[p][j] & mask, 0u);
+            ctl = spins < (int)a.lookback_spins ? kLbRetry : kLbFallback;
+            s_ctl64[1] = (uint64_t)(j - 4 * fl - qs);  // the unready chunk
           }
-        }
-        const uint32_t upos = tb + RAW + 128u * k + excl;
-        if (U <= 64u) {
-          uint64_t msk = 0;
-          uint32_t pos = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            pos += m[p][j] >> k;
-            msk |= 1ull << pos;
-            pos += 1;
-          }
-          lds_or64(s_stage, upos, (uint32_t)msk, (uint32_t)(msk >> 32));
-        } else {
-          uint32_t pos = upos;
-          for (int j = 0; j < 8; ++j) {
-            pos += m[p][j] >> k;
-            atomicOr(&s_stage[1 + (pos >> 5)], 1u << (pos & 31));
-            pos += 1;
-          }
+          s_ctl[0] = ctl;
+          s_ctl64[0] = add;
         }
       }
-    }
-    __syncthreads();
-
-    // publish the last 32 bits of the local stream, then look back for the
-    // exclusive prefix (wave 0; 4 descriptors per lane, 256 per round)
-    if (wv == 0) {
-      uint64_t excl = 0;
-      if (lane == 0) {
-        const uint32_t b = A - 32u;  // A >= 128: every chunk holds a tile
+      __syncthreads();
+      const uint32_t ctl = s_ctl[0];
+      const uint64_t add = s_ctl64[0];
+      const int64_t jf = (int64_t)s_ctl64[1];
+      __syncthreads();
+      if (ctl == kLbDone) {
+        excl += add;
+        break;
+      }
+      if (ctl == kLbAdvance) {
+        excl += add;
+        j -= 256;
+        continue;
+      }
+      if (ctl == kLbRetry) {
+        ++spins;
+        __builtin_amdgcn_s_sleep(2);
+        continue;
+      }
+      // Fallback: compute chunk jf's aggregate here (and, for the immediate
+      // predecessor, its last 32 bits), then continue below it.
+      const uint64_t tf = (uint64_t)jf * kChunkTiles;  // a full chunk: jf < chunk
+      for (uint32_t i = tid; i < kMaxRecordWords + 4; i += 256) s_tbuf[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const int slot = p * 16 + wv * 4 + grp;
+        TileSyms fsy;
+        tile_front<L, DITHER, BF16>(a, lc, tf + slot, true, v, r, grp, fsy);
+        if (r == 0) s_len2[slot] = fsy.L;
+        if (jf == (int64_t)chunk - 1 && p == kPasses - 1 && wv == 3) {
+          tile_pack<L>(s_tbuf, 0u, fsy, v, r, lane, grp, grp == 3);  // slot kChunkTiles-1
+          if (grp == 3 && r == 0) s_ctl[2] = fsy.L;
+        }
+      }
+      __syncthreads();
+      if (wv == 0) chunk_scan(s_len2, s_lo2, tid, lane);
+      __syncthreads();
+      excl += add + s_lo2[kChunkTiles];
+      if (jf == (int64_t)chunk - 1 && tid == 0) {
+        const uint32_t Lt = s_ctl[2], b = Lt - 32u;
         const uint32_t w = 1 + (b >> 5), sh = b & 31;
-        const uint32_t tailv = sh ? __builtin_amdgcn_alignbit(s_stage[w + 1], s_stage[w], sh) : s_stage[w];
-        __hip_atomic_store(&a.tail[chunk], ((uint64_t)epoch << 32) | tailv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_stage[0] = sh ? __builtin_amdgcn_alignbit(s_tbuf[w + 1], s_tbuf[w], sh) : s_tbuf[w];
+        s_ctl[1] = 1;
       }
-      if (chunk > 0) {
-        int64_t j = (int64_t)chunk - 1;  // newest descriptor of the window
-        while (true) {
-          uint64_t val[4];
-          bool rdy[4], isP[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t idx = j - 4 * lane - q;
-            const uint64_t d = idx >= 0 ? __hip_atomic_load(&a.desc[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-            const uint32_t dep = (uint32_t)(d >> kDescEpochShift) & 0xFFFFFFu;
-            const uint64_t flag = d >> 62;
-            rdy[q] = idx < 0 || (flag != 0 && dep == epoch);
-            isP[q] = idx < 0 || (rdy[q] && flag == 2);
-            val[q] = idx >= 0 ? (d & kDescValueMask) : 0ull;
-          }
-          int qp = 4;  // first inclusive descriptor of this lane (newest first)
-#pragma unroll
-          for (int q = 3; q >= 0; --q) qp = isP[q] ? q : qp;
-          bool lane_rdy = true;
-          uint64_t upto = 0, all4 = 0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (q <= qp) { lane_rdy &= rdy[q]; upto += val[q]; }
-            all4 += val[q];
-          }
-          const uint64_t bp = __ballot(qp < 4), br = __ballot(lane_rdy);
-          const int fl = bp ? __builtin_ctzll(bp) : 64;
-          const uint64_t need = fl >= 63 ? ~0ull : ((2ull << fl) - 1ull);
-          if ((br & need) != need) {
-            __builtin_amdgcn_s_sleep(1);
-            continue;
-          }
-          uint64_t contrib = lane < fl ? all4 : (lane == fl ? upto : 0ull);
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) contrib += __shfl_xor(contrib, o);
-          excl += contrib;
-          if (fl < 64) break;
-          j -= 256;
-        }
-        if (lane == 0)
-          __hip_atomic_store(&a.desc[chunk], kDescFlagIncl | ep | (excl + A), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (lane == 0) {
-        s_misc[2] = (uint32_t)excl;
-        s_misc[3] = (uint32_t)(excl >> 32);
-        uint32_t pt = 0;
-        if (chunk > 0) {  // the predecessor's last 32 bits, tagged with the epoch
-          uint64_t tw;
-          while (((tw = __hip_atomic_load(&a.tail[chunk - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 32) !=
-                 (uint64_t)epoch)
-            __builtin_amdgcn_s_sleep(1);
-          pt = (uint32_t)tw;
-        }
-        s_stage[0] = pt;
+      j = jf - 1;
+      spins = 0;
+      __syncthreads();
+    }
+    if (tid == 0) {
+      if (chunk > 0)
+        __hip_atomic_store(&a.desc[chunk], kDescFlagIncl | ep | (excl + A), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ctl64[0] = excl;
+      if (chunk == 0) {
+        s_stage[0] = 0;
+      } else if (s_ctl[1] == 0) {
+        // the predecessor is running (it published its descriptor itself) and
+        // publishes its tail before its own look-back
+        uint64_t tw;
+        while (((tw = __hip_atomic_load(&a.tail[chunk - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 32) !=
+               (uint64_t)epoch)
+          __builtin_amdgcn_s_sleep(1);
+        s_stage[0] = (uint32_t)tw;
       }
     }
     __syncthreads();
 
-    const uint64_t E = (uint64_t)s_misc[2] | ((uint64_t)s_misc[3] << 32);
+    const uint64_t E = s_ctl64[0];
     if (tid < kChunkTiles) {
       const uint64_t t = t_first + tid;
       if (t < a.n_tiles) {
@@ -377,12 +470,6 @@ __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
       const uint32_t i = (uint32_t)(w - first);
       a.words[w] = sh ? __builtin_amdgcn_alignbit(s_stage[1 + i], s_stage[i], 32 - sh) : s_stage[1 + i];
     }
-
-  }
-  __syncthreads();  // the chunk's LDS is reused by the next chunk
-  }
-  if constexpr (LEN_ONLY) {
-    if (tid == 0) a.partials[blockIdx.x] = len_acc;
   }
 }
 
@@ -646,33 +733,17 @@ __global__ __launch_bounds__(256) void reduce_k(const T* p, uint32_t n, T* out) 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// Work-groups of a kernel that fit on the device at once.
-template <typename K>
-static uint32_t coresident_blocks(K kernel) {
-  int dev = 0, cus = 0, nb = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 256, 0) != hipSuccess) return 0;
-  return (uint32_t)(nb * cus);
-}
-
 template <int L, bool DITHER, bool BF16>
 static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
+  const dim3 grid(a.n_chunks);
   if (len_only) {
-    auto k = encode_k<L, DITHER, BF16, true>;
-    static uint32_t cap = coresident_blocks(k);
-    const uint32_t grid = a.n_chunks < cap ? a.n_chunks : (cap ? cap : 1u);
-    hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((encode_k<L, DITHER, BF16, true>), grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL(reduce_k<unsigned long long>, dim3(1), dim3(256), 0, st,
-                       (const unsigned long long*)a.partials, grid, &a.ws->bits);
-    return hipGetLastError();
+                       (const unsigned long long*)a.partials, a.n_chunks, &a.ws->bits);
+  } else {
+    hipLaunchKernelGGL((encode_k<L, DITHER, BF16, false>), grid, dim3(256), 0, st, a);
   }
-  auto k = encode_k<L, DITHER, BF16, false>;
-  static uint32_t cap = coresident_blocks(k);
-  if (cap == 0) return hipErrorInvalidConfiguration;
-  const uint32_t grid = a.n_chunks < cap ? a.n_chunks : cap;
-  void* args[] = {&a};
-  return hipLaunchCooperativeKernel((const void*)k, dim3(grid), dim3(256), args, 0, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_encode(int lat, bool dither, bool bf16, bool len_only, const EncArgs& a, hipStream_t st) {
