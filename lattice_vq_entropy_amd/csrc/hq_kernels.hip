@@ -492,41 +492,49 @@ __device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t j) {
   return pos;
 }
 
-// Parse the lane's 8 symbols of one tile record held in LDS and return the
-// dequantised real-space lattice coordinates.  Returns false when the record
-// is corrupt (the verdict is uniform over the 16 lanes of the tile).
+// Lattice coordinates of the lane's 8 symbols (inverse zigzag and unstrip),
+// as fp32 real-space points.  With s = sext(bit 0 of m), 2*unzigzag(m) is
+// m ^ s, so a halved coordinate plus the raw bit is one v_xad_u32.
 template <int L>
-__device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uint32_t Lb, uint32_t k, int v, int r,
-                                           int lane, uint32_t* ust, float p[8]) {
-  constexpr uint32_t RAW = Lat<L>::raw;
-  uint32_t raw = 0;
-  if constexpr (RAW > 0) {
-    const uint32_t P = base + (uint32_t)v;
-    raw = (s[P >> 5] >> (P & 31)) & 1u;
-  }
-  uint32_t rem[8];
-  const uint32_t rpos = base + RAW + 8u * (uint32_t)v * k;
-  const uint32_t mask = k ? ((1u << k) - 1u) : 0u;
-  if (k == 0) {
+__device__ __forceinline__ void dequant_lane(const uint32_t m[8], uint32_t raw, float p[8]) {
+  uint32_t t[8];  // 2 * unzigzag(m)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) rem[j] = 0;
-  } else if (k <= 8) {
-    const uint32_t w = rpos >> 5, sh = rpos & 31;
-    const uint32_t w0 = s[w], w1 = s[w + 1], w2 = s[w + 2];
-    const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);
-    const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, sh);
-    const uint64_t R = (uint64_t)lo | ((uint64_t)hi << 32);
+  for (int j = 0; j < 8; ++j) t[j] = m[j] ^ (uint32_t)__builtin_amdgcn_sbfe((int)m[j], 0, 1);
+  if constexpr (L == 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) rem[j] = (uint32_t)(R >> (j * k)) & mask;
-  } else {
+    for (int j = 0; j < 8; ++j) p[j] = (float)((int32_t)t[j] >> 1);
+  } else if constexpr (L == 1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t P = rpos + j * k;
-      rem[j] = __builtin_amdgcn_alignbit(s[(P >> 5) + 1], s[P >> 5], P & 31) & mask;
+    for (int j = 0; j < 8; j += 2) {
+      const int32_t jj = (int32_t)t[j + 1] >> 1;              // j
+      const int32_t ii = (int32_t)(t[j] + ((uint32_t)jj & 1u));  // i = 2 i' + (j & 1)
+      p[j] = (float)ii;
+      p[j + 1] = (float)jj * kSqrt3;
     }
+  } else if constexpr (L == 2) {
+#pragma unroll
+    for (int h = 0; h < 8; h += 4) {
+      const uint32_t par = ((t[h] ^ t[h + 1] ^ t[h + 2]) >> 1) & 1u;  // parity of x0 + x1 + x2
+#pragma unroll
+      for (int j = 0; j < 3; ++j) p[h + j] = (float)((int32_t)t[h + j] >> 1);
+      p[h + 3] = (float)(int32_t)(t[h + 3] + par);
+    }
+  } else {
+    // x_i = 2 y_i + b; y_7 = 2 z_7 + parity(y_0 + ... + y_6), bit 1 of x_i = bit 0 of y_i
+    uint32_t x[8];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) x[j] = t[j] + raw;
+    const uint32_t par = ((x[0] ^ x[1] ^ x[2] ^ x[3] ^ x[4] ^ x[5] ^ x[6]) >> 1) & 1u;
+    x[7] = ((t[7] + par) << 1) + raw;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = (float)(int32_t)x[j];
   }
-  // unary section: count ones per word, scan, select the segment starts
-  const uint32_t ustart = base + RAW + 128u * k, uend = base + Lb;
+}
+
+// General segment starts (any unary length): count ones per word 16 words
+// at a time, scan, select rank 8v-1 for every vector v.  Writes ust[1..15].
+__device__ __forceinline__ uint32_t unary_starts_general(const uint32_t* s, uint32_t ustart, uint32_t uend, int r,
+                                                         uint32_t* ust) {
   const uint32_t wA = ustart >> 5, wB = (uend - 1u) >> 5, nW = wB - wA + 1u;
   uint32_t rank_base = 0;
   for (uint32_t it = 0; it < nW; it += 16) {
@@ -544,37 +552,127 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uin
     }
     rank_base += row_sum_u32(cnt);
   }
-  const uint32_t lastbit = (s[(uend - 1u) >> 5] >> ((uend - 1u) & 31)) & 1u;
-  if (rank_base != 128u || !lastbit) return false;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  uint32_t pos = v == 0 ? ustart : ust[v];
-  bool ok = true;
-  uint32_t m[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t st = pos;
-    const uint32_t wlim = (uend >> 5) + 1u;  // the staging buffer holds words up to here
-    uint32_t w = s[min(pos >> 5, wlim)] >> (pos & 31);
-    while (w == 0u && pos < uend) {
-      pos = (pos | 31u) + 1u;
-      w = s[min(pos >> 5, wlim)];
-    }
-    pos += (uint32_t)__builtin_ctz(w | 0x80000000u);  // w != 0 within a valid record
-    const uint32_t q = pos - st;
-    ok &= pos < uend && q < (kMLimit >> k);
-    m[j] = (q << k) | rem[j];
-    pos += 1;
+  return rank_base;
+}
+
+// Parse the lane's 8 symbols of one tile record held in LDS (record at local
+// bit base, length Lb, Rice parameter k) and return the dequantised
+// real-space lattice coordinates.  Returns false when the record is corrupt
+// (the verdict is uniform over the 16 lanes of the tile).  ust: 16 words of
+// LDS per tile; tb: 16 bytes of LDS per tile.
+template <int L>
+__device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uint32_t Lb, uint32_t k, int v, int r,
+                                           int lane, uint32_t* ust, uint8_t* tb, float p[8]) {
+  constexpr uint32_t RAW = Lat<L>::raw;
+  uint32_t raw = 0;
+  if constexpr (RAW > 0) {
+    const uint32_t f = __builtin_amdgcn_alignbit(s[(base >> 5) + 1], s[base >> 5], base & 31);
+    raw = (f >> v) & 1u;
   }
-  const bool bad = ((__ballot(!ok) >> (lane & ~15)) & 0xFFFFull) != 0;
-  if (bad) return false;
-  int32_t sym[8];
+  // remainders: 8 fields of k bits at fixed positions
+  uint32_t rem[8];
+  const uint32_t rpos = base + RAW + 8u * (uint32_t)v * k;
+  if (k <= 7) {
+    const uint32_t w = rpos >> 5, sh = rpos & 31;
+    const uint32_t w0 = s[w], w1 = s[w + 1], w2 = s[w + 2];
+    const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);
+    const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, sh);
+    const uint32_t h4 = __builtin_amdgcn_alignbit(hi, lo, 4 * k);  // fields 4..7 (4k < 32)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) sym[j] = unzigzag(m[j]);
-  constexpr int D = Lat<L>::dim;
+    for (int j = 0; j < 4; ++j) rem[j] = __builtin_amdgcn_ubfe(lo, j * k, k);
 #pragma unroll
-  for (int q = 0; q < 8; q += D) unstrip_embed<L>(&sym[q], raw, &p[q]);
+    for (int j = 0; j < 4; ++j) rem[4 + j] = __builtin_amdgcn_ubfe(h4, j * k, k);
+  } else {
+    const uint32_t mask = (1u << k) - 1u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t P = rpos + j * k;
+      rem[j] = __builtin_amdgcn_alignbit(s[(P >> 5) + 1], s[P >> 5], P & 31) & mask;
+    }
+  }
+  // unary section [ustart, uend): 128 ones; lane v's 8 codes start after the
+  // (8v)-th one
+  const uint32_t ustart = base + RAW + 128u * k, uend = base + Lb;
+  const uint32_t wA = ustart >> 5, nW = ((uend - 1u) >> 5) - wA + 1u;
+  uint32_t start;
+  bool ok = true;
+  if (nW <= 16) {
+    // one word per lane: inclusive one-counts I_r, kept as bytes in LDS
+    uint32_t word = (uint32_t)r < nW ? s[wA + r] : 0u;
+    if (r == 0) word &= ~0u << (ustart & 31);
+    if ((uint32_t)r == nW - 1 && (uend & 31)) word &= (1u << (uend & 31)) - 1u;
+    const uint32_t I = row_scan_u32(__builtin_popcount(word));
+    if (r == 15) ok = I == 128u;
+    tb[r] = (uint8_t)(I < 127u ? I : 127u);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint4 T = *reinterpret_cast<const uint4*>(tb);
+    start = ustart;
+    if (v > 0) {
+      // word holding rank R = 8v-1: the number of words with I_w <= R, by a
+      // packed-byte compare (byte 0x80 + R - I_w keeps bit 7 iff I_w <= R;
+      // 7 <= R <= 119 and I_w <= 127, so no byte borrows)
+      const uint32_t R = 8u * (uint32_t)v - 1u;
+      const uint32_t key = (R * 0x01010101u) | 0x80808080u;
+      const uint32_t wsel = __builtin_popcount((key - T.x) & 0x80808080u) + __builtin_popcount((key - T.y) & 0x80808080u) +
+                            __builtin_popcount((key - T.z) & 0x80808080u) + __builtin_popcount((key - T.w) & 0x80808080u);
+      const uint32_t q4 = wsel == 0 ? 0u : wsel - 1u;  // byte index of I_(w-1)
+      const uint32_t Td = q4 < 4 ? T.x : q4 < 8 ? T.y : q4 < 12 ? T.z : T.w;
+      const uint32_t Iprev = wsel == 0 ? 0u : __builtin_amdgcn_ubfe(Td, 8 * (q4 & 3), 8);
+      uint32_t wd = s[wA + min(wsel, 15u)];
+      if (wsel == 0) wd &= ~0u << (ustart & 31);
+      start = (wA + wsel) * 32u + select_bit(wd, R - Iprev) + 1u;
+    }
+  } else {
+    ok = unary_starts_general(s, ustart, uend, r, ust) == 128u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    start = v == 0 ? ustart : ust[v];
+  }
+  const uint32_t lastbit = (s[(uend - 1u) >> 5] >> ((uend - 1u) & 31)) & 1u;
+  ok &= lastbit != 0;
+  if (((__ballot(!ok) >> (lane & ~15)) & 0xFFFFull) != 0) return false;
+  // the lane's 8 unary codes: q zeros then a one, from start
+  uint32_t m[8];
+  const uint32_t qlim = kMLimit >> k;
+  {
+    const uint32_t w = min(start >> 5, (uint32_t)kStageWords - 2u), sh = start & 31;
+    uint32_t win = __builtin_amdgcn_alignbit(s[w + 1], s[w], sh);
+    if (__builtin_popcount(win) >= 8) {
+      uint32_t prev = 0, qmax = 0;  // prev: bit after the previous one
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t pos = (uint32_t)__builtin_ctz(win);
+        const uint32_t q = pos - prev;  // < 32
+        qmax = max(qmax, q);
+        m[j] = (q << k) | rem[j];
+        prev = pos + 1;
+        win &= win - 1u;
+      }
+      ok &= qmax < qlim;
+    } else {
+      uint32_t pos = start;
+      const uint32_t wlim = (uend >> 5) + 1u;  // the staging buffer holds words up to here
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t st = pos;
+        uint32_t ww = s[min(pos >> 5, wlim)] >> (pos & 31);
+        while (ww == 0u && pos < uend) {
+          pos = (pos | 31u) + 1u;
+          ww = s[min(pos >> 5, wlim)];
+        }
+        pos += (uint32_t)__builtin_ctz(ww | 0x80000000u);
+        const uint32_t q = pos - st;
+        ok &= pos < uend && q < qlim;
+        m[j] = (q << k) | rem[j];
+        pos += 1;
+      }
+    }
+  }
+  if (((__ballot(!ok) >> (lane & ~15)) & 0xFFFFull) != 0) return false;
+  dequant_lane<L>(m, raw, p);
   return true;
 }
 
@@ -586,6 +684,7 @@ __global__ __launch_bounds__(256) void decode_k(DecArgs a) {
   __shared__ uint64_t s_off[kChunkTiles + 1];
   __shared__ uint32_t s_k[kChunkTiles];
   __shared__ uint32_t s_ust[16][16];
+  __shared__ uint4 s_tb[16];  // per tile of a pass: 16 one-count bytes
   __shared__ float s_q[OUT == kOutScores ? 16 : 1][kTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
@@ -649,7 +748,8 @@ __global__ __launch_bounds__(256) void decode_k(DecArgs a) {
       const uint64_t Lr = o1 - o0;
       const bool ok = span_ok && o1 >= o0 && k <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + k) && Lr <= MAXREC;
       bool good = false;
-      if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, s_ust[pslot], pv);
+      if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, s_ust[pslot],
+                                       reinterpret_cast<uint8_t*>(&s_tb[pslot]), pv);
       if (!good) {
         if (r == 0) set_status(a.ws, 5);
 #pragma unroll
