@@ -35,7 +35,9 @@ def parse():
     ap.add_argument("--bps", type=float, default=4.0)
     ap.add_argument("--sets", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=15)
+    ap.add_argument("--no-rows", action="store_true", help="only the headline workload")
+    ap.add_argument("--row-iters", type=int, default=10)
     return ap.parse_args()
 
 
@@ -56,6 +58,98 @@ def cpu_baseline(x_host_bits, alpha, seed, reps):
             "kind": "oracle",
             "sample": f"whole 4096x4096 bf16 tensor, encode+decode, {reps} repetitions, "
                       f"{t_total:.1f} s single-threaded"}
+
+
+def _time(torch, fn, iters):
+    """Median launch time (ms) of fn() over iters runs, HIP events on the stream."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def _row(name, op, ms, n_el, in_bytes_per_el, stream_bits, n_tiles, extra=None, other_bytes=0.0):
+    alg = n_el * in_bytes_per_el + stream_bits / 8.0 + 9.0 * n_tiles + other_bytes
+    r = {"workload": name, "op": op, "ms": round(ms, 5),
+         "GBps_in": round(n_el * in_bytes_per_el / (ms * 1e-3) / 1e9, 1),
+         "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if extra:
+        r.update(extra)
+    return r
+
+
+def workload_rows(hq, W, torch, np, iters):
+    """encode/decode (and fused-score) timings of the other workload shapes."""
+    dev = torch.device("cuda:0")
+    rows = []
+    seed = W.PLAN_SEED
+
+    def codec(name, x, lat, bps, dithered=False, tile_base=0, alpha=None, out_dtype=torch.bfloat16):
+        n_el = x.numel()
+        n_tiles = n_el // 128
+        plan = hq.Plan(lat, bps, seed)
+        ws = plan.workspace(n_tiles)
+        if alpha is None:
+            plan.calibrate(x, ws, dithered=dithered, tile_base=tile_base)
+        else:
+            plan.set_alpha(alpha)
+        out = hq.alloc_stream(plan, n_tiles, dev)
+        y = torch.empty(n_el, dtype=out_dtype, device=dev)
+        enc = hq.encode(plan, x, ws, out=out, dithered=dithered, tile_base=tile_base)
+        te = _time(torch, lambda: hq.encode(plan, x, ws, out=out, dithered=dithered, tile_base=tile_base), iters)
+        td = _time(torch, lambda: hq.decode(plan, enc, ws, out=y), iters)
+        hq.check(ws)
+        bits = enc.total_bits()
+        inb = x.element_size()
+        extra = {"lattice": "ZA2D4E8"[[0, 1, 3, 5][lat]:[1, 3, 5, 7][lat]], "bps": round(bits / n_el, 4),
+                 "dithered": dithered}
+        rows.append(_row(name, "kv_encode" if dithered else "encode", te, n_el, inb, bits, n_tiles, extra))
+        rows.append(_row(name, "kv_decode" if dithered else "decode", td, n_el, y.element_size(), bits, n_tiles,
+                         extra))
+        return plan, enc, ws
+
+    x = W.c1(dev)
+    alpha = float(np.float32(np.sqrt(2 * np.pi * np.e) * W.c1_sigma_eff() / 32.0))
+    codec("fp32 4096x128 (one tile per row), fixed alpha", x, 3, 4.0, alpha=alpha, out_dtype=torch.float32)
+    x = W.c2(dev)
+    for bps in (3.0, 5.0):
+        codec("bf16 4096x4096 weight", x, 3, bps)
+    del x
+    k, v, q = W.c3(dev)
+    codec("KV bf16 [8,8,32768,128] K", k, 2, 2.0, dithered=True)
+    codec("KV bf16 [8,8,32768,128] V", v, 2, 2.0, dithered=True, tile_base=k.numel() // 128)
+    del k, v, q
+    torch.cuda.empty_cache()
+    x = W.c4(dev)
+    for lat, bps in ((1, 3.0), (1, 5.0), (0, 3.0), (0, 5.0), (3, 4.0)):
+        codec("bf16 8192x28672 weight", x, lat, bps)
+        torch.cuda.empty_cache()
+    del x
+    torch.cuda.empty_cache()
+    k, v, q = W.c5(dev)
+    heads, seq, qph = 8, 131072, 4
+    plan, enc, ws = codec("KV bf16 [1,8,131072,128] K", k, 3, 1.7, dithered=True)
+    sc = torch.empty(heads * qph, seq, dtype=torch.float32, device=dev)
+    ts = _time(torch, lambda: hq.kv_scores(plan, enc, heads, seq, q, qph, ws, out=sc), iters)
+    hq.check(ws)
+    n_el = k.numel()
+    bits = enc.total_bits()
+    rows.append(_row("KV bf16 [1,8,131072,128] K x 32 query heads", "kv_scores (fused decode + dot)", ts, n_el, 0.0,
+                     bits, n_el // 128, {"bps": round(bits / n_el, 4),
+                                         "scores_GBps": round(sc.numel() * 4 / (ts * 1e-3) / 1e9, 1)},
+                     other_bytes=4.0 * (sc.numel() + q.numel())))
+    codec("KV bf16 [1,8,131072,128] V", v, 3, 1.7, dithered=True, tile_base=n_el // 128)
+    del k, v, q, sc
+    torch.cuda.empty_cache()
+    return rows
 
 
 def main():
@@ -166,6 +260,8 @@ def main():
             "algorithmic_bytes_per_launch": int(alg_bytes),
         },
     }
+    if not args.no_rows:
+        line["rows"] = workload_rows(hq, W, torch, np, args.row_iters)
     if not args.no_cpu_baseline:
         xb = x0.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
         line["cpu_baseline"] = cpu_baseline(xb, alpha, seed, args.cpu_reps)
