@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=15)
     ap.add_argument("--no-rows", action="store_true", help="only the headline workload")
     ap.add_argument("--row-iters", type=int, default=10)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 64 MiB device-to-device copy (known bytes, to scale HBM counters)")
     return ap.parse_args()
 
 
@@ -193,6 +195,13 @@ def main():
             ev[2].record(stream)
         return enc
 
+    if args.calib_copy:
+        a = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+        b = torch.ones(64 << 20, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            a.copy_(b)
+        torch.cuda.synchronize()
+        del a, b
     for i in range(args.warmup):
         step(i)
     hq.check(ws)

@@ -6,9 +6,7 @@
 #include <cstdlib>
 #include <cstdint>
 #include <cstring>
-#include <mutex>
 #include <new>
-#include <unordered_map>
 
 #include "../../include/hq.h"
 #include "hq_kernels.h"
@@ -50,26 +48,6 @@ bool lattice_ok(int lat) { return lat >= HQ_Z && lat <= HQ_E8; }
 
 hq_status dev_err(hipError_t e) { return e == hipSuccess ? HQ_OK : HQ_ERR_DEVICE; }
 
-// Calls on one workspace are stream-ordered, so the host numbers them: the
-// number tags the look-back words of that call (1 .. 2^24-1, never 0, so a
-// zero-filled workspace never matches).
-// Rounds a work-group waits on an unready predecessor before recomputing its
-// aggregate itself (environment HQ_LOOKBACK_SPINS; 0 forces recomputation).
-uint32_t lookback_spins() {
-  const char* e = std::getenv("HQ_LOOKBACK_SPINS");
-  if (!e || !*e) return 512u;
-  return (uint32_t)std::strtoul(e, nullptr, 10);
-}
-
-uint32_t next_epoch(void* ws) {
-  static std::mutex mu;
-  static std::unordered_map<void*, uint32_t> epochs;
-  std::lock_guard<std::mutex> g(mu);
-  uint32_t& e = epochs[ws];
-  e = e % 0xFFFFFFu + 1u;
-  return e;
-}
-
 void fill_common(const hq_plan_s* p, uint32_t sgn[4], uint32_t& k0, uint32_t& k1) {
   for (int i = 0; i < 4; ++i) sgn[i] = p->sgn[i];
   k0 = (uint32_t)p->seed;
@@ -92,8 +70,9 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   if (!x) return HQ_ERR_ARG;
   if (!len_only && (!words || !k)) return HQ_ERR_ARG;
   if (((uintptr_t)x & 15u) != 0) return HQ_ERR_ARG;
-  // descriptors hold 38-bit bit counts; chunk tickets are 32-bit
-  if (n_tiles > (hq::kDescValueMask / max_record_bits(plan->lattice))) return HQ_ERR_ARG;
+  if (((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+  // chunk indices are 32-bit (grid x)
+  if (hq::ws_chunks(n_tiles) > 0x7FFFFFFFull) return HQ_ERR_ARG;
   hq::EncArgs a{};
   a.x = x;
   a.n_tiles = n_tiles;
@@ -105,13 +84,13 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   a.c_enc = plan->c_enc;
   a.tile_base = tile_base;
   a.ws = (hq::WsHeader*)ws;
-  const uint64_t chunks = hq::ws_chunks(n_tiles);
-  a.desc = (uint64_t*)((char*)ws + sizeof(hq::WsHeader));
-  a.tail = a.desc + chunks;
-  a.partials = (unsigned long long*)a.desc;
-  a.n_chunks = (uint32_t)chunks;
-  a.epoch = len_only ? 0u : next_epoch(ws);
-  a.lookback_spins = lookback_spins();
+  const hq::WsLayout lay = hq::ws_layout(n_tiles);
+  a.n_chunks = (uint32_t)hq::ws_chunks(n_tiles);
+  a.agg = (uint32_t*)((char*)ws + lay.agg);
+  a.E = (uint64_t*)((char*)ws + lay.E);
+  a.loc = (uint32_t*)((char*)ws + lay.loc);
+  a.stage = (uint32_t*)((char*)ws + lay.stage);
+  a.partials = (unsigned long long*)a.E;
   return dev_err(hq::launch_encode(plan->lattice, dither, dtype == HQ_BF16, len_only, a, st));
 }
 

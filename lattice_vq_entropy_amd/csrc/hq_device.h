@@ -107,22 +107,35 @@ __device__ __forceinline__ uint32_t row_scan_u32(uint32_t x) {
         "+v"(x[6]), "+v"(x[7])                                                   \
       : "v"(c))
 
+// Lanes of a 16-lane row whose vector index v(r) has bit s set (s = 0..3), and
+// those where popcount(v(r)) is odd, repeated over the four rows of a wave.
+constexpr uint64_t kLaneBit0 = 0x5A5A5A5A5A5A5A5Aull;
+constexpr uint64_t kLaneBit1 = 0x3C3C3C3C3C3C3C3Cull;
+constexpr uint64_t kLaneBit2 = 0xF0F0F0F0F0F0F0F0ull;
+constexpr uint64_t kLaneBit3 = 0xFF00FF00FF00FF00ull;
+constexpr uint64_t kLaneOdd = 0x6996699669966996ull;
+
+// +1 in the lanes outside the lane mask, -1 inside it.  Built at its use (the
+// asm is not hoisted or merged), so it holds a register only for one stage.
+__device__ __forceinline__ float lane_sign_of(uint64_t mask) {
+  float c;
+  asm volatile("v_cndmask_b32_e64 %0, 1.0, -1.0, %1" : "=v"(c) : "s"(mask));
+  return c;
+}
+
 struct FwhtSigns {
-  float c0, c1, c2, c3;  // +1 / -1 per cross-lane stage: bit s of the lane's vector
-  float lane_sign;       // (-1)^popcount(v)
+  float lane_sign;  // (-1)^popcount(v)
 };
 
 __device__ __forceinline__ FwhtSigns fwht_signs(int v) {
   FwhtSigns s;
-  s.c0 = (v & 1) ? -1.0f : 1.0f;
-  s.c1 = (v & 2) ? -1.0f : 1.0f;
-  s.c2 = (v & 4) ? -1.0f : 1.0f;
-  s.c3 = (v & 8) ? -1.0f : 1.0f;
   s.lane_sign = (__builtin_popcount(v) & 1) ? -1.0f : 1.0f;
   return s;
 }
 
-__device__ __forceinline__ void fwht_tile(float x[8], const FwhtSigns& fs) {
+// Cross-lane stage s pairs lane r with the lane holding vector v ^ 2^s; the
+// sign c = -1 where bit s of v is set.
+__device__ __forceinline__ void fwht_tile(float x[8], const FwhtSigns&) {
   // in-lane strides 1, 2, 4 (index bits 0..2): plain butterflies
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
@@ -135,10 +148,10 @@ __device__ __forceinline__ void fwht_tile(float x[8], const FwhtSigns& fs) {
     }
   }
   float c;
-  c = fs.c0; HQ_DPP_STAGE("quad_perm:[1,0,3,2]");  // stride 8
-  c = fs.c1; HQ_DPP_STAGE("quad_perm:[2,3,0,1]");  // stride 16
-  c = fs.c2; HQ_DPP_STAGE("row_half_mirror");      // stride 32
-  c = fs.c3; HQ_DPP_STAGE("row_ror:8");            // stride 64
+  c = lane_sign_of(kLaneBit0); HQ_DPP_STAGE("quad_perm:[1,0,3,2]");  // stride 8
+  c = lane_sign_of(kLaneBit1); HQ_DPP_STAGE("quad_perm:[2,3,0,1]");  // stride 16
+  c = lane_sign_of(kLaneBit2); HQ_DPP_STAGE("row_half_mirror");      // stride 32
+  c = lane_sign_of(kLaneBit3); HQ_DPP_STAGE("row_ror:8");            // stride 64
 }
 
 // ---------------------------------------------------------------------------
@@ -158,41 +171,49 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
 // ---------------------------------------------------------------------------
 // Nearest points [HQ Methodology 2; SPLAG ch. 20] in the integer embeddings
 // Z, A2 checkerboard {(i,j): i = j mod 2} with real point (i, j sqrt3),
-// D4 = {x in Z^4: sum even}, 2E8.  Outputs are the stripped symbols
-// [HQ Methodology 3] of each vector directly, and for E8 the raw coset bit.
+// D4 = {x in Z^4: sum even}, 2E8.  Rounding to the nearest integer (ties to
+// even) is the fp32 add of 1.5*2^23: for |h| < 2^22 the sum r has ulp 1, so it
+// holds rint(h) exactly, read as r - 1.5*2^23 or, as an integer, as
+// bits(r) - bits(1.5*2^23); the parity of rint(h) is bit 0 of bits(r).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void np_z(const float* u, int32_t* sym) {
-  sym[0] = (int32_t)__builtin_rintf(u[0]);
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr uint32_t kMagicBits = 0x4B400000u;
+
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+__device__ __forceinline__ uint32_t zigzag(int32_t v) {
+  return ((uint32_t)v << 1) ^ (uint32_t)(v >> 31);
+}
+__device__ __forceinline__ int32_t unzigzag(uint32_t m) {
+  return (int32_t)(m >> 1) ^ -(int32_t)(m & 1u);
 }
 
-// D4: round, fix the parity on the first coordinate of largest error; symbols
-// x0, x1, x2 and (x3 - parity(x0+x1+x2)) >> 1.
-__device__ __forceinline__ void np_d4(const float* u, int32_t* sym) {
-  float f[4];
+// D4: round every coordinate; when the sum is odd, move the first coordinate of
+// largest |u - f| by 1 toward u (upward iff u - f >= 0).  e = u - f is exact.
+__device__ __forceinline__ void d4_core(const float u[4], int32_t x[4]) {
+  float e[4];
+  uint32_t rb[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = __builtin_rintf(u[i]);
-  int32_t xi[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xi[i] = (int32_t)f[i];
-  int32_t s = xi[0] + xi[1] + xi[2] + xi[3];
-  if (s & 1) {
-    float e[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = __builtin_fabsf(u[i] - f[i]);
-    int j = 0;
-    float w = e[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) if (e[i] > w) { w = e[i]; j = i; }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i == j) xi[i] += (u[i] - f[i] >= 0.0f) ? 1 : -1;
+  for (int i = 0; i < 4; ++i) {
+    const float r = u[i] + kMagic;
+    rb[i] = fbits(r);
+    e[i] = u[i] - (r - kMagic);
   }
-  int32_t p = (xi[0] + xi[1] + xi[2]) & 1;
-  sym[0] = xi[0]; sym[1] = xi[1]; sym[2] = xi[2];
-  sym[3] = (xi[3] - p) >> 1;
+  const bool odd = ((rb[0] ^ rb[1] ^ rb[2] ^ rb[3]) & 1u) != 0;
+  const float emax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(e[0]), __builtin_fabsf(e[1])),
+                                     __builtin_fmaxf(__builtin_fabsf(e[2]), __builtin_fabsf(e[3])));
+  bool seen = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool hit = __builtin_fabsf(e[i]) == emax;
+    const bool fj = odd && hit && !seen;
+    seen = seen || hit;
+    const bool up = e[i] >= 0.0f;
+    x[i] = (int32_t)(rb[i] - kMagicBits) + (int32_t)(fj && up) - (int32_t)(fj && !up);
+  }
 }
 
-// A2: best of the two rectangular cosets; symbols (i - (j & 1)) >> 1 and j.
+// A2: best of the two rectangular cosets (ties even).
 __device__ __forceinline__ float a2_dist(float u0, float u1, int32_t i, int32_t j) {
   float e0 = u0 - (float)i;
   float t = (float)j * kSqrt3;
@@ -210,66 +231,63 @@ __device__ __forceinline__ void np_a2_codes(float u0, float u1, int32_t& i, int3
   j = even ? je : jo;
 }
 
-__device__ __forceinline__ void np_a2(const float* u, int32_t* sym) {
-  int32_t i, j;
-  np_a2_codes(u[0], u[1], i, j);
-  sym[0] = (i - (j & 1)) >> 1;
-  sym[1] = j;
-}
-
-// 2E8 = 2D8 u (2D8 + 1).  With h = u/2, ye = rint(h), yo = floor(h) and
-// a_i = |u_i - 2 ye_i| (exact), the halved squared-distance difference of the
-// parity-fixed even and odd candidates is
-//   (sum a_i - 4) + [sum ye odd] 2 (1 - max a) - [sum yo odd] 2 min a,
+// 2E8 = 2D8 u (2D8 + 1), returned as halves y (x = 2y + b, b = 1 for the odd
+// coset).  With h = u/2, ye = rint(h) and d = u - 2 ye (exact, |d| <= 1; as
+// fma(2, M - r, u) it is never -0), floor(h) = ye - [d < 0], and the halved
+// squared-distance difference of the parity-fixed even and odd candidates is
+//   (sum |d_i| - 4) + [sum ye odd] 2 (1 - max |d|) - [sum floor(h) odd] 2 min |d|,
 // evaluated in fp32 in this order (sum sequential); even wins ties.  The fix
-// moves the first coordinate of largest |u - c| by 2 toward u.  Symbols: the
-// halves y_i = (x_i - b) / 2 with y_7's redundant low bit dropped, i.e. y_7 >> 1
-// (the sum of the halves is even), and the raw coset bit b.
-__device__ __forceinline__ void np_e8(const float* u, int32_t* sym, uint32_t& raw) {
-  float ye[8], yo[8], a[8];
+// moves the first coordinate of largest |u - c| by 2 toward u: for the even
+// coset the first argmax of |d|, upward iff d >= 0; for the odd coset the
+// first argmin of |d|, upward iff d < 0 or d = 1 (d = 1 at the argmin means
+// every |d_i| = 1, i.e. min |d| = 1).  Every adjustment of ye is -1, 0 or +1:
+// a borrow and a carry on the integer.
+__device__ __forceinline__ void e8_core(const float u[8], int32_t y[8], bool& odd) {
+  float d[8];
+  uint32_t rb[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float h = u[i] * 0.5f;
-    ye[i] = __builtin_rintf(h);
-    yo[i] = __builtin_floorf(h);
-    a[i] = __builtin_fabsf(__builtin_fmaf(-2.0f, ye[i], u[i]));  // exact
+    const float r = __builtin_fmaf(u[i], 0.5f, kMagic);  // u/2 is exact: one rounding
+    rb[i] = fbits(r);
+    d[i] = __builtin_fmaf(2.0f, kMagic - r, u[i]);
   }
-  float S = a[0];
+  float S = __builtin_fabsf(d[0]), amax = S, amin = S;
 #pragma unroll
-  for (int i = 1; i < 8; ++i) S = S + a[i];
-  float sye = ye[0], syo = yo[0];  // integer-valued sums: exact in fp32
+  for (int i = 1; i < 8; ++i) {
+    const float ai = __builtin_fabsf(d[i]);
+    S = S + ai;
+    amax = __builtin_fmaxf(amax, ai);
+    amin = __builtin_fminf(amin, ai);
+  }
+  const uint32_t xr = rb[0] ^ rb[1] ^ rb[2] ^ rb[3] ^ rb[4] ^ rb[5] ^ rb[6] ^ rb[7];
+  bool pn = false;  // parity of the number of negative d
 #pragma unroll
-  for (int i = 1; i < 8; ++i) { sye = sye + ye[i]; syo = syo + yo[i]; }
-  int pe = (int32_t)sye & 1, po = (int32_t)syo & 1;
-  float amax = a[0], amin = a[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) { amax = __builtin_fmaxf(amax, a[i]); amin = __builtin_fminf(amin, a[i]); }
+  for (int i = 0; i < 8; ++i) pn = pn != (d[i] < 0.0f);
+  const bool pe = (xr & 1u) != 0;
+  const bool po = pe != pn;
   float delta = S - 4.0f;
-  if (pe) delta = delta + 2.0f * (1.0f - amax);
-  if (po) delta = delta - 2.0f * amin;
-  bool even = delta <= 0.0f;
-  float target = even ? amax : amin;
-  int fix = even ? pe : po;
-  // first coordinate attaining the target
-  int j = 7;
+  const float t1 = __builtin_fmaf(2.0f, 1.0f - amax, delta);  // delta + 2 (1 - max): exact product
+  delta = pe ? t1 : delta;
+  const float t2 = __builtin_fmaf(-2.0f, amin, delta);  // delta - 2 min: exact product
+  delta = po ? t2 : delta;
+  const bool even = delta <= 0.0f;
+  odd = !even;
+  const float target = even ? amax : amin;
+  const bool fix = even ? pe : po;
+  const bool amin1 = amin == 1.0f;
+  bool seen = false;
 #pragma unroll
-  for (int i = 6; i >= 0; --i) j = (a[i] == target) ? i : j;
-  int32_t y[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = (int32_t)(even ? ye[i] : yo[i]);
-  if (fix) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i != j) continue;
-      // even: direction of u - 2ye; odd: of u - (2yo + 1)
-      float c = even ? 2.0f * ye[i] : __builtin_fmaf(2.0f, yo[i], 1.0f);
-      y[i] += (u[i] - c >= 0.0f) ? 1 : -1;
-    }
+  for (int i = 0; i < 8; ++i) {
+    const bool neg = d[i] < 0.0f;
+    const bool hit = __builtin_fabsf(d[i]) == target;
+    const bool fj = fix && hit && !seen;
+    seen = seen || hit;
+    const bool up = even ? !neg : (neg || amin1);
+    const bool down = odd && neg;  // floor(h) = ye - 1
+    const bool P = fj && up && !down;
+    const bool Q = (down && !fj) || (fj && !up);
+    y[i] = (int32_t)(rb[i] - kMagicBits) + (int32_t)P - (int32_t)Q;
   }
-#pragma unroll
-  for (int i = 0; i < 7; ++i) sym[i] = y[i];
-  sym[7] = y[7] >> 1;
-  raw = even ? 0u : 1u;
 }
 
 // Codes of one lattice vector from its symbols (inverse of the strip), as
@@ -301,20 +319,41 @@ template <> __device__ __forceinline__ void unstrip_embed<3>(const int32_t* sym,
   p[7] = (float)(2 * (2 * sym[7] + par) + b);
 }
 
-// Quantise the 8 values of one lane to symbols (and raw bits for E8).
-template <int L> __device__ __forceinline__ void quantize_lane(const float u[8], int32_t sym[8], uint32_t& raw) {
-  raw = 0;
+// Quantise the lane's 8 values [HQ Methodology 2] and strip them
+// [Methodology 3]: zigzag symbols, and for E8 the coset bit.  Symbols: Z x;
+// A2 (i - (j & 1)) >> 1 and j; D4 x0, x1, x2, (x3 - parity(x0+x1+x2)) >> 1;
+// E8 the halves y_0..y_6 and y_7 >> 1 (the sum of the halves is even).
+template <int L>
+__device__ __forceinline__ void quantize_syms(const float u[8], uint32_t m[8], bool& odd) {
+  odd = false;
   if constexpr (L == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) np_z(&u[i], &sym[i]);
+    for (int i = 0; i < 8; ++i) m[i] = zigzag((int32_t)(fbits(u[i] + kMagic) - kMagicBits));
   } else if constexpr (L == 1) {
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) np_a2(&u[i], &sym[i]);
+    for (int h = 0; h < 8; h += 2) {
+      int32_t i, j;
+      np_a2_codes(u[h], u[h + 1], i, j);
+      m[h] = zigzag((i - (j & 1)) >> 1);
+      m[h + 1] = zigzag(j);
+    }
   } else if constexpr (L == 2) {
-    np_d4(&u[0], &sym[0]);
-    np_d4(&u[4], &sym[4]);
+#pragma unroll
+    for (int h = 0; h < 8; h += 4) {
+      int32_t x[4];
+      d4_core(&u[h], x);
+      const int32_t p = (x[0] ^ x[1] ^ x[2]) & 1;
+      m[h] = zigzag(x[0]);
+      m[h + 1] = zigzag(x[1]);
+      m[h + 2] = zigzag(x[2]);
+      m[h + 3] = zigzag((x[3] - p) >> 1);
+    }
   } else {
-    np_e8(u, sym, raw);
+    int32_t y[8];
+    e8_core(u, y, odd);
+#pragma unroll
+    for (int i = 0; i < 7; ++i) m[i] = zigzag(y[i]);
+    m[7] = zigzag(y[7] >> 1);
   }
 }
 
@@ -348,32 +387,20 @@ __device__ __forceinline__ void dither_lane(uint32_t k0, uint32_t k1, uint64_t t
   } else if constexpr (L == 2) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) tau[i] = 2.0f * f[i];
-    int32_t s[8];
-    np_d4(&tau[0], &s[0]);
-    np_d4(&tau[4], &s[4]);
-    float p[8];
-    unstrip_embed<2>(&s[0], 0, &p[0]);
-    unstrip_embed<2>(&s[4], 0, &p[4]);
+    int32_t x[8];
+    d4_core(&tau[0], &x[0]);
+    d4_core(&tau[4], &x[4]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = tau[i] - p[i];
+    for (int i = 0; i < 8; ++i) d[i] = tau[i] - (float)x[i];
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) tau[i] = 4.0f * f[i];
-    int32_t s[8];
-    uint32_t raw;
-    np_e8(tau, s, raw);
-    float p[8];
-    unstrip_embed<3>(s, raw, p);
+    int32_t y[8];
+    bool odd;
+    e8_core(tau, y, odd);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = tau[i] - p[i];
+    for (int i = 0; i < 8; ++i) d[i] = tau[i] - (float)(2 * y[i] + (odd ? 1 : 0));
   }
-}
-
-__device__ __forceinline__ uint32_t zigzag(int32_t v) {
-  return ((uint32_t)v << 1) ^ (uint32_t)(v >> 31);
-}
-__device__ __forceinline__ int32_t unzigzag(uint32_t m) {
-  return (int32_t)(m >> 1) ^ -(int32_t)(m & 1u);
 }
 
 }  // namespace hq

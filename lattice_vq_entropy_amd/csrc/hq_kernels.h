@@ -21,12 +21,23 @@ struct EncArgs {
   uint32_t key0, key1;
   uint64_t tile_base;
   WsHeader* ws;
-  uint64_t* desc;
-  uint64_t* tail;  // (epoch << 32) | last 32 bits of each chunk
-  unsigned long long* partials;  // length-only pass: bits per work-group
   uint32_t n_chunks;
-  uint32_t epoch;  // tag of this call's look-back words, 1 .. 2^24-1
-  uint32_t lookback_spins;  // rounds before an unready predecessor is recomputed
+  uint32_t* agg;     // bits per chunk
+  uint64_t* E;       // chunk bit offsets, n_chunks + 1
+  uint32_t* loc;     // chunk-local bit offset per tile
+  uint32_t* stage;   // kSlotWords staging words per chunk
+  unsigned long long* partials;  // length-only pass: bits per chunk
+};
+
+struct PlaceArgs {
+  const uint32_t* stage;
+  const uint64_t* E;
+  const uint32_t* loc;
+  uint64_t n_tiles;
+  uint32_t n_chunks;
+  uint32_t* words;
+  uint64_t cap_words;
+  uint64_t* offsets;
 };
 
 struct DecArgs {

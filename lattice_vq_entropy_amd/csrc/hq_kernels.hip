@@ -21,28 +21,26 @@ namespace hq {
 
 __device__ __forceinline__ void set_status(WsHeader* ws, int code) { atomicOr(&ws->status, 1u << code); }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+// One lane's 8 input coordinates of one tile, as loaded (raw bits).
+template <bool BF16> struct InVec;
+template <> struct InVec<true> { uint4 w; };
+template <> struct InVec<false> { uint4 w0, w1; };
 
-// Load the lane's 8 coordinates of tile t (fp32 or bf16), signs of D applied.
 template <bool BF16>
-__device__ __forceinline__ void load_lane(const void* x, uint64_t t, int v, const uint32_t smask[8], float xv[8]) {
+__device__ __forceinline__ InVec<BF16> load_in(const void* x, uint64_t t, int v, bool valid) {
+  InVec<BF16> in;
   if constexpr (BF16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + t * kTile + 8 * v);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t s = ww[i] ^ smask[i];  // sign bits 15 and 31 of the pair
-      xv[2 * i] = bf16_lo(s);
-      xv[2 * i + 1] = bf16_hi(s);
-    }
+    in.w = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) in.w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + t * kTile + 8 * v);
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + t * kTile + 8 * v);
-    const uint4 w0 = p[0], w1 = p[1];
-    const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xv[i] = __builtin_bit_cast(float, ww[i] ^ smask[i]);
+    in.w0 = in.w1 = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + t * kTile + 8 * v);
+      in.w0 = p[0];
+      in.w1 = p[1];
+    }
   }
+  return in;
 }
 
 template <bool BF16>
@@ -60,21 +58,15 @@ __device__ __forceinline__ bool lane_nonfinite(const void* x, uint64_t t, int v)
   return nf;
 }
 
-// OR a value of up to 64 bits into the LDS bit stream at bit P (stream word i
-// lives at s[1 + i]; s[0] holds the predecessor's tail).
-__device__ __forceinline__ void lds_or64(uint32_t* s, uint32_t P, uint32_t lo, uint32_t hi) {
-  const uint32_t w = 1 + (P >> 5), sh = P & 31;
-  if (sh == 0) {
-    if (lo) atomicOr(&s[w], lo);
-    if (hi) atomicOr(&s[w + 1], hi);
-  } else {
-    const uint32_t x0 = lo << sh;
-    const uint32_t x1 = __builtin_amdgcn_alignbit(hi, lo, 32 - sh);
-    const uint32_t x2 = hi >> (32 - sh);
-    if (x0) atomicOr(&s[w], x0);
-    if (x1) atomicOr(&s[w + 1], x1);
-    if (x2) atomicOr(&s[w + 2], x2);
-  }
+// OR a value of up to 64 bits into the LDS bit stream s at bit P (stream bit
+// P is bit P % 32 of s[P / 32]).
+__device__ __forceinline__ void lds_or64(uint32_t* s, uint32_t P, uint64_t val) {
+  const uint32_t w = P >> 5, sh = P & 31;
+  const uint64_t lo = val << sh;                      // words w, w + 1
+  const uint32_t x2 = (uint32_t)((val >> 32) << sh >> 32);  // word w + 2
+  atomicOr(&s[w], (uint32_t)lo);
+  atomicOr(&s[w + 1], (uint32_t)(lo >> 32));
+  if (x2) atomicOr(&s[w + 2], x2);
 }
 
 __device__ __forceinline__ uint32_t rev4(uint32_t n) {
@@ -84,26 +76,43 @@ __device__ __forceinline__ uint32_t rev4(uint32_t n) {
 // ===========================================================================
 // Encode
 // ===========================================================================
-// Per-lane constants of a plan: butterfly signs, the scale with the lane
-// sign folded in, and the sign bits of D for the lane's 8 coordinates.
+// Per-lane constants of a plan: butterfly signs, the scale with the lane sign
+// folded in, and the sign bits of D for the lane's 8 coordinates.
 template <bool BF16>
 struct LaneConst {
   FwhtSigns fs;
   float scale;
-  uint32_t smask[8];
+  // signs of D for the lane's 8 coordinates: bf16, bit 15 - i = coordinate
+  // 2i and bit 31 - i = coordinate 2i + 1 (so pair i's flips are
+  // (sm << i) & 0x80008000); fp32, bit 31 - i = coordinate i
+  uint32_t sm;
   __device__ __forceinline__ LaneConst(const uint32_t sgn[4], int v, float c) {
     fs = fwht_signs(v);
     scale = fs.lane_sign * c;
     const uint32_t sbyte = (sgn[v >> 2] >> ((v & 3) * 8)) & 0xFFu;
+    sm = 0;
     if constexpr (BF16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        smask[i] = (((sbyte >> (2 * i)) & 1u) << 15) | (((sbyte >> (2 * i + 1)) & 1u) << 31);
-#pragma unroll
-      for (int i = 4; i < 8; ++i) smask[i] = 0;
+      for (int i = 0; i < 4; ++i) sm |= (((sbyte >> (2 * i)) & 1u) << (15 - i)) | (((sbyte >> (2 * i + 1)) & 1u) << (31 - i));
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) smask[i] = ((sbyte >> i) & 1u) << 31;
+      for (int i = 0; i < 8; ++i) sm |= ((sbyte >> i) & 1u) << (31 - i);
+    }
+  }
+  // the lane's 8 coordinates with the signs of D applied, as fp32
+  __device__ __forceinline__ void apply(const InVec<BF16>& in, float xv[8]) const {
+    if constexpr (BF16) {
+      const uint32_t ww[4] = {in.w.x, in.w.y, in.w.z, in.w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t s = ww[i] ^ ((sm << i) & 0x80008000u);  // sign bits 15 and 31 of the pair
+        xv[2 * i] = __builtin_bit_cast(float, s << 16);
+        xv[2 * i + 1] = __builtin_bit_cast(float, s & 0xFFFF0000u);
+      }
+    } else {
+      const uint32_t ww[8] = {in.w0.x, in.w0.y, in.w0.z, in.w0.w, in.w1.x, in.w1.y, in.w1.z, in.w1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[i] = __builtin_bit_cast(float, ww[i] ^ ((sm << i) & 0x80000000u));
     }
   }
 };
@@ -112,41 +121,38 @@ struct LaneConst {
 // record length.
 struct TileSyms {
   uint32_t m[8];  // zigzag symbols of the lane's coordinates
-  uint32_t raw;   // E8 coset bit of the lane's vector
   uint32_t k;     // Rice parameter of the tile
-  uint32_t L;     // record length of the tile (bits)
-  uint32_t ulen;  // unary bits of the lane's 8 symbols
+  uint32_t L;     // record length of the tile (bits); 0 for a tile past the end
+  uint32_t U;     // unary bits of the lane's 8 symbols
+  bool odd;       // E8 coset bit of the lane's vector
 };
 
 // RHT -> (dither) -> nearest point -> strip -> zigzag -> Rice k for tile t,
 // held by the 16-lane row of the calling lane.  Every lane of the wave calls
-// it (it uses ballots); invalid tiles yield zero symbols.
+// it (ballots).  A tile past the end has zero input and L = 0.
 template <int L, bool DITHER, bool BF16>
-__device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF16>& lc, uint64_t t, bool valid,
-                                           int v, int r, int grp, TileSyms& ts) {
+__device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF16>& lc, const InVec<BF16>& in,
+                                           uint64_t t, bool valid, int v, int r, int grp, TileSyms& ts) {
   constexpr uint32_t RAW = Lat<L>::raw;
-  float xv[8];
-  if (valid) {
-    load_lane<BF16>(a.x, t, v, lc.smask, xv);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xv[i] = 0.0f;
-  }
-  fwht_tile(xv, lc.fs);
+  float d[8];  // the dither first: its own nearest-point search then runs with only the input in flight
+  if constexpr (DITHER) dither_lane<L>(a.key0, a.key1, a.tile_base + t, v, d);
   float u[8];
+  lc.apply(in, u);
+  fwht_tile(u, lc.fs);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) u[i] = xv[i] * lc.scale;
+  for (int i = 0; i < 8; ++i) u[i] = u[i] * lc.scale;
   if constexpr (DITHER) {
-    float d[8];
-    dither_lane<L>(a.key0, a.key1, a.tile_base + t, v, d);
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[i] = u[i] + d[i];
   }
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) bad |= !(__builtin_fabsf(u[i]) < kRangeLimit);
+  quantize_syms<L>(u, ts.m, ts.odd);
   const uint64_t bad_mask = __ballot(bad);
   if (bad_mask) {
+    // a tile with a non-finite input or a coordinate beyond the range: record
+    // the error and code it as zeros (the output is unspecified then)
     const bool tile_bad = ((bad_mask >> (grp * 16)) & 0xFFFFull) != 0;
     bool nf = false;
     if (tile_bad && valid) nf = lane_nonfinite<BF16>(a.x, t, v);
@@ -154,322 +160,239 @@ __device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF1
     if (tile_bad) {
       if (r == 0 && valid) set_status(a.ws, tile_nf ? 2 : 3);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) u[i] = 0.0f;
+      for (int i = 0; i < 8; ++i) ts.m[i] = 0u;
+      ts.odd = false;
     }
-  }
-  int32_t sym[8];
-  quantize_lane<L>(u, sym, ts.raw);
-  uint32_t lsum = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ts.m[i] = valid ? zigzag(sym[i]) : 0u;
-    lsum += ts.m[i];
   }
   // Rice parameter: the smallest k with S(k) = sum ceil((m >> k)/2) <= 128
   // minimises the tile length.  From M = sum m: S(k) <= 128 once
   // M <= 2^(k+7) (at kA) and S(k) > 128 while M >= 3*2^(k+7), so the answer
   // is one of kA-2, kA-1, kA; S(k) = A_k - A_(k+1) with A_j = sum m >> j.
-  const uint32_t M = row_sum_u32(lsum);
-  const int kA = M <= 128u ? 0 : (32 - __builtin_clz(M - 1u)) - 7;
-  const int c = kA >= 2 ? kA - 2 : 0;
+  const uint32_t M = row_sum_u32(((ts.m[0] + ts.m[1]) + (ts.m[2] + ts.m[3])) + ((ts.m[4] + ts.m[5]) + (ts.m[6] + ts.m[7])));
+  const uint32_t kA = M <= 128u ? 0u : (32u - (uint32_t)__builtin_clz(M - 1u)) - 7u;
+  const uint32_t c = kA >= 2u ? kA - 2u : 0u;
   uint32_t a0 = 0, a1 = 0, a2 = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t tt = ts.m[i] >> c;
-    a0 += tt;
-    a1 += tt >> 1;
-    a2 += tt >> 2;
+    a0 += ts.m[i] >> c;
+    a1 += ts.m[i] >> (c + 1u);
+    a2 += ts.m[i] >> (c + 2u);
   }
   const uint32_t tot = row_sum_u32(a0 | (a1 << 10) | (a2 << 20));  // A_c <= 512
   const uint32_t A0 = tot & 1023u, A1 = (tot >> 10) & 1023u, A2 = tot >> 20;
   uint32_t Ak, ak;
   if (A0 - A1 <= 128u) { ts.k = c; Ak = A0; ak = a0; }
-  else if (A1 - A2 <= 128u) { ts.k = c + 1; Ak = A1; ak = a1; }
-  else { ts.k = c + 2; Ak = A2; ak = a2; }
-  ts.ulen = ak + 8u;
+  else if (A1 - A2 <= 128u) { ts.k = c + 1u; Ak = A1; ak = a1; }
+  else { ts.k = c + 2u; Ak = A2; ak = a2; }
+  ts.U = ak + 8u;
   ts.L = valid ? RAW + 128u * (1u + ts.k) + Ak : 0u;
 }
 
-// Assemble one tile's record at local bit tb of the LDS stream s (stream word
-// i at s[1 + i]).  Every lane of the wave calls it (ballot, shuffles); only
-// lanes of valid tiles write.
+// Assemble one tile's record at local bit tb of the zero-filled LDS stream s.  Every lane of the wave calls it (ballot,
+// shuffles); only lanes of valid tiles write.
 template <int L>
 __device__ __forceinline__ void tile_pack(uint32_t* s, uint32_t tb, const TileSyms& ts, int v, int r, int lane,
                                           int grp, bool valid) {
   constexpr uint32_t RAW = Lat<L>::raw;
   const uint32_t k = ts.k;
   if constexpr (RAW > 0) {
-    const uint64_t bm = __ballot((ts.raw & 1u) != 0);
+    const uint64_t bm = __ballot(ts.odd);
     const uint32_t g16 = (uint32_t)(bm >> (grp * 16)) & 0xFFFFu;
     // bit v of the field is the coset bit of vector v, held by lane v(r)
     const uint32_t raw16 = (g16 & 0x0F0Fu) | (rev4((g16 >> 4) & 0xFu) << 4) | (rev4((g16 >> 12) & 0xFu) << 12);
-    if (valid && r == 0) lds_or64(s, tb, raw16, 0u);
+    if (valid && r == 0) lds_or64(s, tb, raw16);
   }
   // exclusive scan of the unary lengths in vector order
-  const uint32_t U = ts.ulen;
-  const int rowbase = lane & ~15;
-  const uint32_t Uv = (uint32_t)__shfl((int)U, rowbase | lane_vector(r));
+  const int src = (lane & ~15) | lane_vector(r);
+  const uint32_t Uv = (uint32_t)__shfl((int)ts.U, src);
   const uint32_t incl = row_scan_u32(Uv);
-  const uint32_t exv = incl - Uv;
-  const uint32_t excl = (uint32_t)__shfl((int)exv, rowbase | lane_vector(r));
+  const uint32_t excl = (uint32_t)__shfl((int)(incl - Uv), src);
   if (!valid) return;
-  const uint32_t rpos = tb + RAW + 8u * (uint32_t)v * k;
   if (k != 0) {
-    const uint32_t mask = (1u << k) - 1u;
+    const uint32_t rpos = tb + RAW + 8u * (uint32_t)v * k;
     if (k <= 8) {
-      uint32_t lo = 0, hi = 0;
+      uint32_t lo = __builtin_amdgcn_ubfe(ts.m[0], 0, k), hi = __builtin_amdgcn_ubfe(ts.m[4], 0, k);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) lo |= (ts.m[j] & mask) << (j * k);
-#pragma unroll
-      for (int j = 4; j < 8; ++j) hi |= (ts.m[j] & mask) << ((j - 4) * k);
-      const uint64_t R = (uint64_t)lo | ((uint64_t)hi << (4 * k));
-      lds_or64(s, rpos, (uint32_t)R, (uint32_t)(R >> 32));
+      for (int j = 1; j < 4; ++j) {
+        lo |= __builtin_amdgcn_ubfe(ts.m[j], 0, k) << (j * k);
+        hi |= __builtin_amdgcn_ubfe(ts.m[4 + j], 0, k) << (j * k);
+      }
+      lds_or64(s, rpos, (uint64_t)lo | ((uint64_t)hi << (4 * k)));
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) lds_or64(s, rpos + j * k, ts.m[j] & mask, 0u);
+      for (int j = 0; j < 8; ++j) lds_or64(s, rpos + j * k, __builtin_amdgcn_ubfe(ts.m[j], 0, k));
     }
   }
   const uint32_t upos = tb + RAW + 128u * k + excl;
-  if (U <= 64u) {
+  if (ts.U <= 64u) {
     uint64_t msk = 0;
-    uint32_t pos = 0;
+    uint32_t pos = ~0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      pos += ts.m[j] >> k;
-      msk |= 1ull << pos;
-      pos += 1;
+      pos += (ts.m[j] >> k) + 1u;
+      msk += 1ull << pos;
     }
-    lds_or64(s, upos, (uint32_t)msk, (uint32_t)(msk >> 32));
+    lds_or64(s, upos, msk);
   } else {
     uint32_t pos = upos;
     for (int j = 0; j < 8; ++j) {
       pos += ts.m[j] >> k;
-      atomicOr(&s[1 + (pos >> 5)], 1u << (pos & 31));
+      atomicOr(&s[pos >> 5], 1u << (pos & 31));
       pos += 1;
     }
   }
 }
 
-// Exclusive scan of the kChunkTiles lengths in ln[] into lo[0..kChunkTiles]
-// (lo[kChunkTiles] = chunk total); wave 0 only.
-__device__ __forceinline__ void chunk_scan(const uint32_t* ln, uint32_t* lo, int tid, int lane) {
-  uint32_t l = tid < kChunkTiles ? ln[tid] : 0u;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(l, o);
-    if (lane >= o) l += y;
-  }
-  if (tid < kChunkTiles) lo[tid + 1] = l;
-  if (tid == 0) lo[0] = 0;
+// Sum of a 32-bit value over the 64 lanes; every lane receives it.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  x = row_sum_u32(x);
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+         __builtin_amdgcn_readlane(x, 48);
 }
 
-// Look-back control words (LDS) written by wave 0 for the whole work-group.
-enum : uint32_t { kLbDone = 0, kLbAdvance = 1, kLbRetry = 2, kLbFallback = 3 };
-
-// One chunk per work-group, chunk = blockIdx.x.  The single pass computes the
-// chunk's symbols and lengths, publishes its bit total (aggregate), packs its
-// bits in LDS, publishes its last 32 bits (tail), looks back over the
-// predecessors' descriptors for its exclusive bit offset, then stores.
-//
-// Forward progress needs no assumption about dispatch order or residency:
-// when a predecessor's descriptor stays unready for a.lookback_spins rounds
-// (one round: device-coherent loads of 256 descriptors and a short sleep),
-// the work-group recomputes that chunk's aggregate itself (and its tail if it
-// is the immediate predecessor), as in the "decoupled fallback" single-pass
-// scan.  All inter-work-group words carry the call's epoch, so relaxed
-// device-scope atomics suffice and no same-address atomic is used.
+// Encode, step 1 of 3: one chunk of kChunkTiles tiles per work-group, chunk =
+// blockIdx.x.  Per pass of 16 tiles: front, tile lengths, offsets within the
+// chunk, packing into LDS.  Then the chunk's bits go to its staging slot, its
+// bit count to agg, and per tile the chunk-local bit offset and k.  No
+// work-group waits on another.  LEN_ONLY: the chunk's bit count only.
 template <int L, bool DITHER, bool BF16, bool LEN_ONLY>
 __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
-  __shared__ uint32_t s_stage[kStageWords + 1];
-  __shared__ uint32_t s_tbuf[kMaxRecordWords + 4];  // fallback: one tile's record
-  __shared__ uint32_t s_len[kChunkTiles], s_lo[kChunkTiles + 1], s_k[kChunkTiles];
-  __shared__ uint32_t s_len2[kChunkTiles], s_lo2[kChunkTiles + 1];
-  __shared__ uint32_t s_ctl[4];
-  __shared__ uint64_t s_ctl64[2];
+  __shared__ __align__(16) uint32_t s_stage[kSlotWords];
+  __shared__ uint32_t s_len[kChunkTiles], s_lo[kChunkTiles], s_k[kChunkTiles];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
   const int v = lane_vector(r);
+  const int pslot = wv * 4 + grp;
   const LaneConst<BF16> lc(a.sgn, v, a.c_enc);
   const uint32_t chunk = blockIdx.x;
-  const uint32_t epoch = a.epoch;
   const uint64_t t_first = (uint64_t)chunk * kChunkTiles;
 
-  TileSyms ts[kPasses];
+  InVec<BF16> in[kPasses];
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
-    const int slot = p * 16 + wv * 4 + grp;
-    const uint64_t t = t_first + slot;
-    const bool valid = t < a.n_tiles;
-    tile_front<L, DITHER, BF16>(a, lc, t, valid, v, r, grp, ts[p]);
-    if (r == 0) {
-      s_len[slot] = ts[p].L;
-      s_k[slot] = ts[p].k;
-    }
+    const uint64_t t = t_first + p * 16 + pslot;
+    in[p] = load_in<BF16>(a.x, t, v, t < a.n_tiles);
   }
-  __syncthreads();
-  if (wv == 0) chunk_scan(s_len, s_lo, tid, lane);
-  __syncthreads();
-  const uint32_t A = s_lo[kChunkTiles];
 
   if constexpr (LEN_ONLY) {
-    if (tid == 0) a.partials[chunk] = A;
-  } else {
-    const uint64_t ep = (uint64_t)epoch << kDescEpochShift;
-    if (tid == 0)
-      __hip_atomic_store(&a.desc[chunk], (chunk == 0 ? kDescFlagIncl : kDescFlagAgg) | ep | (uint64_t)A,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t nz = ((A + 31u) >> 5) + 2u;
-    for (uint32_t i = tid; i < nz; i += 256) s_stage[1 + i] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-      const int slot = p * 16 + wv * 4 + grp;
-      tile_pack<L>(s_stage, s_lo[slot], ts[p], v, r, lane, grp, t_first + slot < a.n_tiles);
+      const int slot = p * 16 + pslot;
+      const uint64_t t = t_first + slot;
+      TileSyms ts;
+      tile_front<L, DITHER, BF16>(a, lc, in[p], t, t < a.n_tiles, v, r, grp, ts);
+      if (r == 0) s_len[slot] = ts.L;
     }
     __syncthreads();
-    if (tid == 0) {
-      const uint32_t b = A - 32u;  // A >= 128: every chunk holds a tile
-      const uint32_t w = 1 + (b >> 5), sh = b & 31;
-      const uint32_t tailv = sh ? __builtin_amdgcn_alignbit(s_stage[w + 1], s_stage[w], sh) : s_stage[w];
-      __hip_atomic_store(&a.tail[chunk], ((uint64_t)epoch << 32) | tailv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_ctl[1] = 0;  // predecessor tail not yet known
+    if (wv == 0) {
+      const uint32_t A = wave_sum_u32(lane < kChunkTiles ? s_len[lane] : 0u);
+      if (lane == 0) a.partials[chunk] = A;
     }
-
-    // ---- look-back (work-group-wide loop; wave 0 reads 256 descriptors) ----
-    uint64_t excl = 0;
-    int64_t j = (int64_t)chunk - 1;
-    int spins = 0;
-    while (j >= 0) {
-      if (wv == 0) {
-        uint64_t val[4];
-        bool rdy[4], isP[4];
+  } else {
+    for (int i = tid; i < kSlotWords / 4; i += 256) reinterpret_cast<uint4*>(s_stage)[i] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t base = 0;  // wave-uniform bit offset of the current pass
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t idx = j - 4 * lane - q;
-          const uint64_t d = idx >= 0 ? __hip_atomic_load(&a.desc[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-          const uint32_t dep = (uint32_t)(d >> kDescEpochShift) & 0xFFFFFFu;
-          const uint64_t flag = d >> 62;
-          rdy[q] = idx < 0 || (flag != 0 && dep == epoch);
-          isP[q] = idx < 0 || (rdy[q] && flag == 2);
-          val[q] = idx >= 0 ? (d & kDescValueMask) : 0ull;
-        }
-        // first stop (inclusive or unready descriptor), newest first
-        int qs = 4;
-#pragma unroll
-        for (int q = 3; q >= 0; --q) qs = (isP[q] || !rdy[q]) ? q : qs;
-        uint64_t before = 0, all4 = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (q < qs) before += val[q];
-          all4 += val[q];
-        }
-        const uint64_t bs = __ballot(qs < 4);
-        const int fl = bs ? __builtin_ctzll(bs) : 64;
-        uint64_t contrib = lane < fl ? all4 : (lane == fl ? before : 0ull);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) contrib += __shfl_xor(contrib, o);
-        if (lane == (fl < 64 ? fl : 0)) {
-          uint32_t ctl;
-          uint64_t add = contrib;
-          if (fl == 64) {
-            ctl = kLbAdvance;
-          } else if (isP[qs < 4 ? qs : 0] && qs < 4) {
-            ctl = kLbDone;
-            add += val[qs];
-          } else {
-            ctl = spins < (int)a.lookback_spins ? kLbRetry : kLbFallback;
-            s_ctl64[1] = (uint64_t)(j - 4 * fl - qs);  // the unready chunk
-          }
-          s_ctl[0] = ctl;
-          s_ctl64[0] = add;
-        }
+    for (int p = 0; p < kPasses; ++p) {
+      const int slot = p * 16 + pslot;
+      const uint64_t t = t_first + slot;
+      const bool valid = t < a.n_tiles;
+      TileSyms ts;
+      tile_front<L, DITHER, BF16>(a, lc, in[p], t, valid, v, r, grp, ts);
+      if (r == 0) {
+        s_len[slot] = ts.L;
+        s_k[slot] = ts.k;
       }
       __syncthreads();
-      const uint32_t ctl = s_ctl[0];
-      const uint64_t add = s_ctl64[0];
-      const int64_t jf = (int64_t)s_ctl64[1];
-      __syncthreads();
-      if (ctl == kLbDone) {
-        excl += add;
-        break;
-      }
-      if (ctl == kLbAdvance) {
-        excl += add;
-        j -= 256;
-        continue;
-      }
-      if (ctl == kLbRetry) {
-        ++spins;
-        __builtin_amdgcn_s_sleep(2);
-        continue;
-      }
-      // Fallback: compute chunk jf's aggregate here (and, for the immediate
-      // predecessor, its last 32 bits), then continue below it.
-      const uint64_t tf = (uint64_t)jf * kChunkTiles;  // a full chunk: jf < chunk
-      for (uint32_t i = tid; i < kMaxRecordWords + 4; i += 256) s_tbuf[i] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int p = 0; p < kPasses; ++p) {
-        const int slot = p * 16 + wv * 4 + grp;
-        TileSyms fsy;
-        tile_front<L, DITHER, BF16>(a, lc, tf + slot, true, v, r, grp, fsy);
-        if (r == 0) s_len2[slot] = fsy.L;
-        if (jf == (int64_t)chunk - 1 && p == kPasses - 1 && wv == 3) {
-          tile_pack<L>(s_tbuf, 0u, fsy, v, r, lane, grp, grp == 3);  // slot kChunkTiles-1
-          if (grp == 3 && r == 0) s_ctl[2] = fsy.L;
-        }
-      }
-      __syncthreads();
-      if (wv == 0) chunk_scan(s_len2, s_lo2, tid, lane);
-      __syncthreads();
-      excl += add + s_lo2[kChunkTiles];
-      if (jf == (int64_t)chunk - 1 && tid == 0) {
-        const uint32_t Lt = s_ctl[2], b = Lt - 32u;
-        const uint32_t w = 1 + (b >> 5), sh = b & 31;
-        s_stage[0] = sh ? __builtin_amdgcn_alignbit(s_tbuf[w + 1], s_tbuf[w], sh) : s_tbuf[w];
-        s_ctl[1] = 1;
-      }
-      j = jf - 1;
-      spins = 0;
-      __syncthreads();
+      // offsets within the pass: every row scans the pass's 16 lengths
+      const uint32_t len = s_len[p * 16 + r];
+      const uint32_t incl = row_scan_u32(len);
+      const uint32_t tb = base + (uint32_t)__shfl((int)(incl - len), (lane & ~15) | pslot);
+      if (r == 0) s_lo[slot] = tb;
+      base += __builtin_amdgcn_readlane(incl, 15);
+      tile_pack<L>(s_stage, tb, ts, v, r, lane, grp, valid);
     }
-    if (tid == 0) {
-      if (chunk > 0)
-        __hip_atomic_store(&a.desc[chunk], kDescFlagIncl | ep | (excl + A), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_ctl64[0] = excl;
-      if (chunk == 0) {
-        s_stage[0] = 0;
-      } else if (s_ctl[1] == 0) {
-        // the predecessor is running (it published its descriptor itself) and
-        // publishes its tail before its own look-back
-        uint64_t tw;
-        while (((tw = __hip_atomic_load(&a.tail[chunk - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 32) !=
-               (uint64_t)epoch)
-          __builtin_amdgcn_s_sleep(1);
-        s_stage[0] = (uint32_t)tw;
-      }
-    }
+    const uint32_t A = base;  // >= 256: every chunk holds a tile
     __syncthreads();
-
-    const uint64_t E = s_ctl64[0];
+    // the used words and at least one zero word after them, in whole uint4
+    const uint32_t n4 = ((A >> 5) + 2u + 3u) >> 2;
+    uint4* dst = reinterpret_cast<uint4*>(a.stage + (uint64_t)chunk * kSlotWords);
+    for (uint32_t i = tid; i < n4; i += 256) dst[i] = reinterpret_cast<const uint4*>(s_stage)[i];
     if (tid < kChunkTiles) {
       const uint64_t t = t_first + tid;
       if (t < a.n_tiles) {
-        a.offsets[t] = E + s_lo[tid];
+        a.loc[t] = s_lo[tid];
         a.kout[t] = (uint8_t)s_k[tid];
-        if (t == a.n_tiles - 1) a.offsets[a.n_tiles] = E + s_lo[tid + 1];
       }
     }
-    const bool last = t_first + kChunkTiles >= a.n_tiles;
-    const uint64_t first = E >> 5;
-    const uint32_t sh = (uint32_t)(E & 31);
-    const uint64_t endw = last ? (E + A + 31) >> 5 : (E + A) >> 5;
-    if (tid == 0 && endw > a.cap_words) set_status(a.ws, 4);
-    const uint64_t stop = endw < a.cap_words ? endw : a.cap_words;
-    for (uint64_t w = first + tid; w < stop; w += 256) {
-      const uint32_t i = (uint32_t)(w - first);
-      a.words[w] = sh ? __builtin_amdgcn_alignbit(s_stage[1 + i], s_stage[i], 32 - sh) : s_stage[1 + i];
+    if (tid == 0) a.agg[chunk] = A;
+  }
+}
+
+// Encode, step 2 of 3: exclusive scan of the chunk bit counts into the chunk
+// offsets E[0..n] (E[n] = total), by one work-group of 1024 threads, each
+// summing a contiguous strip.
+__global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, uint64_t* E, uint64_t cap_words,
+                                               WsHeader* ws) {
+  __shared__ uint64_t s_w[16];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t per = (n + 1023u) / 1024u;
+  const uint32_t lo = min(tid * per, n), hi = min(lo + per, n);
+  uint64_t sum = 0;
+  for (uint32_t i = lo; i < hi; ++i) sum += agg[i];
+  // inclusive scan over the wave, then over the 16 wave totals
+  uint64_t x = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(x, o);
+    if ((int)lane >= o) x += y;
+  }
+  if (lane == 63) s_w[wv] = x;
+  __syncthreads();
+  uint64_t before = 0;
+  for (uint32_t w = 0; w < wv; ++w) before += s_w[w];
+  uint64_t run = before + x - sum;
+  for (uint32_t i = lo; i < hi; ++i) {
+    E[i] = run;
+    run += agg[i];
+  }
+  if (tid == 1023) {
+    E[n] = run;  // the last thread's strip ends at n
+    if ((run + 31) / 32 > cap_words) atomicOr(&ws->status, 1u << 4);
+  }
+}
+
+// Encode, step 3 of 3: one chunk per work-group.  The chunk's staged bits go
+// to stream bits [E[c], E[c+1]) with a funnel shift; the word shared with the
+// predecessor takes the predecessor's last bits from its staging slot, so
+// every stream word is written exactly once.  Also the per-tile offsets.
+__global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
+  const uint32_t chunk = blockIdx.x, tid = threadIdx.x;
+  const uint64_t E = a.E[chunk], E1 = a.E[chunk + 1];
+  const uint64_t t_first = (uint64_t)chunk * kChunkTiles;
+  if (tid < kChunkTiles) {
+    const uint64_t t = t_first + tid;
+    if (t < a.n_tiles) {
+      a.offsets[t] = E + a.loc[t];
+      if (t == a.n_tiles - 1) a.offsets[a.n_tiles] = E1;
     }
+  }
+  const uint32_t* st = a.stage + (uint64_t)chunk * kSlotWords;
+  uint32_t tail = 0;  // bits E-32 .. E-1 of the stream
+  if (chunk > 0) {
+    const uint32_t* sp = st - kSlotWords;
+    const uint32_t b = (uint32_t)(E - a.E[chunk - 1]) - 32u;
+    tail = __builtin_amdgcn_alignbit(sp[(b >> 5) + 1], sp[b >> 5], b & 31);
+  }
+  const bool last = chunk == a.n_chunks - 1;
+  const uint64_t first = E >> 5;
+  const uint32_t sh = (uint32_t)(E & 31);
+  const uint64_t endw = last ? (E1 + 31) >> 5 : E1 >> 5;
+  const uint64_t stop = endw < a.cap_words ? endw : a.cap_words;
+  for (uint64_t w = first + tid; w < stop; w += 256) {
+    const uint32_t i = (uint32_t)(w - first);
+    const uint32_t cur = st[i];
+    const uint32_t prev = i == 0 ? tail : st[i - 1];
+    a.words[w] = sh ? __builtin_amdgcn_alignbit(cur, prev, 32 - sh) : cur;
   }
 }
 
@@ -840,9 +763,20 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
     hipLaunchKernelGGL((encode_k<L, DITHER, BF16, true>), grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL(reduce_k<unsigned long long>, dim3(1), dim3(256), 0, st,
                        (const unsigned long long*)a.partials, a.n_chunks, &a.ws->bits);
-  } else {
-    hipLaunchKernelGGL((encode_k<L, DITHER, BF16, false>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
   }
+  hipLaunchKernelGGL((encode_k<L, DITHER, BF16, false>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(scan_k, dim3(1), dim3(1024), 0, st, (const uint32_t*)a.agg, a.n_chunks, a.E, a.cap_words, a.ws);
+  PlaceArgs pa;
+  pa.stage = a.stage;
+  pa.E = a.E;
+  pa.loc = a.loc;
+  pa.n_tiles = a.n_tiles;
+  pa.n_chunks = a.n_chunks;
+  pa.words = a.words;
+  pa.cap_words = a.cap_words;
+  pa.offsets = a.offsets;
+  hipLaunchKernelGGL(place_k, grid, dim3(256), 0, st, pa);
   return hipGetLastError();
 }
 
