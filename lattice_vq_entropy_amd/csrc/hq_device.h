@@ -181,6 +181,17 @@ constexpr uint32_t kMagicBits = 0x4B400000u;
 
 __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// x - c + [lane in plus] - [lane in minus]: one add with carry-in and one
+// subtract with borrow-in, the lane masks being wave-wide (scalar) values.
+// c is held in a vector register (one scalar operand per instruction).
+__device__ __forceinline__ int32_t add_sub_lane(uint32_t x, uint32_t c, uint64_t plus, uint64_t minus) {
+  uint32_t t, r;
+  uint64_t co;
+  asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(t), "=s"(co) : "v"(x), "s"(plus));
+  asm("v_subb_co_u32_e64 %0, %1, %2, %3, %4" : "=v"(r), "=s"(co) : "v"(t), "v"(c), "s"(minus));
+  return (int32_t)r;
+}
+
 __device__ __forceinline__ uint32_t zigzag(int32_t v) {
   return ((uint32_t)v << 1) ^ (uint32_t)(v >> 31);
 }
@@ -190,6 +201,9 @@ __device__ __forceinline__ int32_t unzigzag(uint32_t m) {
 
 // D4: round every coordinate; when the sum is odd, move the first coordinate of
 // largest |u - f| by 1 toward u (upward iff u - f >= 0).  e = u - f is exact.
+// The decisions are wave-wide lane masks (ballots), combined with scalar
+// logic, and applied as carry/borrow.  Every lane of the wave (or of the
+// active set) must call it.
 __device__ __forceinline__ void d4_core(const float u[4], int32_t x[4]) {
   float e[4];
   uint32_t rb[4];
@@ -199,17 +213,18 @@ __device__ __forceinline__ void d4_core(const float u[4], int32_t x[4]) {
     rb[i] = fbits(r);
     e[i] = u[i] - (r - kMagic);
   }
-  const bool odd = ((rb[0] ^ rb[1] ^ rb[2] ^ rb[3]) & 1u) != 0;
+  const uint64_t ODD = __ballot(((rb[0] ^ rb[1] ^ rb[2] ^ rb[3]) & 1u) != 0);
   const float emax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(e[0]), __builtin_fabsf(e[1])),
                                      __builtin_fmaxf(__builtin_fabsf(e[2]), __builtin_fabsf(e[3])));
-  bool seen = false;
+  const uint32_t cm = kMagicBits;
+  uint64_t seen = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bool hit = __builtin_fabsf(e[i]) == emax;
-    const bool fj = odd && hit && !seen;
-    seen = seen || hit;
-    const bool up = e[i] >= 0.0f;
-    x[i] = (int32_t)(rb[i] - kMagicBits) + (int32_t)(fj && up) - (int32_t)(fj && !up);
+    const uint64_t HIT = __ballot(__builtin_fabsf(e[i]) == emax);
+    const uint64_t UP = __ballot(e[i] >= 0.0f);
+    const uint64_t FJ = ODD & HIT & ~seen;
+    seen |= HIT;
+    x[i] = add_sub_lane(rb[i], cm, FJ & UP, FJ & ~UP);
   }
 }
 
@@ -259,12 +274,18 @@ __device__ __forceinline__ void e8_core(const float u[8], int32_t y[8], bool& od
     amax = __builtin_fmaxf(amax, ai);
     amin = __builtin_fminf(amin, ai);
   }
-  const uint32_t xr = rb[0] ^ rb[1] ^ rb[2] ^ rb[3] ^ rb[4] ^ rb[5] ^ rb[6] ^ rb[7];
-  bool pn = false;  // parity of the number of negative d
+  // wave-wide lane masks; the logic below is scalar
+  uint64_t NEG[8], PN = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pn = pn != (d[i] < 0.0f);
-  const bool pe = (xr & 1u) != 0;
-  const bool po = pe != pn;
+  for (int i = 0; i < 8; ++i) {
+    NEG[i] = __ballot(d[i] < 0.0f);
+    PN ^= NEG[i];  // parity of the number of negative d
+  }
+  const uint32_t xr = rb[0] ^ rb[1] ^ rb[2] ^ rb[3] ^ rb[4] ^ rb[5] ^ rb[6] ^ rb[7];
+  const uint64_t PE = __ballot((xr & 1u) != 0);
+  const uint64_t PO = PE ^ PN;
+  const bool pe = __builtin_amdgcn_inverse_ballot_w64(PE);
+  const bool po = __builtin_amdgcn_inverse_ballot_w64(PO);
   float delta = S - 4.0f;
   const float t1 = __builtin_fmaf(2.0f, 1.0f - amax, delta);  // delta + 2 (1 - max): exact product
   delta = pe ? t1 : delta;
@@ -273,20 +294,21 @@ __device__ __forceinline__ void e8_core(const float u[8], int32_t y[8], bool& od
   const bool even = delta <= 0.0f;
   odd = !even;
   const float target = even ? amax : amin;
-  const bool fix = even ? pe : po;
-  const bool amin1 = amin == 1.0f;
-  bool seen = false;
+  const uint64_t EVEN = __ballot(even);
+  const uint64_t FIX = (EVEN & PE) | (~EVEN & PO);
+  const uint64_t ODDUP = ~EVEN & __ballot(amin == 1.0f);
+  const uint32_t cm = kMagicBits;
+  uint64_t seen = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const bool neg = d[i] < 0.0f;
-    const bool hit = __builtin_fabsf(d[i]) == target;
-    const bool fj = fix && hit && !seen;
-    seen = seen || hit;
-    const bool up = even ? !neg : (neg || amin1);
-    const bool down = odd && neg;  // floor(h) = ye - 1
-    const bool P = fj && up && !down;
-    const bool Q = (down && !fj) || (fj && !up);
-    y[i] = (int32_t)(rb[i] - kMagicBits) + (int32_t)P - (int32_t)Q;
+    const uint64_t HIT = __ballot(__builtin_fabsf(d[i]) == target);
+    const uint64_t FJ = FIX & HIT & ~seen;
+    seen |= HIT;
+    const uint64_t DOWN = ~EVEN & NEG[i];                    // floor(h) = ye - 1
+    const uint64_t UP = (EVEN & ~NEG[i]) | DOWN | ODDUP;     // direction of the fix
+    const uint64_t P = FJ & UP & ~DOWN;
+    const uint64_t Q = (DOWN & ~FJ) | (FJ & ~UP);
+    y[i] = add_sub_lane(rb[i], cm, P, Q);
   }
 }
 

@@ -225,13 +225,10 @@ __device__ __forceinline__ void tile_pack(uint32_t* s, uint32_t tb, const TileSy
   }
   const uint32_t upos = tb + RAW + 128u * k + excl;
   if (ts.U <= 64u) {
-    uint64_t msk = 0;
-    uint32_t pos = ~0u;
+    // built from the last code back: V_j = ((V_(j+1) << 1) | 1) << q_j
+    uint64_t msk = 1ull << (ts.m[7] >> k);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pos += (ts.m[j] >> k) + 1u;
-      msk += 1ull << pos;
-    }
+    for (int j = 6; j >= 0; --j) msk = ((msk << 1) | 1ull) << (ts.m[j] >> k);
     lds_or64(s, upos, msk);
   } else {
     uint32_t pos = upos;
