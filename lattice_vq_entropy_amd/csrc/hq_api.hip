@@ -89,6 +89,7 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   a.agg = (uint32_t*)((char*)ws + lay.agg);
   a.E = (uint64_t*)((char*)ws + lay.E);
   a.loc = (uint32_t*)((char*)ws + lay.loc);
+  a.tailw = (uint32_t*)((char*)ws + lay.tailw);
   a.stage = (uint32_t*)((char*)ws + lay.stage);
   a.partials = (unsigned long long*)a.E;
   return dev_err(hq::launch_encode(plan->lattice, dither, dtype == HQ_BF16, len_only, a, st));

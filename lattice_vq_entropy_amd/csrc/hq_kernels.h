@@ -25,6 +25,7 @@ struct EncArgs {
   uint32_t* agg;     // bits per chunk
   uint64_t* E;       // chunk bit offsets, n_chunks + 1
   uint32_t* loc;     // chunk-local bit offset per tile
+  uint32_t* tailw;   // last 32 stream bits of each chunk
   uint32_t* stage;   // kSlotWords staging words per chunk
   unsigned long long* partials;  // length-only pass: bits per chunk
 };
@@ -33,6 +34,7 @@ struct PlaceArgs {
   const uint32_t* stage;
   const uint64_t* E;
   const uint32_t* loc;
+  const uint32_t* tailw;
   uint64_t n_tiles;
   uint32_t n_chunks;
   uint32_t* words;

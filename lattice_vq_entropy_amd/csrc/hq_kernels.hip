@@ -321,21 +321,47 @@ __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
         a.kout[t] = (uint8_t)s_k[tid];
       }
     }
-    if (tid == 0) a.agg[chunk] = A;
+    if (tid == 0) {
+      a.agg[chunk] = A;
+      const uint32_t b = A - 32u, w = b >> 5, sh = b & 31;
+      a.tailw[chunk] = sh ? __builtin_amdgcn_alignbit(s_stage[w + 1], s_stage[w], sh) : s_stage[w];
+    }
   }
 }
 
 // Encode, step 2 of 3: exclusive scan of the chunk bit counts into the chunk
-// offsets E[0..n] (E[n] = total), by one work-group of 1024 threads, each
-// summing a contiguous strip.
+// offsets E[0..n] (E[n] = total), by one work-group of 1024 threads.  Thread
+// i owns the strip of 4*per consecutive counts starting at 4*per*i, loaded
+// once (all loads in flight together) and kept in registers; agg is padded to
+// 64 entries, E to an even count.  Up to kScanRegs uint4 per thread (n up to
+// 32 Ki chunks); longer inputs read the rest of the strip twice.
+constexpr uint32_t kScanRegs = 8;
 __global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, uint64_t* E, uint64_t cap_words,
                                                WsHeader* ws) {
   __shared__ uint64_t s_w[16];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint32_t per = (n + 1023u) / 1024u;
-  const uint32_t lo = min(tid * per, n), hi = min(lo + per, n);
+  const uint32_t per = (n + 4095u) / 4096u;  // uint4 per thread
+  const uint32_t lo = tid * per * 4u;
+  uint4 q[kScanRegs];
   uint64_t sum = 0;
-  for (uint32_t i = lo; i < hi; ++i) sum += agg[i];
+#pragma unroll
+  for (uint32_t j = 0; j < kScanRegs; ++j) {
+    const uint32_t i = lo + 4u * j;
+    q[j] = (j < per && i < n) ? *reinterpret_cast<const uint4*>(agg + i) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  for (uint32_t j = kScanRegs; j < per; ++j) {  // long inputs only
+    const uint32_t i = lo + 4u * j;
+    if (i < n) {
+      const uint4 t = *reinterpret_cast<const uint4*>(agg + i);
+      sum += (uint64_t)t.x + (i + 1 < n ? t.y : 0u) + (i + 2 < n ? t.z : 0u) + (i + 3 < n ? t.w : 0u);
+    }
+  }
+#pragma unroll
+  for (uint32_t j = 0; j < kScanRegs; ++j) {
+    const uint32_t i = lo + 4u * j;
+    sum += (uint64_t)(i < n ? q[j].x : 0u) + (i + 1 < n ? q[j].y : 0u) + (i + 2 < n ? q[j].z : 0u) +
+           (i + 3 < n ? q[j].w : 0u);
+  }
   // inclusive scan over the wave, then over the 16 wave totals
   uint64_t x = sum;
 #pragma unroll
@@ -345,51 +371,84 @@ __global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, 
   }
   if (lane == 63) s_w[wv] = x;
   __syncthreads();
-  uint64_t before = 0;
-  for (uint32_t w = 0; w < wv; ++w) before += s_w[w];
-  uint64_t run = before + x - sum;
-  for (uint32_t i = lo; i < hi; ++i) {
-    E[i] = run;
-    run += agg[i];
+  uint64_t run = x - sum;
+  for (uint32_t w = 0; w < wv; ++w) run += s_w[w];
+  // writes four offsets from the counts t at i (i a multiple of 4, E + i
+  // 16-byte aligned) and advances run
+  auto put4 = [&](uint32_t i, const uint4& t) {
+    const uint64_t e0 = run, e1 = e0 + t.x, e2 = e1 + t.y, e3 = e2 + t.z;
+    if (i + 3 < n) {
+      reinterpret_cast<ulonglong2*>(E + i)[0] = make_ulonglong2(e0, e1);
+      reinterpret_cast<ulonglong2*>(E + i)[1] = make_ulonglong2(e2, e3);
+      run = e3 + t.w;
+    } else {  // the strip holding the last count
+      const uint32_t r = n - i;
+      E[i] = e0;
+      if (r > 1) E[i + 1] = e1;
+      if (r > 2) E[i + 2] = e2;
+      run = r == 1 ? e1 : r == 2 ? e2 : e3;
+    }
+  };
+#pragma unroll
+  for (uint32_t j = 0; j < kScanRegs; ++j) {
+    const uint32_t i = lo + 4u * j;
+    if (j < per && i < n) put4(i, q[j]);
   }
-  if (tid == 1023) {
-    E[n] = run;  // the last thread's strip ends at n
+  for (uint32_t j = kScanRegs; j < per; ++j) {
+    const uint32_t i = lo + 4u * j;
+    if (i < n) put4(i, *reinterpret_cast<const uint4*>(agg + i));
+  }
+  if (lo < n && lo + 4u * per >= n) {
+    E[n] = run;
     if ((run + 31) / 32 > cap_words) atomicOr(&ws->status, 1u << 4);
   }
 }
 
 // Encode, step 3 of 3: one chunk per work-group.  The chunk's staged bits go
-// to stream bits [E[c], E[c+1]) with a funnel shift; the word shared with the
-// predecessor takes the predecessor's last bits from its staging slot, so
-// every stream word is written exactly once.  Also the per-tile offsets.
+// to stream bits [E[c], E[c+1]) with a funnel shift, four words per thread
+// (one uint4 staging load, issued with the offset loads before they arrive);
+// the word shared with the predecessor takes the predecessor's last 32 bits,
+// recorded by step 1, so every stream word is written exactly once.  Also the
+// per-tile offsets.
 __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
-  const uint32_t chunk = blockIdx.x, tid = threadIdx.x;
-  const uint64_t E = a.E[chunk], E1 = a.E[chunk + 1];
-  const uint64_t t_first = (uint64_t)chunk * kChunkTiles;
-  if (tid < kChunkTiles) {
-    const uint64_t t = t_first + tid;
-    if (t < a.n_tiles) {
-      a.offsets[t] = E + a.loc[t];
-      if (t == a.n_tiles - 1) a.offsets[a.n_tiles] = E1;
-    }
-  }
+  const uint32_t tid = threadIdx.x, chunk = blockIdx.x;
   const uint32_t* st = a.stage + (uint64_t)chunk * kSlotWords;
-  uint32_t tail = 0;  // bits E-32 .. E-1 of the stream
-  if (chunk > 0) {
-    const uint32_t* sp = st - kSlotWords;
-    const uint32_t b = (uint32_t)(E - a.E[chunk - 1]) - 32u;
-    tail = __builtin_amdgcn_alignbit(sp[(b >> 5) + 1], sp[b >> 5], b & 31);
+  const uint64_t E = a.E[chunk], E1 = a.E[chunk + 1];
+  const uint4 c0 = *reinterpret_cast<const uint4*>(st + 4u * tid);  // words < 1024 < kSlotWords
+  uint32_t p0 = tid ? st[4u * tid - 1u] : 0u;
+  if (tid == 0 && chunk > 0) p0 = a.tailw[chunk - 1];
+  const uint64_t t = (uint64_t)chunk * kChunkTiles + tid;
+  const uint32_t lc = (tid < kChunkTiles && t < a.n_tiles) ? a.loc[t] : 0u;
+  if (tid < kChunkTiles && t < a.n_tiles) {
+    a.offsets[t] = E + lc;
+    if (t == a.n_tiles - 1) a.offsets[a.n_tiles] = E1;
   }
   const bool last = chunk == a.n_chunks - 1;
   const uint64_t first = E >> 5;
   const uint32_t sh = (uint32_t)(E & 31);
   const uint64_t endw = last ? (E1 + 31) >> 5 : E1 >> 5;
   const uint64_t stop = endw < a.cap_words ? endw : a.cap_words;
-  for (uint64_t w = first + tid; w < stop; w += 256) {
-    const uint32_t i = (uint32_t)(w - first);
-    const uint32_t cur = st[i];
-    const uint32_t prev = i == 0 ? tail : st[i - 1];
-    a.words[w] = sh ? __builtin_amdgcn_alignbit(cur, prev, 32 - sh) : cur;
+  const uint32_t nw = stop > first ? (uint32_t)(stop - first) : 0u;
+  uint4 c = c0;
+  uint32_t p = p0;
+  // staging words i..i+3 with i < nw <= 2962 stay inside the slot
+  for (uint32_t i = 4u * tid; i < nw; i += 1024u) {
+    if (i >= 1024u) {
+      c = *reinterpret_cast<const uint4*>(st + i);
+      p = st[i - 1];
+    }
+    uint32_t o[4];
+    if (sh) {
+      o[0] = __builtin_amdgcn_alignbit(c.x, p, 32 - sh);
+      o[1] = __builtin_amdgcn_alignbit(c.y, c.x, 32 - sh);
+      o[2] = __builtin_amdgcn_alignbit(c.z, c.y, 32 - sh);
+      o[3] = __builtin_amdgcn_alignbit(c.w, c.z, 32 - sh);
+    } else {
+      o[0] = c.x; o[1] = c.y; o[2] = c.z; o[3] = c.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i + e < nw) a.words[first + i + e] = o[e];
   }
 }
 
@@ -768,6 +827,7 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   pa.stage = a.stage;
   pa.E = a.E;
   pa.loc = a.loc;
+  pa.tailw = a.tailw;
   pa.n_tiles = a.n_tiles;
   pa.n_chunks = a.n_chunks;
   pa.words = a.words;

@@ -30,17 +30,19 @@ inline uint64_t ws_align(uint64_t b) { return (b + 255) & ~uint64_t(255); }
 
 // Regions after the header: agg (u32 per chunk), E (u64 per chunk + 1; the
 // length-only pass keeps its per-chunk partials here), loc (u32 per tile
-// slot), staging (kSlotWords u32 per chunk).
+// slot), tailw (u32 per chunk), staging (kSlotWords u32 per chunk).  Each
+// region starts on 256 bytes.
 struct WsLayout {
-  uint64_t agg, E, loc, stage, bytes;
+  uint64_t agg, E, loc, tailw, stage, bytes;
 };
 inline WsLayout ws_layout(uint64_t n_tiles) {
   const uint64_t c = ws_chunks(n_tiles);
   WsLayout L;
   L.agg = sizeof(WsHeader);
-  L.E = L.agg + ws_align(4 * c);
+  L.E = L.agg + ws_align(4 * c);  // 64 counts a block: the scan reads whole uint4
   L.loc = L.E + ws_align(8 * (c + 1));
-  L.stage = L.loc + ws_align(4 * c * kChunkTiles);
+  L.tailw = L.loc + ws_align(4 * c * kChunkTiles);
+  L.stage = L.tailw + ws_align(4 * c);
   L.bytes = L.stage + 4 * c * (uint64_t)kSlotWords;
   return L;
 }
