@@ -620,17 +620,20 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uin
     const uint32_t w = min(start >> 5, (uint32_t)kStageWords - 2u), sh = start & 31;
     uint32_t win = __builtin_amdgcn_alignbit(s[w + 1], s[w], sh);
     if (__builtin_popcount(win) >= 8) {
-      uint32_t prev = 0, qmax = 0;  // prev: bit after the previous one
+      // all 8 codes inside the 32-bit window: q < 32 <= qlim for k <= 17
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t pos = (uint32_t)__builtin_ctz(win);
-        const uint32_t q = pos - prev;  // < 32
-        qmax = max(qmax, q);
+        const uint32_t q = (uint32_t)__builtin_ctz(win);
         m[j] = (q << k) | rem[j];
-        prev = pos + 1;
-        win &= win - 1u;
+        win = (win >> q) >> 1;
       }
-      ok &= qmax < qlim;
+      if (k > 17u) {
+        // a quotient of up to 31 may reach 2^22 only for k > 17
+        uint32_t qmax = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qmax = max(qmax, m[j] >> k);
+        ok &= qmax < qlim;
+      }
     } else {
       uint32_t pos = start;
       const uint32_t wlim = (uend >> 5) + 1u;  // the staging buffer holds words up to here
@@ -659,7 +662,7 @@ template <int L, bool DITHER, int OUT>
 __global__ __launch_bounds__(256) void decode_k(DecArgs a) {
   constexpr uint32_t RAW = Lat<L>::raw;
   constexpr uint32_t MAXREC = RAW + 128u * 23u;
-  __shared__ uint32_t s_stage[kStageWords];
+  __shared__ __align__(16) uint32_t s_stage[kStageWords];
   __shared__ uint64_t s_off[kChunkTiles + 1];
   __shared__ uint32_t s_k[kChunkTiles];
   __shared__ uint32_t s_ust[16][16];
@@ -698,13 +701,44 @@ __global__ __launch_bounds__(256) void decode_k(DecArgs a) {
     }
   }
   __syncthreads();
-  const uint64_t w_first = s_off[0] >> 5;
+  // stream words [w_first, w_end) into LDS from the 16-byte boundary below
+  // w_first (s_stage[i] = word w_first + i), in uint4 loads all issued
+  // before the LDS stores; the words from w_end on read as zero
+  const uint64_t w_first = (s_off[0] >> 5) & ~3ull;
   const uint64_t w_end = (s_off[nt] + 31) >> 5;
-  const bool span_ok = s_off[nt] >= s_off[0] && (w_end - w_first) <= (uint64_t)kStageWords - 4 && w_end <= a.n_words;
+  const bool span_ok = s_off[nt] >= s_off[0] && (w_end - w_first) <= (uint64_t)kStageWords - 8 && w_end <= a.n_words;
   if (span_ok) {
     const uint32_t n = (uint32_t)(w_end - w_first);
-    for (uint32_t i = tid; i < n; i += 256) s_stage[i] = a.words[w_first + i];
-    for (uint32_t i = n + tid; i < n + 4; i += 256) s_stage[i] = 0u;
+    const uint32_t n4 = (n + 3) >> 2;
+    uint4 q[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const uint32_t i4 = (uint32_t)tid + 256u * j;
+      q[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (i4 < n4) {
+        const uint64_t wg = w_first + 4ull * i4;
+        if (wg + 4 <= a.n_words) {
+          q[j] = *reinterpret_cast<const uint4*>(a.words + wg);
+        } else {
+          q[j].x = a.words[wg];
+          if (4 * i4 + 1 < n) q[j].y = a.words[wg + 1];
+          if (4 * i4 + 2 < n) q[j].z = a.words[wg + 2];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const uint32_t i4 = (uint32_t)tid + 256u * j;
+      if (i4 <= n4) {  // one zero uint4 after the last
+        uint4 v4 = q[j];
+        const uint32_t i = 4 * i4;
+        if (i + 0 >= n) v4.x = 0u;
+        if (i + 1 >= n) v4.y = 0u;
+        if (i + 2 >= n) v4.z = 0u;
+        if (i + 3 >= n) v4.w = 0u;
+        reinterpret_cast<uint4*>(s_stage)[i4] = v4;
+      }
+    }
   }
   __syncthreads();
 
