@@ -182,7 +182,22 @@ def traffic_for(op: str):
     if vals.get("source_hash") != source_hash():
         return None
     return {"fetch_bytes": float(vals["fetch_bytes"]), "write_bytes": float(vals["write_bytes"]),
-            "total_bytes": float(vals["fetch_bytes"]) + float(vals["write_bytes"])}
+            "total_bytes": float(vals["fetch_bytes"]) + float(vals["write_bytes"]),
+            "valu_lane_ops": float(vals["valu_lane_ops"]) if "valu_lane_ops" in vals else None}
+
+
+VALU_PEAK = 256 * 4 * 16 * 2.4e9  # CUs x SIMDs x lanes x clock: 32-bit VALU lane-ops per second
+
+
+def valu_for(op: str, ms: float):
+    """VALU issue of one launch from the counter summary: lane-ops per second
+    against the 39.3 T lane-ops/s the vector ALUs can issue."""
+    t = traffic_for(op)
+    if not t or not t.get("valu_lane_ops"):
+        return None
+    ach = t["valu_lane_ops"] / (ms * 1e-3)
+    return {"achieved": round(ach / 1e12, 2), "peak": round(VALU_PEAK / 1e12, 2), "unit": "T lane-ops/s",
+            "frac": round(ach / VALU_PEAK, 4), "ops_per_launch": t["valu_lane_ops"]}
 
 
 def main():
@@ -339,9 +354,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_for(dominant),
+            "traffic": (traffic_for(dominant) or {}).get("total_bytes"),
             "algorithmic_bytes_per_launch": int(alg_bytes),
         },
+        "valu": {"encode": valu_for("encode", enc_ms), "decode": valu_for("decode", dec_ms)},
     }
     if not args.no_rows:
         line["rows"] = workload_rows(hq, W, torch, np, args.row_iters)

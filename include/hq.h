@@ -27,13 +27,15 @@
  *     corrupt stream) are recorded in the workspace and returned by
  *     hq_status_sync; the outputs of the failing call are then unspecified.
  *     When several data errors occur, the lowest code is reported.
- *   - Workspace: a device buffer of hq_workspace_bytes() bytes, zero-filled
- *     by the caller once before its first use.  One workspace must not be
- *     used by two calls that can run concurrently (e.g. on two streams).
- *   - hq_encode has no device-wide wait that depends on scheduling: a
- *     work-group that waits too long on a predecessor's bit count recomputes
- *     it.  The environment variable HQ_LOOKBACK_SPINS (default 512) sets how
- *     long it waits; 0 recomputes at once (a test setting).
+ *   - Workspace: a device buffer of hq_workspace_bytes() bytes (about 12 KB
+ *     per 32 tiles: it holds each chunk's staged bits between the launches of
+ *     one encode), 16-byte aligned, zero-filled by the caller once before its
+ *     first use.  One workspace must not be used by two calls that can run
+ *     concurrently (e.g. on two streams).
+ *   - No call waits on another work-group's progress; encode is three
+ *     stream-ordered launches (pack per chunk, scan of the chunk bit counts,
+ *     placement).  Encode and decode allocate nothing and can be captured in
+ *     a HIP graph.
  *   - Tensors are row-major; every 128 consecutive elements form one tile
  *     (weights: tiles along rows; KV [B, H, S, 128]: one tile per vector).
  *   - Stream layout: record of tile t at bits [offsets[t], offsets[t+1]):

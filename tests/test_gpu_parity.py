@@ -118,17 +118,17 @@ def test_lattice_parity_ragged(hq, orc, lat, dtype, dithered):
     full_parity(hq, orc, lat, x, alpha_for(lat, sigma, bps), dithered=dithered, tile_base=12345 if dithered else 0)
 
 
-@pytest.mark.parametrize("lat", [3, 2])
-def test_lookback_recomputation_path(hq, orc, lat, monkeypatch):
-    """With no wait budget every work-group that meets an unready predecessor
-    recomputes that chunk's bit count (and tail) itself; the stream must be
-    identical."""
+@pytest.mark.parametrize("lat,bps", [(3, 4.0), (2, 4.0), (3, 7.5)])
+def test_many_chunks(hq, orc, lat, bps):
+    """8000 tiles (250 chunks of 32): the chunk scan and the placement of each
+    chunk's staged bits, including every word shared by two chunks; at 7.5 bps
+    a chunk holds more staging words than the placement reads before it knows
+    the chunk's length."""
     from lattice_vq_entropy_amd import workloads as W
-    monkeypatch.setenv("HQ_LOOKBACK_SPINS", "0")
-    x = W.c2("cpu", rows=1000, cols=1024, seed=21).cuda()  # 8000 tiles, 250 chunks
+    x = W.c2("cpu", rows=1000, cols=1024, seed=21).cuda()
     sigma = float(x.float().pow(2).mean().sqrt())
-    full_parity(hq, orc, lat, x, alpha_for(lat, sigma, 4.0), decode=False)
-    full_parity(hq, orc, lat, x, alpha_for(lat, sigma, 4.0), dithered=True, tile_base=99, decode=False)
+    full_parity(hq, orc, lat, x, alpha_for(lat, sigma, bps), decode=False)
+    full_parity(hq, orc, lat, x, alpha_for(lat, sigma, bps), dithered=True, tile_base=99, decode=False)
 
 
 @pytest.mark.parametrize("n_tiles", [1, 31, 32, 33, 97])
