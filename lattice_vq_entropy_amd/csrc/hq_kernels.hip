@@ -414,8 +414,13 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   const uint32_t tid = threadIdx.x, chunk = blockIdx.x;
   const uint32_t* st = a.stage + (uint64_t)chunk * kSlotWords;
   const uint64_t E = a.E[chunk], E1 = a.E[chunk + 1];
-  const uint4 c0 = *reinterpret_cast<const uint4*>(st + 4u * tid);  // words < 1024 < kSlotWords
-  uint32_t p0 = tid ? st[4u * tid - 1u] : 0u;
+  // the first kSpecWords staging words are read before the chunk's length is
+  // known (enough below about 6 bits per scalar); longer chunks read the rest
+  // after it
+  constexpr uint32_t kSpecWords = 768;
+  const bool spec = 4u * tid < kSpecWords;
+  const uint4 c0 = spec ? *reinterpret_cast<const uint4*>(st + 4u * tid) : make_uint4(0u, 0u, 0u, 0u);
+  uint32_t p0 = (spec && tid) ? st[4u * tid - 1u] : 0u;
   if (tid == 0 && chunk > 0) p0 = a.tailw[chunk - 1];
   const uint64_t t = (uint64_t)chunk * kChunkTiles + tid;
   const uint32_t lc = (tid < kChunkTiles && t < a.n_tiles) ? a.loc[t] : 0u;
@@ -433,7 +438,7 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   uint32_t p = p0;
   // staging words i..i+3 with i < nw <= 2962 stay inside the slot
   for (uint32_t i = 4u * tid; i < nw; i += 1024u) {
-    if (i >= 1024u) {
+    if (i >= kSpecWords) {
       c = *reinterpret_cast<const uint4*>(st + i);
       p = st[i - 1];
     }
