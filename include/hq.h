@@ -32,10 +32,11 @@
  *     one encode), 16-byte aligned, zero-filled by the caller once before its
  *     first use.  One workspace must not be used by two calls that can run
  *     concurrently (e.g. on two streams).
- *   - No call waits on another work-group's progress; encode is three
- *     stream-ordered launches (pack per chunk, scan of the chunk bit counts,
- *     placement).  Encode and decode allocate nothing and can be captured in
- *     a HIP graph.
+ *   - No call waits on another work-group's progress; encode is two
+ *     stream-ordered launches (pack per chunk, then placement, which sums the
+ *     bit counts of the chunks before its own) up to 8192 chunks of 32 tiles,
+ *     and three above (a scan of the chunk bit counts between them).  Encode
+ *     and decode allocate nothing and can be captured in a HIP graph.
  *   - Tensors are row-major; every 128 consecutive elements form one tile
  *     (weights: tiles along rows; KV [B, H, S, 128]: one tile per vector).
  *   - Stream layout: record of tile t at bits [offsets[t], offsets[t+1]):

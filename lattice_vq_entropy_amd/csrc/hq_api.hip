@@ -18,7 +18,8 @@ struct hq_plan_s {
   uint64_t seed;
   bool has_alpha;
   float alpha, c_enc, c_dec;
-  uint32_t sgn[4];
+  uint32_t sgn[4];              // bit c: coordinate c of D is -1
+  uint32_t sl16[4], sl32[4];    // the same in the kernels' lane layouts
 };
 
 namespace {
@@ -48,8 +49,27 @@ bool lattice_ok(int lat) { return lat >= HQ_Z && lat <= HQ_E8; }
 
 hq_status dev_err(hipError_t e) { return e == hipSuccess ? HQ_OK : HQ_ERR_DEVICE; }
 
-void fill_common(const hq_plan_s* p, uint32_t sgn[4], uint32_t& k0, uint32_t& k1) {
-  for (int i = 0; i < 4; ++i) sgn[i] = p->sgn[i];
+// The signs of D (bit c of the 128: coordinate c is -1) in the two layouts the
+// kernels read.  The lane holding vector v (coordinates 8v..8v+7) takes word
+// v >> 2, in slot j = v & 3: for bf16 pairs, bit 15 - 4j - i is coordinate
+// 8v + 2i and bit 31 - 4j - i coordinate 8v + 2i + 1 (i < 4); for fp32, bit
+// 31 - 8j - i is coordinate 8v + i (i < 8).  A shift by 4j (8j) and a mask
+// then give the lane its signs at the bit positions its arithmetic uses.
+void sign_layouts(const uint32_t sgn[4], uint32_t sl16[4], uint32_t sl32[4]) {
+  for (int q = 0; q < 4; ++q) sl16[q] = sl32[q] = 0;
+  for (int c = 0; c < 128; ++c) {
+    if (!((sgn[c >> 5] >> (c & 31)) & 1u)) continue;
+    const int v = c >> 3, j = v & 3, i = c & 7;
+    sl32[v >> 2] |= 1u << (31 - 8 * j - i);
+    sl16[v >> 2] |= 1u << (((i & 1) ? 31 : 15) - 4 * j - (i >> 1));
+  }
+}
+
+void fill_common(const hq_plan_s* p, uint32_t sl16[4], uint32_t sl32[4], uint32_t& k0, uint32_t& k1) {
+  for (int q = 0; q < 4; ++q) {
+    sl16[q] = p->sl16[q];
+    sl32[q] = p->sl32[q];
+  }
   k0 = (uint32_t)p->seed;
   k1 = (uint32_t)(p->seed >> 32);
 }
@@ -80,7 +100,7 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   a.cap_words = cap_words;
   a.offsets = offsets;
   a.kout = k;
-  fill_common(plan, a.sgn, a.key0, a.key1);
+  fill_common(plan, a.sl16, a.sl32, a.key0, a.key1);
   a.c_enc = plan->c_enc;
   a.tile_base = tile_base;
   a.ws = (hq::WsHeader*)ws;
@@ -111,7 +131,7 @@ hq_status decode_impl(hq_plan_t plan, const uint32_t* words, uint64_t n_words, c
   a.kin = k;
   a.n_tiles = n_tiles;
   a.y = y;
-  fill_common(plan, a.sgn, a.key0, a.key1);
+  fill_common(plan, a.sl16, a.sl32, a.key0, a.key1);
   a.c_dec = plan->c_dec;
   a.tile_base = tile_base;
   a.ws = (hq::WsHeader*)ws;
@@ -160,6 +180,7 @@ hq_status hq_plan(hq_lattice lattice, int tile, float bps, uint64_t seed, hq_pla
   uint32_t c[4] = {0u, 0u, 0u, kTagSign};
   philox_host(c, (uint32_t)seed, (uint32_t)(seed >> 32));
   for (int i = 0; i < 4; ++i) p->sgn[i] = c[i];
+  sign_layouts(p->sgn, p->sl16, p->sl32);
   *out = p;
   return HQ_OK;
 }
@@ -228,7 +249,7 @@ hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words, 
   a.offsets = offsets;
   a.kin = k;
   a.n_tiles = (uint64_t)n_heads * tiles_per_head;
-  fill_common(plan, a.sgn, a.key0, a.key1);
+  fill_common(plan, a.sl16, a.sl32, a.key0, a.key1);
   a.c_dec = plan->c_dec;
   a.tile_base = tile_base;
   a.ws = (hq::WsHeader*)ws;

@@ -123,6 +123,23 @@ __device__ __forceinline__ float lane_sign_of(uint64_t mask) {
   return c;
 }
 
+// The lane's word of a 4-word lane-layout table (word v >> 2; the lane masks
+// of vector bits 2 and 3 are constants).
+__device__ __forceinline__ uint32_t lane_word4(const uint32_t W[4], int v) {
+  const uint32_t lo = (v & 4) ? W[1] : W[0];
+  const uint32_t hi = (v & 4) ? W[3] : W[2];
+  return (v & 8) ? hi : lo;
+}
+// Signs of D for the lane's 8 coordinates from the host's lane layouts: bf16
+// pairs, bit 15 - i = coordinate 2i and bit 31 - i = coordinate 2i + 1 (so
+// pair i's flips are (sm << i) & 0x80008000); fp32, bit 31 - i = coordinate i.
+__device__ __forceinline__ uint32_t lane_signs16(const uint32_t sl16[4], int v) {
+  return (lane_word4(sl16, v) << (4 * (v & 3))) & 0xF000F000u;
+}
+__device__ __forceinline__ uint32_t lane_signs32(const uint32_t sl32[4], int v) {
+  return (lane_word4(sl32, v) << (8 * (v & 3))) & 0xFF000000u;
+}
+
 struct FwhtSigns {
   float lane_sign;  // (-1)^popcount(v)
 };
@@ -181,6 +198,13 @@ constexpr uint32_t kMagicBits = 0x4B400000u;
 
 __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// a ^ b ^ c in one instruction
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // x - c + [lane in plus] - [lane in minus]: one add with carry-in and one
 // subtract with borrow-in, the lane masks being wave-wide (scalar) values.
 // c is held in a vector register (one scalar operand per instruction).
@@ -188,13 +212,34 @@ __device__ __forceinline__ int32_t add_sub_lane(uint32_t x, uint32_t c, uint64_t
   uint32_t t, r;
   uint64_t co;
   asm("v_addc_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(t), "=s"(co) : "v"(x), "s"(plus));
-  asm("v_subb_co_u32_e64 %0, %1, %2, %3, %4" : "=v"(r), "=s"(co) : "v"(t), "v"(c), "s"(minus));
+  if (__builtin_constant_p(c) && c == 0u)
+    asm("v_subb_co_u32_e64 %0, %1, %2, 0, %3" : "=v"(r), "=s"(co) : "v"(t), "s"(minus));
+  else
+    asm("v_subb_co_u32_e64 %0, %1, %2, %3, %4" : "=v"(r), "=s"(co) : "v"(t), "v"(c), "s"(minus));
   return (int32_t)r;
 }
 
 __device__ __forceinline__ uint32_t zigzag(int32_t v) {
   return ((uint32_t)v << 1) ^ (uint32_t)(v >> 31);
 }
+
+// The encoder keeps every symbol m as w = 2 m + 1; for m = zigzag(y) that is
+// |4y + 1|.  From y held with an even bias, yb = y + B (|4y + 1| < 2^24 and
+// 4B + 2^24 < 2^32 taken mod 2^32), it is one shift-or and one absolute
+// difference against fourB = 4B mod 2^32.
+__device__ __forceinline__ uint32_t zz1_biased(uint32_t yb, uint32_t fourB) {
+  const uint32_t t = (yb << 2) | 1u;
+  uint32_t r;
+  asm("v_sad_u32 %0, %1, %2, 0" : "=v"(r) : "v"(t), "s"(fourB));
+  return r;
+}
+// the same from an unbiased y
+__device__ __forceinline__ uint32_t zz1(int32_t y) {
+  const int32_t t = (int32_t)(((uint32_t)y << 2) | 1u);
+  return (uint32_t)max(t, -t);
+}
+constexpr uint32_t kFourMagic = 4u * kMagicBits;  // mod 2^32
+constexpr uint32_t kTwoMagic = 2u * kMagicBits;
 __device__ __forceinline__ int32_t unzigzag(uint32_t m) {
   return (int32_t)(m >> 1) ^ -(int32_t)(m & 1u);
 }
@@ -204,7 +249,9 @@ __device__ __forceinline__ int32_t unzigzag(uint32_t m) {
 // The decisions are wave-wide lane masks (ballots), combined with scalar
 // logic, and applied as carry/borrow.  Every lane of the wave (or of the
 // active set) must call it.
-__device__ __forceinline__ void d4_core(const float u[4], int32_t x[4]) {
+// x is returned as rint bits - cm: cm = kMagicBits gives the integers, cm = 0
+// the integers biased by kMagicBits.
+__device__ __forceinline__ void d4_core(const float u[4], int32_t x[4], uint32_t cm) {
   float e[4];
   uint32_t rb[4];
 #pragma unroll
@@ -216,7 +263,6 @@ __device__ __forceinline__ void d4_core(const float u[4], int32_t x[4]) {
   const uint64_t ODD = __ballot(((rb[0] ^ rb[1] ^ rb[2] ^ rb[3]) & 1u) != 0);
   const float emax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(e[0]), __builtin_fabsf(e[1])),
                                      __builtin_fmaxf(__builtin_fabsf(e[2]), __builtin_fabsf(e[3])));
-  const uint32_t cm = kMagicBits;
   uint64_t seen = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -257,7 +303,8 @@ __device__ __forceinline__ void np_a2_codes(float u0, float u1, int32_t& i, int3
 // first argmin of |d|, upward iff d < 0 or d = 1 (d = 1 at the argmin means
 // every |d_i| = 1, i.e. min |d| = 1).  Every adjustment of ye is -1, 0 or +1:
 // a borrow and a carry on the integer.
-__device__ __forceinline__ void e8_core(const float u[8], int32_t y[8], bool& odd) {
+// (y is returned as in d4_core: cm = kMagicBits unbiased, cm = 0 biased.)
+__device__ __forceinline__ void e8_core(const float u[8], int32_t y[8], bool& odd, uint32_t cm) {
   float d[8];
   uint32_t rb[8];
 #pragma unroll
@@ -281,7 +328,7 @@ __device__ __forceinline__ void e8_core(const float u[8], int32_t y[8], bool& od
     NEG[i] = __ballot(d[i] < 0.0f);
     PN ^= NEG[i];  // parity of the number of negative d
   }
-  const uint32_t xr = rb[0] ^ rb[1] ^ rb[2] ^ rb[3] ^ rb[4] ^ rb[5] ^ rb[6] ^ rb[7];
+  const uint32_t xr = xor3(xor3(rb[0], rb[1], rb[2]), xor3(rb[3], rb[4], rb[5]), rb[6] ^ rb[7]);
   const uint64_t PE = __ballot((xr & 1u) != 0);
   const uint64_t PO = PE ^ PN;
   const bool pe = __builtin_amdgcn_inverse_ballot_w64(PE);
@@ -297,7 +344,6 @@ __device__ __forceinline__ void e8_core(const float u[8], int32_t y[8], bool& od
   const uint64_t EVEN = __ballot(even);
   const uint64_t FIX = (EVEN & PE) | (~EVEN & PO);
   const uint64_t ODDUP = ~EVEN & __ballot(amin == 1.0f);
-  const uint32_t cm = kMagicBits;
   uint64_t seen = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -342,40 +388,42 @@ template <> __device__ __forceinline__ void unstrip_embed<3>(const int32_t* sym,
 }
 
 // Quantise the lane's 8 values [HQ Methodology 2] and strip them
-// [Methodology 3]: zigzag symbols, and for E8 the coset bit.  Symbols: Z x;
-// A2 (i - (j & 1)) >> 1 and j; D4 x0, x1, x2, (x3 - parity(x0+x1+x2)) >> 1;
-// E8 the halves y_0..y_6 and y_7 >> 1 (the sum of the halves is even).
+// [Methodology 3]: the symbols as w = 2 zigzag(sym) + 1, and for E8 the coset
+// bit.  Symbols: Z x; A2 (i - (j & 1)) >> 1 and j; D4 x0, x1, x2,
+// (x3 - parity(x0+x1+x2)) >> 1; E8 the halves y_0..y_6 and y_7 >> 1 (the sum
+// of the halves is even).  Z, D4 and E8 work on integers biased by kMagicBits
+// (even, so parities and halvings carry over).
 template <int L>
-__device__ __forceinline__ void quantize_syms(const float u[8], uint32_t m[8], bool& odd) {
+__device__ __forceinline__ void quantize_syms(const float u[8], uint32_t w[8], bool& odd) {
   odd = false;
   if constexpr (L == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = zigzag((int32_t)(fbits(u[i] + kMagic) - kMagicBits));
+    for (int i = 0; i < 8; ++i) w[i] = zz1_biased(fbits(u[i] + kMagic), kFourMagic);
   } else if constexpr (L == 1) {
 #pragma unroll
     for (int h = 0; h < 8; h += 2) {
       int32_t i, j;
       np_a2_codes(u[h], u[h + 1], i, j);
-      m[h] = zigzag((i - (j & 1)) >> 1);
-      m[h + 1] = zigzag(j);
+      w[h] = zz1((i - (j & 1)) >> 1);
+      w[h + 1] = zz1(j);
     }
   } else if constexpr (L == 2) {
 #pragma unroll
     for (int h = 0; h < 8; h += 4) {
       int32_t x[4];
-      d4_core(&u[h], x);
-      const int32_t p = (x[0] ^ x[1] ^ x[2]) & 1;
-      m[h] = zigzag(x[0]);
-      m[h + 1] = zigzag(x[1]);
-      m[h + 2] = zigzag(x[2]);
-      m[h + 3] = zigzag((x[3] - p) >> 1);
+      d4_core(&u[h], x, 0u);
+      const uint32_t p = ((uint32_t)x[0] ^ (uint32_t)x[1] ^ (uint32_t)x[2]) & 1u;
+      w[h] = zz1_biased((uint32_t)x[0], kFourMagic);
+      w[h + 1] = zz1_biased((uint32_t)x[1], kFourMagic);
+      w[h + 2] = zz1_biased((uint32_t)x[2], kFourMagic);
+      w[h + 3] = zz1_biased(((uint32_t)x[3] - p) >> 1, kTwoMagic);
     }
   } else {
     int32_t y[8];
-    e8_core(u, y, odd);
+    e8_core(u, y, odd, 0u);
 #pragma unroll
-    for (int i = 0; i < 7; ++i) m[i] = zigzag(y[i]);
-    m[7] = zigzag(y[7] >> 1);
+    for (int i = 0; i < 7; ++i) w[i] = zz1_biased((uint32_t)y[i], kFourMagic);
+    w[7] = zz1_biased((uint32_t)y[7] >> 1, kTwoMagic);
   }
 }
 
@@ -410,8 +458,8 @@ __device__ __forceinline__ void dither_lane(uint32_t k0, uint32_t k1, uint64_t t
 #pragma unroll
     for (int i = 0; i < 8; ++i) tau[i] = 2.0f * f[i];
     int32_t x[8];
-    d4_core(&tau[0], &x[0]);
-    d4_core(&tau[4], &x[4]);
+    d4_core(&tau[0], &x[0], kMagicBits);
+    d4_core(&tau[4], &x[4], kMagicBits);
 #pragma unroll
     for (int i = 0; i < 8; ++i) d[i] = tau[i] - (float)x[i];
   } else {
@@ -419,7 +467,7 @@ __device__ __forceinline__ void dither_lane(uint32_t k0, uint32_t k1, uint64_t t
     for (int i = 0; i < 8; ++i) tau[i] = 4.0f * f[i];
     int32_t y[8];
     bool odd;
-    e8_core(tau, y, odd);
+    e8_core(tau, y, odd, kMagicBits);
 #pragma unroll
     for (int i = 0; i < 8; ++i) d[i] = tau[i] - (float)(2 * y[i] + (odd ? 1 : 0));
   }

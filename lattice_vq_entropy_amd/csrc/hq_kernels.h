@@ -16,7 +16,9 @@ struct EncArgs {
   uint64_t cap_words;
   uint64_t* offsets;
   uint8_t* kout;
-  uint32_t sgn[4];  // bit i of the 128: coordinate i of D is -1
+  // signs of D in the two lane layouts (sign_layouts on the host): for bf16
+  // pairs and for fp32 values
+  uint32_t sl16[4], sl32[4];
   float c_enc;
   uint32_t key0, key1;
   uint64_t tile_base;
@@ -32,6 +34,8 @@ struct EncArgs {
 
 struct PlaceArgs {
   const uint32_t* stage;
+  const uint32_t* agg;  // bits per chunk (padded to 64 entries)
+  WsHeader* ws;
   const uint64_t* E;
   const uint32_t* loc;
   const uint32_t* tailw;
@@ -49,7 +53,7 @@ struct DecArgs {
   const uint8_t* kin;
   uint64_t n_tiles;
   void* y;
-  uint32_t sgn[4];
+  uint32_t sl16[4], sl32[4];  // as in EncArgs
   float c_dec;
   uint32_t key0, key1;
   uint64_t tile_base;

@@ -69,10 +69,6 @@ __device__ __forceinline__ void lds_or64(uint32_t* s, uint32_t P, uint64_t val) 
   if (x2) atomicOr(&s[w + 2], x2);
 }
 
-__device__ __forceinline__ uint32_t rev4(uint32_t n) {
-  return ((n & 1u) << 3) | ((n & 2u) << 1) | ((n & 4u) >> 1) | ((n & 8u) >> 3);
-}
-
 // ===========================================================================
 // Encode
 // ===========================================================================
@@ -82,22 +78,11 @@ template <bool BF16>
 struct LaneConst {
   FwhtSigns fs;
   float scale;
-  // signs of D for the lane's 8 coordinates: bf16, bit 15 - i = coordinate
-  // 2i and bit 31 - i = coordinate 2i + 1 (so pair i's flips are
-  // (sm << i) & 0x80008000); fp32, bit 31 - i = coordinate i
-  uint32_t sm;
-  __device__ __forceinline__ LaneConst(const uint32_t sgn[4], int v, float c) {
+  uint32_t sm;  // lane_signs16 (bf16) or lane_signs32 (fp32)
+  __device__ __forceinline__ LaneConst(const EncArgs& a, int v) {
     fs = fwht_signs(v);
-    scale = fs.lane_sign * c;
-    const uint32_t sbyte = (sgn[v >> 2] >> ((v & 3) * 8)) & 0xFFu;
-    sm = 0;
-    if constexpr (BF16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm |= (((sbyte >> (2 * i)) & 1u) << (15 - i)) | (((sbyte >> (2 * i + 1)) & 1u) << (31 - i));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm |= ((sbyte >> i) & 1u) << (31 - i);
-    }
+    scale = fs.lane_sign * a.c_enc;
+    sm = BF16 ? lane_signs16(a.sl16, v) : lane_signs32(a.sl32, v);
   }
   // the lane's 8 coordinates with the signs of D applied, as fp32
   __device__ __forceinline__ void apply(const InVec<BF16>& in, float xv[8]) const {
@@ -120,7 +105,7 @@ struct LaneConst {
 // One tile's symbols as seen by one lane, and the tile's Rice parameter and
 // record length.
 struct TileSyms {
-  uint32_t m[8];  // zigzag symbols of the lane's coordinates
+  uint32_t w[8];  // 2 m + 1 for the zigzag symbols m of the lane's coordinates
   uint32_t k;     // Rice parameter of the tile
   uint32_t L;     // record length of the tile (bits); 0 for a tile past the end
   uint32_t U;     // unary bits of the lane's 8 symbols
@@ -148,7 +133,7 @@ __device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF1
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) bad |= !(__builtin_fabsf(u[i]) < kRangeLimit);
-  quantize_syms<L>(u, ts.m, ts.odd);
+  quantize_syms<L>(u, ts.w, ts.odd);
   const uint64_t bad_mask = __ballot(bad);
   if (bad_mask) {
     // a tile with a non-finite input or a coordinate beyond the range: record
@@ -160,7 +145,7 @@ __device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF1
     if (tile_bad) {
       if (r == 0 && valid) set_status(a.ws, tile_nf ? 2 : 3);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ts.m[i] = 0u;
+      for (int i = 0; i < 8; ++i) ts.w[i] = 1u;  // m = 0
       ts.odd = false;
     }
   }
@@ -168,16 +153,19 @@ __device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF1
   // minimises the tile length.  From M = sum m: S(k) <= 128 once
   // M <= 2^(k+7) (at kA) and S(k) > 128 while M >= 3*2^(k+7), so the answer
   // is one of kA-2, kA-1, kA; S(k) = A_k - A_(k+1) with A_j = sum m >> j.
-  const uint32_t M = row_sum_u32(((ts.m[0] + ts.m[1]) + (ts.m[2] + ts.m[3])) + ((ts.m[4] + ts.m[5]) + (ts.m[6] + ts.m[7])));
-  const uint32_t kA = M <= 128u ? 0u : (32u - (uint32_t)__builtin_clz(M - 1u)) - 7u;
-  const uint32_t c = kA >= 2u ? kA - 2u : 0u;
+  // With w = 2m + 1: the row sum of w is 2M + 128, and m >> j = w >> (j + 1).
+  const uint32_t S2 = row_sum_u32(((ts.w[0] + ts.w[1]) + (ts.w[2] + ts.w[3])) + ((ts.w[4] + ts.w[5]) + (ts.w[6] + ts.w[7])));
+  // M > 128 iff 2M + 128 > 384; then ceil(log2 M) = 32 - clz(M - 1) = 31 - clz(2M - 2)
+  const uint32_t kA = S2 <= 384u ? 0u : 24u - (uint32_t)__builtin_clz(S2 - 130u);
+  const uint32_t c1 = (kA >= 2u ? kA - 2u : 0u) + 1u;
   uint32_t a0 = 0, a1 = 0, a2 = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    a0 += ts.m[i] >> c;
-    a1 += ts.m[i] >> (c + 1u);
-    a2 += ts.m[i] >> (c + 2u);
+    a0 += ts.w[i] >> c1;
+    a1 += ts.w[i] >> (c1 + 1u);
+    a2 += ts.w[i] >> (c1 + 2u);
   }
+  const uint32_t c = c1 - 1u;
   const uint32_t tot = row_sum_u32(a0 | (a1 << 10) | (a2 << 20));  // A_c <= 512
   const uint32_t A0 = tot & 1023u, A1 = (tot >> 10) & 1023u, A2 = tot >> 20;
   uint32_t Ak, ak;
@@ -189,51 +177,56 @@ __device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF1
 }
 
 // Assemble one tile's record at local bit tb of the zero-filled LDS stream s.  Every lane of the wave calls it (ballot,
-// shuffles); only lanes of valid tiles write.
+// permutes); only lanes of valid tiles write.  vaddr: byte address, for a lane permute, of the lane in the same row
+// that holds vector r.
 template <int L>
-__device__ __forceinline__ void tile_pack(uint32_t* s, uint32_t tb, const TileSyms& ts, int v, int r, int lane,
+__device__ __forceinline__ void tile_pack(uint32_t* s, uint32_t tb, const TileSyms& ts, int v, int r, int vaddr,
                                           int grp, bool valid) {
   constexpr uint32_t RAW = Lat<L>::raw;
-  const uint32_t k = ts.k;
+  const uint32_t k = ts.k, k1 = k + 1u;  // m >> j = w >> (j + 1); the low k bits of m are bits 1..k of w
   if constexpr (RAW > 0) {
-    const uint64_t bm = __ballot(ts.odd);
-    const uint32_t g16 = (uint32_t)(bm >> (grp * 16)) & 0xFFFFu;
-    // bit v of the field is the coset bit of vector v, held by lane v(r)
-    const uint32_t raw16 = (g16 & 0x0F0Fu) | (rev4((g16 >> 4) & 0xFu) << 4) | (rev4((g16 >> 12) & 0xFu) << 12);
+    // bit v of a tile's field is the coset bit of vector v, held by lane v(r):
+    // lanes 4..7 and 12..15 of each row hold their vectors in reverse order,
+    // so the bits of every high nibble are reversed (scalar work on the ballot)
+    uint64_t bm = __ballot(ts.odd);
+    uint64_t hi = bm & 0xF0F0F0F0F0F0F0F0ull;
+    hi = ((hi >> 1) & 0x5555555555555555ull) | ((hi & 0x5555555555555555ull) << 1);
+    hi = ((hi >> 2) & 0x3333333333333333ull) | ((hi & 0x3333333333333333ull) << 2);
+    bm = (bm & 0x0F0F0F0F0F0F0F0Full) | hi;
+    const uint32_t raw16 = (uint32_t)(bm >> (grp * 16)) & 0xFFFFu;
     if (valid && r == 0) lds_or64(s, tb, raw16);
   }
   // exclusive scan of the unary lengths in vector order
-  const int src = (lane & ~15) | lane_vector(r);
-  const uint32_t Uv = (uint32_t)__shfl((int)ts.U, src);
+  const uint32_t Uv = (uint32_t)__builtin_amdgcn_ds_bpermute(vaddr, (int)ts.U);
   const uint32_t incl = row_scan_u32(Uv);
-  const uint32_t excl = (uint32_t)__shfl((int)(incl - Uv), src);
+  const uint32_t excl = (uint32_t)__builtin_amdgcn_ds_bpermute(vaddr, (int)(incl - Uv));
   if (!valid) return;
   if (k != 0) {
-    const uint32_t rpos = tb + RAW + 8u * (uint32_t)v * k;
+    const uint32_t rpos = tb + RAW + __umul24(8u * (uint32_t)v, k);
     if (k <= 8) {
-      uint32_t lo = __builtin_amdgcn_ubfe(ts.m[0], 0, k), hi = __builtin_amdgcn_ubfe(ts.m[4], 0, k);
+      uint32_t lo = __builtin_amdgcn_ubfe(ts.w[0], 1, k), hi = __builtin_amdgcn_ubfe(ts.w[4], 1, k);
 #pragma unroll
       for (int j = 1; j < 4; ++j) {
-        lo |= __builtin_amdgcn_ubfe(ts.m[j], 0, k) << (j * k);
-        hi |= __builtin_amdgcn_ubfe(ts.m[4 + j], 0, k) << (j * k);
+        lo |= __builtin_amdgcn_ubfe(ts.w[j], 1, k) << (j * k);
+        hi |= __builtin_amdgcn_ubfe(ts.w[4 + j], 1, k) << (j * k);
       }
       lds_or64(s, rpos, (uint64_t)lo | ((uint64_t)hi << (4 * k)));
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) lds_or64(s, rpos + j * k, __builtin_amdgcn_ubfe(ts.m[j], 0, k));
+      for (int j = 0; j < 8; ++j) lds_or64(s, rpos + j * k, __builtin_amdgcn_ubfe(ts.w[j], 1, k));
     }
   }
   const uint32_t upos = tb + RAW + 128u * k + excl;
   if (ts.U <= 64u) {
     // built from the last code back: V_j = ((V_(j+1) << 1) | 1) << q_j
-    uint64_t msk = 1ull << (ts.m[7] >> k);
+    uint64_t msk = 1ull << (ts.w[7] >> k1);
 #pragma unroll
-    for (int j = 6; j >= 0; --j) msk = ((msk << 1) | 1ull) << (ts.m[j] >> k);
+    for (int j = 6; j >= 0; --j) msk = ((msk << 1) | 1ull) << (ts.w[j] >> k1);
     lds_or64(s, upos, msk);
   } else {
     uint32_t pos = upos;
     for (int j = 0; j < 8; ++j) {
-      pos += ts.m[j] >> k;
+      pos += ts.w[j] >> k1;
       atomicOr(&s[pos >> 5], 1u << (pos & 31));
       pos += 1;
     }
@@ -253,14 +246,14 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
 // bit count to agg, and per tile the chunk-local bit offset and k.  No
 // work-group waits on another.  LEN_ONLY: the chunk's bit count only.
 template <int L, bool DITHER, bool BF16, bool LEN_ONLY>
-__global__ __launch_bounds__(256) void encode_k(EncArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 8 : 1))) void encode_k(EncArgs a) {
   __shared__ __align__(16) uint32_t s_stage[kSlotWords];
   __shared__ uint32_t s_len[kChunkTiles], s_lo[kChunkTiles], s_k[kChunkTiles];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
   const int v = lane_vector(r);
   const int pslot = wv * 4 + grp;
-  const LaneConst<BF16> lc(a.sgn, v, a.c_enc);
+  const LaneConst<BF16> lc(a, v);
   const uint32_t chunk = blockIdx.x;
   const uint64_t t_first = (uint64_t)chunk * kChunkTiles;
 
@@ -287,6 +280,8 @@ __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
     }
   } else {
     for (int i = tid; i < kSlotWords / 4; i += 256) reinterpret_cast<uint4*>(s_stage)[i] = make_uint4(0u, 0u, 0u, 0u);
+    // lane permute addresses: the row's lane of slot pslot, and of vector r
+    const int paddr = ((lane & ~15) | pslot) << 2, vaddr = ((lane & ~15) | v) << 2;
     uint32_t base = 0;  // wave-uniform bit offset of the current pass
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
@@ -303,10 +298,10 @@ __global__ __launch_bounds__(256) void encode_k(EncArgs a) {
       // offsets within the pass: every row scans the pass's 16 lengths
       const uint32_t len = s_len[p * 16 + r];
       const uint32_t incl = row_scan_u32(len);
-      const uint32_t tb = base + (uint32_t)__shfl((int)(incl - len), (lane & ~15) | pslot);
+      const uint32_t tb = base + (uint32_t)__builtin_amdgcn_ds_bpermute(paddr, (int)(incl - len));
       if (r == 0) s_lo[slot] = tb;
       base += __builtin_amdgcn_readlane(incl, 15);
-      tile_pack<L>(s_stage, tb, ts, v, r, lane, grp, valid);
+      tile_pack<L>(s_stage, tb, ts, v, r, vaddr, grp, valid);
     }
     const uint32_t A = base;  // >= 256: every chunk holds a tile
     __syncthreads();
@@ -362,17 +357,31 @@ __global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, 
     sum += (uint64_t)(i < n ? q[j].x : 0u) + (i + 1 < n ? q[j].y : 0u) + (i + 2 < n ? q[j].z : 0u) +
            (i + 3 < n ? q[j].w : 0u);
   }
-  // inclusive scan over the wave, then over the 16 wave totals
-  uint64_t x = sum;
+  // inclusive scan over the wave: 32-bit row scans joined over the rows while
+  // a wave's total stays below 2^32 (4 * per counts of at most 32 * 2960 bits
+  // on each of 64 lanes), else 64-bit shuffles
+  uint64_t x;
+  if (per <= 128u) {
+    uint32_t y = row_scan_u32((uint32_t)sum);
+    const uint32_t t0 = __builtin_amdgcn_readlane(y, 15), t1 = __builtin_amdgcn_readlane(y, 31),
+                   t2 = __builtin_amdgcn_readlane(y, 47);
+    const uint32_t row = lane >> 4;
+    y += (row > 0u ? t0 : 0u) + (row > 1u ? t1 : 0u) + (row > 2u ? t2 : 0u);
+    x = y;
+  } else {
+    x = sum;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint64_t y = __shfl_up(x, o);
-    if ((int)lane >= o) x += y;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t y = __shfl_up(x, o);
+      if ((int)lane >= o) x += y;
+    }
   }
   if (lane == 63) s_w[wv] = x;
   __syncthreads();
+  // plus the totals of the earlier waves (independent LDS reads)
   uint64_t run = x - sum;
-  for (uint32_t w = 0; w < wv; ++w) run += s_w[w];
+#pragma unroll
+  for (uint32_t w = 0; w < 15; ++w) run += w < wv ? s_w[w] : 0ull;
   // writes four offsets from the counts t at i (i a multiple of 4, E + i
   // 16-byte aligned) and advances run
   auto put4 = [&](uint32_t i, const uint4& t) {
@@ -409,11 +418,29 @@ __global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, 
 // (one uint4 staging load, issued with the offset loads before they arrive);
 // the word shared with the predecessor takes the predecessor's last 32 bits,
 // recorded by step 1, so every stream word is written exactly once.  Also the
-// per-tile offsets.
+// per-tile offsets.  SELF_SCAN (inputs of at most kSelfScanChunks chunks):
+// step 2 is skipped and every work-group sums the bit counts of the chunks
+// before its own (all reads of one small array that the L2 serves), which
+// costs less than a launch of the scan.
+constexpr uint32_t kSelfScanChunks = 8192;
+template <bool SELF_SCAN>
 __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   const uint32_t tid = threadIdx.x, chunk = blockIdx.x;
   const uint32_t* st = a.stage + (uint64_t)chunk * kSlotWords;
-  const uint64_t E = a.E[chunk], E1 = a.E[chunk + 1];
+  // SELF_SCAN: the counts [0, chunk) as uint4 (the count array is padded to 64
+  // entries), loaded first so that summing them waits for these loads only;
+  // only the rounds of 1024 that hold counts below chunk are loaded, and lanes
+  // past chunk in the last one read entry 0
+  constexpr uint32_t kR = SELF_SCAN ? kSelfScanChunks / 1024 : 1;
+  uint4 g[kR];
+  if constexpr (SELF_SCAN) {
+#pragma unroll
+    for (uint32_t j = 0; j < kR; ++j) {
+      const uint32_t i = 4u * tid + 1024u * j;
+      g[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (1024u * j < chunk) g[j] = *reinterpret_cast<const uint4*>(a.agg + (i < chunk ? i : 0u));  // uniform test
+    }
+  }
   // the first kSpecWords staging words are read before the chunk's length is
   // known (enough below about 6 bits per scalar); longer chunks read the rest
   // after it
@@ -421,7 +448,31 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   const bool spec = 4u * tid < kSpecWords;
   const uint4 c0 = spec ? *reinterpret_cast<const uint4*>(st + 4u * tid) : make_uint4(0u, 0u, 0u, 0u);
   uint32_t p0 = (spec && tid) ? st[4u * tid - 1u] : 0u;
-  if (tid == 0 && chunk > 0) p0 = a.tailw[chunk - 1];
+  const uint32_t tw = chunk > 0 ? a.tailw[chunk - 1] : 0u;  // work-group uniform
+  if (tid == 0) p0 = tw;
+  uint64_t E, E1;
+  if constexpr (SELF_SCAN) {
+    __shared__ uint32_t s_part[4];
+    const uint32_t A = a.agg[chunk];
+    uint32_t part = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kR; ++j) {
+      const uint32_t i = 4u * tid + 1024u * j;
+      part += (i < chunk ? g[j].x : 0u) + (i + 1 < chunk ? g[j].y : 0u) + (i + 2 < chunk ? g[j].z : 0u) +
+              (i + 3 < chunk ? g[j].w : 0u);
+    }
+    // (the wave total is formed by every lane: a lane-0-only branch would
+    // leave the other rows' sums unfinished when read across lanes)
+    const uint32_t wsum = wave_sum_u32(part);
+    if ((tid & 63) == 0) s_part[tid >> 6] = wsum;
+    __syncthreads();
+    E = (uint64_t)s_part[0] + s_part[1] + s_part[2] + s_part[3];  // at most 8192 * 94720 bits
+    E1 = E + A;
+    if (tid == 0 && chunk == a.n_chunks - 1 && (E1 + 31) / 32 > a.cap_words) atomicOr(&a.ws->status, 1u << 4);
+  } else {
+    E = a.E[chunk];
+    E1 = a.E[chunk + 1];
+  }
   const uint64_t t = (uint64_t)chunk * kChunkTiles + tid;
   const uint32_t lc = (tid < kChunkTiles && t < a.n_tiles) ? a.loc[t] : 0u;
   if (tid < kChunkTiles && t < a.n_tiles) {
@@ -664,7 +715,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uin
 }
 
 template <int L, bool DITHER, int OUT>
-__global__ __launch_bounds__(256) void decode_k(DecArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOutScores ? 1 : 8))) void decode_k(DecArgs a) {
   constexpr uint32_t RAW = Lat<L>::raw;
   constexpr uint32_t MAXREC = RAW + 128u * 23u;
   __shared__ __align__(16) uint32_t s_stage[kStageWords];
@@ -677,7 +728,6 @@ __global__ __launch_bounds__(256) void decode_k(DecArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
   const int v = lane_vector(r);
   const FwhtSigns fs = fwht_signs(v);
-  const uint32_t sbyte = (a.sgn[v >> 2] >> ((v & 3) * 8)) & 0xFFu;
 
   uint64_t t_first, t_limit, head = 0;
   if constexpr (OUT == kOutScores) {
@@ -697,9 +747,10 @@ __global__ __launch_bounds__(256) void decode_k(DecArgs a) {
     const int g = wv * 4 + grp;
     if (g < (int)a.qph) {
       const float* qp = a.q + ((head * a.qph + g) * kTile + 8 * v);
+      const uint32_t sm = lane_signs32(a.sl32, v);
       float xq[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xq[i] = ((sbyte >> i) & 1u) ? -qp[i] : qp[i];
+      for (int i = 0; i < 8; ++i) xq[i] = __builtin_bit_cast(float, fbits(qp[i]) ^ ((sm << i) & 0x80000000u));
       fwht_tile(xq, fs);
 #pragma unroll
       for (int i = 0; i < 8; ++i) s_q[g][8 * v + i] = xq[i] * fs.lane_sign;
@@ -747,9 +798,14 @@ __global__ __launch_bounds__(256) void decode_k(DecArgs a) {
   }
   __syncthreads();
 
+  // output scale: the lane sign and c_dec, then the signs of D (bf16: on the
+  // packed pairs after rounding, which is symmetric in the sign; fp32: folded
+  // into eight per-coordinate scales)
+  const float cs = fs.lane_sign * a.c_dec;
+  const uint32_t sm = OUT == kOutBf16 ? lane_signs16(a.sl16, v) : lane_signs32(a.sl32, v);
   float sc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) sc[i] = (((sbyte >> i) & 1u) ? -fs.lane_sign : fs.lane_sign) * a.c_dec;
+  for (int i = 0; i < 8; ++i) sc[i] = OUT == kOutF32 ? __builtin_bit_cast(float, fbits(cs) ^ ((sm << i) & 0x80000000u)) : cs;
 
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
@@ -803,7 +859,7 @@ __global__ __launch_bounds__(256) void decode_k(DecArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const f32x2_t f = {o[2 * i], o[2 * i + 1]};
-            pk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+            pk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t)) ^ ((sm << i) & 0x80008000u);
           }
           *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.y) + t * kTile + 8 * v) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         } else {
@@ -861,8 +917,12 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
     return hipGetLastError();
   }
   hipLaunchKernelGGL((encode_k<L, DITHER, BF16, false>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(scan_k, dim3(1), dim3(1024), 0, st, (const uint32_t*)a.agg, a.n_chunks, a.E, a.cap_words, a.ws);
+  const bool self_scan = a.n_chunks <= kSelfScanChunks;
+  if (!self_scan)
+    hipLaunchKernelGGL(scan_k, dim3(1), dim3(1024), 0, st, (const uint32_t*)a.agg, a.n_chunks, a.E, a.cap_words, a.ws);
   PlaceArgs pa;
+  pa.agg = a.agg;
+  pa.ws = a.ws;
   pa.stage = a.stage;
   pa.E = a.E;
   pa.loc = a.loc;
@@ -872,7 +932,10 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   pa.words = a.words;
   pa.cap_words = a.cap_words;
   pa.offsets = a.offsets;
-  hipLaunchKernelGGL(place_k, grid, dim3(256), 0, st, pa);
+  if (self_scan)
+    hipLaunchKernelGGL(place_k<true>, grid, dim3(256), 0, st, pa);
+  else
+    hipLaunchKernelGGL(place_k<false>, grid, dim3(256), 0, st, pa);
   return hipGetLastError();
 }
 

@@ -131,6 +131,37 @@ def test_many_chunks(hq, orc, lat, bps):
     full_parity(hq, orc, lat, x, alpha_for(lat, sigma, bps), dithered=True, tile_base=99, decode=False)
 
 
+def test_offset_paths_at_the_boundary(hq, orc):
+    """Up to 8192 chunks of 32 tiles the placement sums the chunk bit counts
+    itself; above that a separate scan computes the chunk offsets.  8193
+    chunks take the scan and 8192 (the same tiles less the last chunk) the
+    summing placement: both streams equal the oracle's, and a capacity one
+    word short is reported on the scan path too."""
+    g = torch.Generator().manual_seed(8193)
+    n_big = 8193 * 32
+    x = (torch.randn(n_big, 128, generator=g) * 0.05).to(torch.bfloat16)
+    alpha = alpha_for(3, 0.05, 4.0)
+    st, ow, oo, ok = orc.encode(3, SEED, alpha, host_input(x))
+    assert st == 0
+    xg = x.cuda()
+    plan = hq.Plan(3, 4.0, SEED).set_alpha(alpha)
+    ws = plan.workspace(n_big)
+    for n in (n_big, n_big - 32):
+        enc = hq.encode(plan, xg[:n], ws)
+        assert hq.status_sync(ws) == hq.OK
+        words, offsets, k = gpu_stream(enc)
+        total = int(oo[n])
+        assert np.array_equal(offsets, oo[: n + 1]), f"offsets differ ({n} tiles)"
+        assert np.array_equal(k, ok[:n]), f"Rice parameters differ ({n} tiles)"
+        full = total >> 5
+        assert np.array_equal(words[:full], ow[:full]), f"words differ ({n} tiles)"
+        if total & 31:
+            assert int(words[full]) == int(ow[full]) & ((1 << (total & 31)) - 1)
+    need = (int(oo[n_big]) + 31) // 32
+    hq.encode(plan, xg, ws, cap_words=need - 1)
+    assert hq.status_sync(ws) == hq.ERR_CAPACITY
+
+
 @pytest.mark.parametrize("n_tiles", [1, 31, 32, 33, 97])
 def test_small_and_ragged_sizes(hq, orc, n_tiles):
     g = torch.Generator().manual_seed(n_tiles)
