@@ -454,12 +454,19 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   if constexpr (SELF_SCAN) {
     __shared__ uint32_t s_part[4];
     const uint32_t A = a.agg[chunk];
+    // rounds wholly below chunk add all four counts; only the round holding
+    // chunk masks (the tests are work-group uniform, so no VALU is spent on
+    // rounds that were not loaded)
     uint32_t part = 0;
 #pragma unroll
     for (uint32_t j = 0; j < kR; ++j) {
-      const uint32_t i = 4u * tid + 1024u * j;
-      part += (i < chunk ? g[j].x : 0u) + (i + 1 < chunk ? g[j].y : 0u) + (i + 2 < chunk ? g[j].z : 0u) +
-              (i + 3 < chunk ? g[j].w : 0u);
+      if (1024u * (j + 1) <= chunk) {
+        part += g[j].x + g[j].y + g[j].z + g[j].w;
+      } else if (1024u * j < chunk) {
+        const uint32_t i = 4u * tid + 1024u * j;
+        part += (i < chunk ? g[j].x : 0u) + (i + 1 < chunk ? g[j].y : 0u) + (i + 2 < chunk ? g[j].z : 0u) +
+                (i + 3 < chunk ? g[j].w : 0u);
+      }
     }
     // (the wave total is formed by every lane: a lane-0-only branch would
     // leave the other rows' sums unfinished when read across lanes)
