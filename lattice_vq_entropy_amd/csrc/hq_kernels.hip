@@ -435,10 +435,11 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   uint4 g[kR];
   if constexpr (SELF_SCAN) {
 #pragma unroll
-    for (uint32_t j = 0; j < kR; ++j) {
+    for (uint32_t j = 0; j < kR; ++j) {  // (the round tests are work-group uniform)
       const uint32_t i = 4u * tid + 1024u * j;
       g[j] = make_uint4(0u, 0u, 0u, 0u);
-      if (1024u * j < chunk) g[j] = *reinterpret_cast<const uint4*>(a.agg + (i < chunk ? i : 0u));  // uniform test
+      if (1024u * (j + 1) <= chunk) g[j] = *reinterpret_cast<const uint4*>(a.agg + i);
+      else if (1024u * j < chunk) g[j] = *reinterpret_cast<const uint4*>(a.agg + (i < chunk ? i : 0u));
     }
   }
   // the first kSpecWords staging words are read before the chunk's length is
