@@ -638,6 +638,53 @@ int orc_kv_scores(int lat, uint64_t seed, float alpha, const uint32_t *words,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Matrix-vector products with a compressed weight matrix, in fp64, by the    */
+/* plain definition y = W_hat x.  The weights are rows x cols with tiles of   */
+/* 128 along each row (tile t = r * (cols / 128) + b holds row r, columns     */
+/* 128 b .. 128 b + 127), as encoded by orc_encode without dither.  W_hat of  */
+/* a tile is the decoder's reconstruction D (c_dec H u_hat) [HQ-explainer,    */
+/* Methodology 1: the inverse of the orthonormal RHT] taken in real           */
+/* arithmetic: H u_hat and the products are fp64 (exact for the integer       */
+/* codes of Z, D4 and E8), with no fp32 rounding of the weights.  x holds nb  */
+/* fp32 vectors [nb][cols]; y[j][r] = sum_c W_hat[r][c] x[j][c].  A tile that */
+/* does not parse counts as zeros and sets the status.                        */
+/* ------------------------------------------------------------------------ */
+int orc_gemv(int lat, uint64_t seed, float alpha, const uint32_t *words, const uint64_t *offsets,
+             const uint8_t *k, uint64_t rows, uint64_t cols, const float *x, uint32_t nb, double *y) {
+  if (lat_dim(lat) == 0 || !(alpha > 0.0f) || nb == 0 || cols == 0 || cols % N) return ORC_ERR_ARG;
+  float s[N], c_enc, c_dec;
+  orc_signs(seed, s);
+  orc_scales(alpha, &c_enc, &c_dec);
+  const uint64_t nblk = cols / N;
+  for (uint64_t i = 0; i < (uint64_t)nb * rows; ++i) y[i] = 0.0;
+  int status = ORC_OK;
+  for (uint64_t r = 0; r < rows; ++r) {
+    for (uint64_t b = 0; b < nblk; ++b) {
+      const uint64_t t = r * nblk + b;
+      int32_t codes[N];
+      int st = orc_parse_tile(lat, words, offsets[t], offsets[t + 1], (int)k[t], codes);
+      if (st != ORC_OK) {
+        status = st;
+        continue;
+      }
+      float uh[N];
+      dequant_codes(lat, seed, codes, 0, t, uh);
+      double w[N];
+      for (int i = 0; i < N; ++i) w[i] = (double)uh[i];
+      fwht128_f64(w);
+      for (int i = 0; i < N; ++i) w[i] = (double)s[i] * ((double)c_dec * w[i]);
+      for (uint32_t j = 0; j < nb; ++j) {
+        const float *xj = &x[(size_t)j * cols + b * N];
+        double acc = 0.0;
+        for (int i = 0; i < N; ++i) acc += w[i] * (double)xj[i];
+        y[(size_t)j * rows + r] += acc;
+      }
+    }
+  }
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Rate calibration [HQ-explainer, Methodology 3: achieved rate within about */
 /* 0.01 bps of the target].  Mechanism (reading): start from the             */
 /* high-resolution estimate alpha0 = sqrt(2 pi e) sigma / (nu 2^R), with     */

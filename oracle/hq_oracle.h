@@ -124,6 +124,12 @@ int orc_kv_scores(int lat, uint64_t seed, float alpha, const uint32_t *words,
                   uint64_t tiles_per_head, uint64_t tile_base, const float *q,
                   uint32_t qph, double *scores);
 
+/* Matrix-vector products with a compressed (undithered) weight matrix, fp64:
+ * y[j][r] = sum_c W_hat[r][c] x[j][c] with W_hat the reconstruction
+ * D (c_dec H u_hat) in real arithmetic; tiles of 128 along the rows. */
+int orc_gemv(int lat, uint64_t seed, float alpha, const uint32_t *words, const uint64_t *offsets,
+             const uint8_t *k, uint64_t rows, uint64_t cols, const float *x, uint32_t nb, double *y);
+
 /* Rate calibration: bisection on log2(alpha) for the payload rate
  * (bits per scalar).  Returns an ORC_ status. */
 int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,

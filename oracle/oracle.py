@@ -82,6 +82,7 @@ def lib():
             "orc_dequant_rotated": (_i, [_i, _u64, _p, _u64, _u64, _i, _i, _u64, _p]),
             "orc_kv_scores": (_i, [_i, _u64, _f, _p, _p, _p, _u32, _u64, _u64, _p, _u32, _p]),
             "orc_calibrate": (_i, [_i, _u64, _f, _p, _i, _u64, _i, _u64, _p, _p, _p]),
+            "orc_gemv": (_i, [_i, _u64, _f, _p, _p, _p, _u64, _u64, _p, _u32, _p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -298,6 +299,18 @@ def kv_scores(lat: int, seed: int, alpha: float, words, offsets, k, n_heads: int
     st = lib().orc_kv_scores(lat, seed, alpha, _ptr(words), _ptr(offsets), _ptr(k), n_heads,
                              tiles_per_head, tile_base, _ptr(q), qph, _ptr(scores))
     return st, scores.reshape(n_heads * qph, tiles_per_head)
+
+
+def gemv(lat: int, seed: int, alpha: float, words, offsets, k, rows: int, cols: int, x: np.ndarray):
+    """y = W_hat x in fp64 for nb fp32 vectors x [nb, cols]; returns (status, y [nb, rows])."""
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.uint64)
+    k = np.ascontiguousarray(k, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, cols)
+    nb = x.shape[0]
+    y = np.zeros(nb * rows, np.float64)
+    st = lib().orc_gemv(lat, seed, alpha, _ptr(words), _ptr(offsets), _ptr(k), rows, cols, _ptr(x), nb, _ptr(y))
+    return st, y.reshape(nb, rows)
 
 
 def calibrate(lat: int, seed: int, bps: float, x: np.ndarray, dithered=False, tile_base=0):

@@ -240,3 +240,60 @@ def test_scores_equal_query_dot_decoded_key(orc):
         want = np.einsum("hgi,hsi->hgs", q.reshape(H, qph, 128).astype(np.float64), khat).reshape(H * qph, S)
         scale = np.linalg.norm(q, axis=1)[:, None] * np.linalg.norm(khat.reshape(H * S, 128), axis=1).reshape(H, S).repeat(qph, 0)
         assert np.all(np.abs(sc - want) <= 1e-5 * scale)
+
+
+def test_gemv_unit_vectors_are_decoded_columns(orc):
+    """y = W_hat x with x = e_c is column c of the reconstruction.  For the
+    integer codes of Z, D4 and E8 the fp32 decoder computes each weight with
+    one rounding (c_dec times an exact integer transform), so the fp64 product
+    rounded to fp32 equals the decoded weight bit for bit; A2's sqrt(3)
+    coordinates make the decoder's transform inexact, within a few ulp.
+    Tiles of 128 along rows: 3 rows x 256 columns is 6 tiles, 2 per row."""
+    rng = np.random.default_rng(1500)
+    rows, cols = 3, 256
+    w = (rng.standard_normal((rows, cols)) * 0.05).astype(np.float32)
+    eye = np.eye(cols, dtype=np.float32)
+    for lat in (0, 1, 2, 3):
+        alpha = 0.01
+        st, words, off, k = orc.encode(lat, SEED, alpha, w)
+        assert st == 0
+        st, wd = orc.decode(lat, SEED, alpha, words, off, k)
+        assert st == 0
+        wd = wd.reshape(rows, cols)
+        st, y = orc.gemv(lat, SEED, alpha, words, off, k, rows, cols, eye)
+        assert st == 0 and y.shape == (cols, rows)
+        if lat == 1:
+            np.testing.assert_allclose(y.T, wd, rtol=0, atol=4e-6 * np.abs(wd).max())
+        else:
+            assert np.array_equal(y.T.astype(np.float32), wd)
+
+
+def test_gemv_batch_and_corrupt_tiles(orc):
+    """Several vectors at once equal the vectors one at a time; the product
+    matches the decoded matrix within the fp32 rounding of the decoded weights;
+    a record that does not parse counts as zeros and sets the status."""
+    rng = np.random.default_rng(1501)
+    rows, cols, nb = 5, 384, 3
+    w = (rng.standard_normal((rows, cols)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((nb, cols)).astype(np.float32)
+    alpha = 0.008
+    st, words, off, k = orc.encode(3, SEED, alpha, w)
+    st, y = orc.gemv(3, SEED, alpha, words, off, k, rows, cols, x)
+    assert st == 0
+    for j in range(nb):
+        st, yj = orc.gemv(3, SEED, alpha, words, off, k, rows, cols, x[j:j + 1])
+        assert np.array_equal(yj[0], y[j])
+    st, wd = orc.decode(3, SEED, alpha, words, off, k)
+    wd = wd.reshape(rows, cols).astype(np.float64)
+    want = x.astype(np.float64) @ wd.T
+    bound = 2.0 ** -24 * (np.abs(x).astype(np.float64) @ np.abs(wd).T) + 1e-12
+    assert np.all(np.abs(y - want) <= bound)
+    # tile 4 (row 1, block 1) corrupt: its contribution vanishes
+    k2 = k.copy()
+    k2[4] = (int(k2[4]) + 1) % 23
+    st, yc = orc.gemv(3, SEED, alpha, words, off, k2, rows, cols, x)
+    assert st == 5
+    part = x[:, 128:256].astype(np.float64) @ wd[1, 128:256]  # from the fp32-rounded weights
+    pbound = 2.0 ** -24 * (np.abs(x[:, 128:256]).astype(np.float64) @ np.abs(wd[1, 128:256])) + 1e-12
+    assert np.all(np.abs(yc[:, 1] - (y[:, 1] - part)) <= pbound)
+    np.testing.assert_array_equal(np.delete(yc, 1, axis=1), np.delete(y, 1, axis=1))
