@@ -118,12 +118,42 @@ def workload_rows(hq, W, torch, np, iters):
                          extra))
         return plan, enc, ws
 
+    def gemv(name, w, lat, bps, nbs=(1, 8)):
+        """Fused decode + matrix-vector products with the compressed matrix,
+        beside the dense bf16 product of the uncompressed matrix (context)."""
+        rows_, cols_ = w.shape
+        n_el = w.numel()
+        n_tiles = n_el // 128
+        plan = hq.Plan(lat, bps, seed)
+        ws = plan.workspace(n_tiles)
+        plan.calibrate(w, ws)
+        enc = hq.encode(plan, w, ws)
+        hq.check(ws)
+        bits = enc.total_bits()
+        for nb in nbs:
+            xv = torch.randn(nb, cols_, generator=torch.Generator(device=dev).manual_seed(nb), device=dev)
+            gws = hq.gemv_workspace(rows_, cols_, nb)
+            y = torch.empty(nb, rows_, dtype=torch.float32, device=dev)
+            tg = _time(torch, lambda: hq.gemv(plan, enc, rows_, cols_, xv, gws, out=y), iters)
+            hq.check(gws)
+            xb = xv.to(torch.bfloat16)
+            td = _time(torch, lambda: torch.matmul(xb, w.t()), iters)
+            r = _row(name, f"gemv (fused decode + dot), {nb} vector{'s' if nb > 1 else ''}", tg, n_el, 0.0, bits,
+                     n_tiles, {"lattice": "ZA2D4E8"[[0, 1, 3, 5][lat]:[1, 3, 5, 7][lat]], "bps": round(bits / n_el, 4),
+                               "weights_GBps_bf16_equiv": round(n_el * 2 / (tg * 1e-3) / 1e9, 1),
+                               "dense_bf16_matmul_ms": round(td, 5)},
+                     other_bytes=4.0 * nb * (rows_ + cols_))
+            del r["GBps_in"]
+            rows.append(r)
+        del ws
+
     x = W.c1(dev)
     alpha = float(np.float32(np.sqrt(2 * np.pi * np.e) * W.c1_sigma_eff() / 32.0))
     codec("fp32 4096x128 (one tile per row), fixed alpha", x, 3, 4.0, alpha=alpha, out_dtype=torch.float32)
     x = W.c2(dev)
     for bps in (3.0, 5.0):
         codec("bf16 4096x4096 weight", x, 3, bps)
+    gemv("bf16 4096x4096 weight", x, 3, 4.0)
     del x
     k, v, q = W.c3(dev)
     codec("KV bf16 [8,8,32768,128] K", k, 2, 2.0, dithered=True)
@@ -134,6 +164,8 @@ def workload_rows(hq, W, torch, np, iters):
     for lat, bps in ((1, 3.0), (1, 5.0), (0, 3.0), (0, 5.0), (3, 4.0)):
         codec("bf16 8192x28672 weight", x, lat, bps)
         torch.cuda.empty_cache()
+    gemv("bf16 8192x28672 weight", x, 3, 4.0)
+    torch.cuda.empty_cache()
     del x
     torch.cuda.empty_cache()
     k, v, q = W.c5(dev)

@@ -135,6 +135,25 @@ hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
                        uint64_t tiles_per_head, uint64_t tile_base, const float* q,
                        uint32_t qph, float* scores, void* ws, void* stream);
 
+/* Matrix-vector products with a compressed weight matrix, without
+ * materialising it: y[j*rows + r] = sum_c W_hat[r][c] x[j*cols + c] for nb
+ * vectors, W_hat being the decoder's reconstruction of a rows x cols matrix
+ * encoded by hq_encode (no dither) with tiles of 128 along each row (tile
+ * r*(cols/128) + b holds columns 128b..128b+127 of row r).  Each tile adds
+ * c_dec <u_hat, H D x_b> [Methodology 1: W_hat = D (c_dec H u_hat), H
+ * symmetric], so the weights are never inverse-transformed.  x: fp32
+ * [nb][cols], 16-byte aligned; y: fp32 [nb][rows]; cols a multiple of 128;
+ * 1 <= nb <= 16; rows * cols / 128 and nb * rows below 2^32.  ws: at least
+ * hq_gemv_workspace_bytes(rows, cols, nb) bytes, 16-byte aligned, zero-filled
+ * once (a hq_workspace_bytes workspace of the same tiles is not enough in
+ * general).  Three stream-ordered launches: rotate the vectors' blocks, one
+ * dot product per tile and vector, fixed-order row sums.  Corrupt records
+ * count as zeros and set HQ_ERR_CORRUPT. */
+size_t hq_gemv_workspace_bytes(uint64_t rows, uint64_t cols, uint32_t nb);
+hq_status hq_gemv(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
+                  const uint64_t* offsets, const uint8_t* k, uint64_t rows, uint64_t cols,
+                  const float* x, uint32_t nb, float* y, void* ws, void* stream);
+
 /* Synchronise stream, return the lowest data error recorded in ws since the
  * last call, and clear it. */
 hq_status hq_status_sync(void* ws, void* stream);

@@ -46,6 +46,8 @@ _SIGNATURES = {
     "hq_kv_encode": (_i, [_p, _p, _i, _u64, _u64, _p, _u64, _p, _p, _p, _p]),
     "hq_kv_decode": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _i, _p, _p]),
     "hq_kv_scores": (_i, [_p, _p, _u64, _p, _p, _u32, _u64, _u64, _p, _u32, _p, _p, _p]),
+    "hq_gemv_workspace_bytes": (C.c_size_t, [_u64, _u64, _u32]),
+    "hq_gemv": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _u32, _p, _p, _p]),
     "hq_status_sync": (_i, [_p, _p]),
     "hq_status_str": (C.c_char_p, [_i]),
 }
@@ -229,6 +231,27 @@ def kv_scores(plan: Plan, enc: Encoded, n_heads: int, tiles_per_head: int, q: to
                             _stream(stream))
     _check(rc, "kv_scores")
     return s
+
+
+def gemv_workspace(rows: int, cols: int, nb: int = 1, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for hq_gemv (the zero fill is required once)."""
+    n = int(lib().hq_gemv_workspace_bytes(rows, cols, nb))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def gemv(plan: Plan, enc: Encoded, rows: int, cols: int, x: torch.Tensor, ws: torch.Tensor,
+         out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """hq_gemv: fp32 [nb, rows] = x W_hat^T for the compressed rows x cols matrix (x fp32 [nb, cols])."""
+    if x.dtype != torch.float32 or not x.is_contiguous() or x.numel() % cols:
+        raise ValueError("x must be contiguous fp32 [nb, cols]")
+    if enc.dithered:
+        raise ValueError("matrix-vector products take an undithered weight stream")
+    nb = x.numel() // cols
+    y = out if out is not None else torch.empty(nb, rows, dtype=torch.float32, device=x.device)
+    rc = lib().hq_gemv(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),
+                       rows, cols, _dptr(x), nb, _dptr(y), _dptr(ws), _stream(stream))
+    _check(rc, "gemv")
+    return y
 
 
 def status_sync(ws: torch.Tensor, stream=None) -> int:

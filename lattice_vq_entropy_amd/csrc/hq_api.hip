@@ -261,6 +261,52 @@ hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words, 
                                    (hipStream_t)stream));
 }
 
+size_t hq_gemv_workspace_bytes(uint64_t rows, uint64_t cols, uint32_t nb) {
+  const uint64_t xr = hq::ws_align(4ull * nb * cols);
+  return (size_t)(sizeof(hq::WsHeader) + xr + 4ull * nb * rows * (cols / 128));
+}
+
+hq_status hq_gemv(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets,
+                  const uint8_t* k, uint64_t rows, uint64_t cols, const float* x, uint32_t nb, float* y,
+                  void* ws, void* stream) {
+  if (!plan) return HQ_ERR_ARG;
+  if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (cols == 0 || cols % 128 || nb == 0 || nb > 16) return HQ_ERR_ARG;
+  if (rows == 0) return HQ_OK;
+  if (!words || !offsets || !k || !x || !y || !ws) return HQ_ERR_ARG;
+  if (((uintptr_t)x & 15u) != 0 || ((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+  const uint64_t nblk = cols / 128, n_tiles = rows * nblk;
+  if (rows > 0xFFFFFFFFull || n_tiles / nblk != rows || n_tiles > 0xFFFFFFFFull || (uint64_t)nb * rows > 0xFFFFFFFFull ||
+      (uint64_t)nb * nblk > 0xFFFFFFFFull)
+    return HQ_ERR_ARG;
+  float* xr = (float*)((char*)ws + sizeof(hq::WsHeader));
+  float* dots = (float*)((char*)xr + hq::ws_align(4ull * nb * cols));
+  hq::DecArgs d{};
+  d.words = words;
+  d.n_words = n_words;
+  d.offsets = offsets;
+  d.kin = k;
+  d.n_tiles = n_tiles;
+  fill_common(plan, d.sl16, d.sl32, d.key0, d.key1);
+  d.c_dec = plan->c_dec;
+  d.ws = (hq::WsHeader*)ws;
+  d.xr = xr;
+  d.dots = dots;
+  d.nb = nb;
+  d.nblk = (uint32_t)nblk;
+  hq::GemvArgs g{};
+  g.x = x;
+  g.xr = xr;
+  g.dots = dots;
+  g.y = y;
+  g.rows = (uint32_t)rows;
+  g.nblk = (uint32_t)nblk;
+  g.nb = nb;
+  for (int i = 0; i < 4; ++i) g.sl32[i] = d.sl32[i];
+  g.c_dec = plan->c_dec;
+  return dev_err(hq::launch_gemv(plan->lattice, d, g, (hipStream_t)stream));
+}
+
 hq_status hq_status_sync(void* ws, void* stream) {
   if (!ws) return HQ_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;

@@ -7,7 +7,7 @@
 
 namespace hq {
 
-constexpr int kOutF32 = 0, kOutBf16 = 1, kOutScores = 2;
+constexpr int kOutF32 = 0, kOutBf16 = 1, kOutScores = 2, kOutGemv = 3;
 
 struct EncArgs {
   const void* x;
@@ -62,10 +62,27 @@ struct DecArgs {
   float* scores;
   uint32_t qph;
   uint64_t tiles_per_head;
+  // matrix-vector mode: rotated vector blocks H D x (nb x cols fp32), per-tile
+  // dot products (n_tiles x nb fp32), vectors per call, 128-column blocks per row
+  const float* xr;
+  float* dots;
+  uint32_t nb;
+  uint32_t nblk;
+};
+
+struct GemvArgs {
+  const float* x;   // nb x cols
+  float* xr;        // nb x cols: H D x per 128-column block
+  const float* dots;
+  float* y;         // nb x rows
+  uint32_t rows, nblk, nb;
+  uint32_t sl32[4];
+  float c_dec;
 };
 
 hipError_t launch_encode(int lat, bool dither, bool bf16, bool len_only, const EncArgs& a, hipStream_t st);
 hipError_t launch_decode(int lat, bool dither, int out, const DecArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_gemv(int lat, const DecArgs& d, const GemvArgs& g, hipStream_t st);
 hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
                         hipStream_t st);
 

@@ -747,6 +747,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
     t_limit = a.n_tiles;
   }
   const uint32_t nt = (uint32_t)((t_limit - t_first) < (uint64_t)kChunkTiles ? (t_limit - t_first) : kChunkTiles);
+  uint32_t blk0 = 0;  // matrix-vector mode, nblk >= 32: block of the chunk's first tile
+  if constexpr (OUT == kOutGemv) blk0 = a.nblk >= 32u ? (uint32_t)t_first % a.nblk : 0u;
 
   if (tid <= (int)nt) s_off[tid] = a.offsets[t_first + tid];
   if (tid < (int)nt) s_k[tid] = a.kin[t_first + tid];
@@ -843,7 +845,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
         for (int i = 0; i < 8; ++i) pv[i] = pv[i] - d[i];
       }
     }
-    if constexpr (OUT == kOutScores) {
+    if constexpr (OUT == kOutGemv) {
+      // tile t covers 128-column block t mod nblk of its row: the dot product
+      // with each vector's rotated block (the rows of a tile share validity)
+      if (valid) {
+        const uint32_t tt = (uint32_t)t;  // n_tiles < 2^32
+        const uint32_t blk = a.nblk >= 32u ? (blk0 + (uint32_t)slot >= a.nblk ? blk0 + (uint32_t)slot - a.nblk
+                                                                                : blk0 + (uint32_t)slot)
+                                           : tt % a.nblk;
+        const float* xb = a.xr + (uint64_t)blk * kTile + 8 * v;
+        for (uint32_t j = 0; j < a.nb; ++j) {
+          const float4 x0 = *reinterpret_cast<const float4*>(xb + (uint64_t)j * a.nblk * kTile);
+          const float4 x1 = *reinterpret_cast<const float4*>(xb + (uint64_t)j * a.nblk * kTile + 4);
+          const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          float acc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(xv[i], pv[i], acc);
+          acc = row_sum_f32(acc);
+          if (r == 0) a.dots[(uint64_t)tt * a.nb + j] = acc;
+        }
+      }
+    } else if constexpr (OUT == kOutScores) {
       if (valid) {
         const uint64_t sidx = t - head * a.tiles_per_head;
         for (uint32_t g = 0; g < a.qph; ++g) {
@@ -976,6 +998,68 @@ hipError_t launch_decode(int lat, bool dither, int out, const DecArgs& a, dim3 g
   HQ_DEC(0) HQ_DEC(1) HQ_DEC(2) HQ_DEC(3)
 #undef HQ_DEC
   return hipErrorInvalidValue;
+}
+
+// Matrix-vector products, step 1: the vectors' 128-column blocks rotated as
+// the weights were, xr = H D x (exact signs, unnormalised transform), one block
+// per 16-lane row, stored in natural coordinate order.
+__global__ __launch_bounds__(256) void rotx_k(GemvArgs g) {
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15;
+  const int v = lane_vector(r);
+  const uint32_t q = blockIdx.x * 16u + (uint32_t)(tid >> 4);  // block of all nb vectors
+  const bool ok = q < g.nb * g.nblk;
+  const uint32_t j = ok ? q / g.nblk : 0u, blk = ok ? q % g.nblk : 0u;
+  const uint64_t base = ((uint64_t)j * g.nblk + blk) * kTile + 8 * v;
+  float xv[8];
+  const float4 x0 = *reinterpret_cast<const float4*>(g.x + base);
+  const float4 x1 = *reinterpret_cast<const float4*>(g.x + base + 4);
+  xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
+  xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
+  const uint32_t sm = lane_signs32(g.sl32, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xv[i] = __builtin_bit_cast(float, fbits(xv[i]) ^ ((sm << i) & 0x80000000u));
+  const FwhtSigns fs = fwht_signs(v);
+  fwht_tile(xv, fs);  // every lane of the row takes part (cross-lane stages)
+  if (ok) {
+    float4* dst = reinterpret_cast<float4*>(g.xr + base);
+    dst[0] = make_float4(xv[0] * fs.lane_sign, xv[1] * fs.lane_sign, xv[2] * fs.lane_sign, xv[3] * fs.lane_sign);
+    dst[1] = make_float4(xv[4] * fs.lane_sign, xv[5] * fs.lane_sign, xv[6] * fs.lane_sign, xv[7] * fs.lane_sign);
+  }
+}
+
+// Matrix-vector products, step 3: y[j][r] = c_dec * sum over the row's blocks
+// of the tile dot products, one wave per (vector, row): lane l adds blocks l,
+// l + 64, ... in order, then a fixed tree over the lanes.
+__global__ __launch_bounds__(256) void rowsum_k(GemvArgs g) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t q = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
+  if (q >= g.nb * g.rows) return;  // the whole wave
+  const uint32_t j = q / g.rows, row = q % g.rows;
+  const float* d = g.dots + (uint64_t)row * g.nblk * g.nb + j;
+  float acc = 0.0f;
+  for (uint32_t b = lane; b < g.nblk; b += 64u) acc += d[(uint64_t)b * g.nb];
+  acc = row_sum_f32(acc);
+  const int ai = __builtin_bit_cast(int, acc);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ai, 48));
+  const float tot3 = ((r0 + r1) + r2) + r3;
+  if (lane == 0) g.y[(uint64_t)j * g.rows + row] = tot3 * g.c_dec;
+}
+
+hipError_t launch_gemv(int lat, const DecArgs& d, const GemvArgs& g, hipStream_t st) {
+  const uint32_t nq = g.nb * g.nblk;
+  hipLaunchKernelGGL(rotx_k, dim3((nq + 15u) / 16u), dim3(256), 0, st, g);
+  const dim3 grid((uint32_t)((d.n_tiles + kChunkTiles - 1) / kChunkTiles));
+  if (lat == 0) hipLaunchKernelGGL((decode_k<0, false, kOutGemv>), grid, dim3(256), 0, st, d);
+  else if (lat == 1) hipLaunchKernelGGL((decode_k<1, false, kOutGemv>), grid, dim3(256), 0, st, d);
+  else if (lat == 2) hipLaunchKernelGGL((decode_k<2, false, kOutGemv>), grid, dim3(256), 0, st, d);
+  else if (lat == 3) hipLaunchKernelGGL((decode_k<3, false, kOutGemv>), grid, dim3(256), 0, st, d);
+  else return hipErrorInvalidValue;
+  const uint32_t nw = g.nb * g.rows;
+  hipLaunchKernelGGL(rowsum_k, dim3((nw + 3u) / 4u), dim3(256), 0, st, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,

@@ -64,3 +64,15 @@ def test_argument_errors_are_synchronous(hq):
     assert L.hq_kv_scores(p.handle, None, 0, None, None, 1, 1, 0, None, 17, None, None, None) == hq.ERR_ARG
     assert L.hq_status_sync(None, None) == hq.ERR_ARG
     assert hq.status_str(hq.ERR_CORRUPT) == "corrupt stream"
+    # matrix-vector products: shape and batch limits, null and misaligned pointers
+    D = C.c_void_p(4096)
+    assert L.hq_gemv(p.handle, D, 8, D, D, 2, 200, D, 1, D, D, None) == hq.ERR_ARG    # cols % 128
+    assert L.hq_gemv(p.handle, D, 8, D, D, 2, 256, D, 0, D, D, None) == hq.ERR_ARG    # nb = 0
+    assert L.hq_gemv(p.handle, D, 8, D, D, 2, 256, D, 17, D, D, None) == hq.ERR_ARG   # nb > 16
+    assert L.hq_gemv(p.handle, D, 8, D, D, 2, 256, None, 1, D, D, None) == hq.ERR_ARG
+    assert L.hq_gemv(p.handle, D, 8, D, D, 2, 256, C.c_void_p(4100), 1, D, D, None) == hq.ERR_ARG
+    assert L.hq_gemv(p.handle, D, 8, D, D, 0, 256, D, 1, D, D, None) == hq.OK         # no rows: nothing to do
+    q = hq.Plan("E8", 4.0, 1)
+    assert L.hq_gemv(q.handle, D, 8, D, D, 2, 256, D, 1, D, D, None) == hq.ERR_NOALPHA
+    # workspace: header, the rotated vectors (256-byte aligned), one fp32 per tile and vector
+    assert L.hq_gemv_workspace_bytes(3, 256, 2) == 256 + 2048 + 4 * 2 * 3 * 2
