@@ -614,7 +614,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uin
   }
   // remainders: 8 fields of k bits at fixed positions
   uint32_t rem[8];
-  const uint32_t rpos = base + RAW + 8u * (uint32_t)v * k;
+  const uint32_t rpos = base + RAW + __umul24(8u * (uint32_t)v, k);
   if (k <= 7) {
     const uint32_t w = rpos >> 5, sh = rpos & 31;
     const uint32_t w0 = s[w], w1 = s[w + 1], w2 = s[w + 2];
@@ -823,26 +823,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
     const int slot = p * 16 + pslot;
     const bool valid = slot < (int)nt;
     const uint64_t t = t_first + slot;
+    // pv is written by a successful parse.  Without dither, slots past the
+    // end and corrupt records (both rare) take zeros in a branch of their own,
+    // so the common path spends no moves on them; the dithered variants keep
+    // the zero start (fewer live registers there).
     float pv[8];
+    if constexpr (DITHER) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pv[i] = 0.0f;
+      for (int i = 0; i < 8; ++i) pv[i] = 0.0f;
+    }
+    bool good = false;
     if (valid) {
       const uint64_t o0 = s_off[slot], o1 = s_off[slot + 1];
       const uint32_t k = s_k[slot];
-      const uint64_t Lr = o1 - o0;
-      const bool ok = span_ok && o1 >= o0 && k <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + k) && Lr <= MAXREC;
-      bool good = false;
+      const uint64_t Lr = o1 - o0;  // wraps past MAXREC when o1 < o0
+      const bool ok = span_ok && k <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + k) && Lr <= MAXREC;
       if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, s_ust[pslot],
                                        reinterpret_cast<uint8_t*>(&s_tb[pslot]), pv);
+      if (!good && r == 0) set_status(a.ws, 5);
+      if constexpr (DITHER) {
+        if (!good) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pv[i] = 0.0f;
+        } else {
+          float d[8];
+          dither_lane<L>(a.key0, a.key1, a.tile_base + t, v, d);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pv[i] = pv[i] - d[i];
+        }
+      }
+    }
+    if constexpr (!DITHER) {
       if (!good) {
-        if (r == 0) set_status(a.ws, 5);
 #pragma unroll
         for (int i = 0; i < 8; ++i) pv[i] = 0.0f;
-      } else if constexpr (DITHER) {
-        float d[8];
-        dither_lane<L>(a.key0, a.key1, a.tile_base + t, v, d);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = pv[i] - d[i];
       }
     }
     if constexpr (OUT == kOutGemv) {
