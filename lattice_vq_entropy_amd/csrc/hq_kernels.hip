@@ -184,6 +184,7 @@ __device__ __forceinline__ void tile_pack(uint32_t* s, uint32_t tb, const TileSy
                                           int grp, bool valid) {
   constexpr uint32_t RAW = Lat<L>::raw;
   const uint32_t k = ts.k, k1 = k + 1u;  // m >> j = w >> (j + 1); the low k bits of m are bits 1..k of w
+  uint32_t raw16 = 0;
   if constexpr (RAW > 0) {
     // bit v of a tile's field is the coset bit of vector v, held by lane v(r):
     // lanes 4..7 and 12..15 of each row hold their vectors in reverse order,
@@ -193,8 +194,10 @@ __device__ __forceinline__ void tile_pack(uint32_t* s, uint32_t tb, const TileSy
     hi = ((hi >> 1) & 0x5555555555555555ull) | ((hi & 0x5555555555555555ull) << 1);
     hi = ((hi >> 2) & 0x3333333333333333ull) | ((hi & 0x3333333333333333ull) << 2);
     bm = (bm & 0x0F0F0F0F0F0F0F0Full) | hi;
-    const uint32_t raw16 = (uint32_t)(bm >> (grp * 16)) & 0xFFFFu;
-    if (valid && r == 0) lds_or64(s, tb, raw16);
+    raw16 = (uint32_t)(bm >> (grp * 16)) & 0xFFFFu;
+    // lane 0 of a row (vector 0) writes the field together with its remainders
+    // when they fit one 64-bit value (1 <= k <= 6), else on its own
+    if (valid && r == 0 && (k == 0 || k > 6)) lds_or64(s, tb, raw16);
   }
   // exclusive scan of the unary lengths in vector order
   const uint32_t Uv = (uint32_t)__builtin_amdgcn_ds_bpermute(vaddr, (int)ts.U);
@@ -210,7 +213,13 @@ __device__ __forceinline__ void tile_pack(uint32_t* s, uint32_t tb, const TileSy
         lo |= __builtin_amdgcn_ubfe(ts.w[j], 1, k) << (j * k);
         hi |= __builtin_amdgcn_ubfe(ts.w[4 + j], 1, k) << (j * k);
       }
-      lds_or64(s, rpos, (uint64_t)lo | ((uint64_t)hi << (4 * k)));
+      uint64_t val = (uint64_t)lo | ((uint64_t)hi << (4 * k));
+      uint32_t pos = rpos;
+      if (RAW > 0 && r == 0 && k <= 6) {  // rpos = tb + RAW for vector 0
+        val = (val << RAW) | raw16;
+        pos = tb;
+      }
+      lds_or64(s, pos, val);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) lds_or64(s, rpos + j * k, __builtin_amdgcn_ubfe(ts.w[j], 1, k));
@@ -221,7 +230,11 @@ __device__ __forceinline__ void tile_pack(uint32_t* s, uint32_t tb, const TileSy
     // built from the last code back: V_j = ((V_(j+1) << 1) | 1) << q_j
     uint64_t msk = 1ull << (ts.w[7] >> k1);
 #pragma unroll
-    for (int j = 6; j >= 0; --j) msk = ((msk << 1) | 1ull) << (ts.w[j] >> k1);
+    for (int j = 6; j >= 0; --j) {
+      uint64_t t;
+      asm("v_lshl_add_u64 %0, %1, 1, 1" : "=v"(t) : "v"(msk));  // (msk << 1) + 1 in one instruction
+      msk = t << (ts.w[j] >> k1);
+    }
     lds_or64(s, upos, msk);
   } else {
     uint32_t pos = upos;
