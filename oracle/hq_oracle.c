@@ -638,6 +638,82 @@ int orc_kv_scores(int lat, uint64_t seed, float alpha, const uint32_t *words,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Attention over compressed keys and values, in fp64, by the plain          */
+/* definition: for each query q_{h,g} (qph queries per KV head h),           */
+/*   s_t = scale * q . k_hat_t,  p = softmax(s) over the seq keys of head h, */
+/*   out = sum_t p_t v_hat_t,                                                */
+/* with k_hat and v_hat the decoder's reconstructions D (c_dec H u_hat) of   */
+/* the dithered KV streams [HQ-explainer, Methodology 1 and 4] taken in real */
+/* arithmetic (fp64, no fp32 rounding of the reconstructions).  Keys of head */
+/* h are tiles h*seq + s of the K stream (tile ids k_tile_base + that), the  */
+/* values likewise in the V stream; the two plans share lattice and seed and */
+/* have their own alpha.  The softmax subtracts the maximum score.  Corrupt  */
+/* records count as zero vectors and set the status.                         */
+/* ------------------------------------------------------------------------ */
+static void recon_f64(int lat, uint64_t seed, const float s[128], float c_dec, const uint32_t *words,
+                      const uint64_t *offsets, const uint8_t *k, uint64_t t, uint64_t tile_id, double w[128],
+                      int *status) {
+  int32_t codes[N];
+  int st = orc_parse_tile(lat, words, offsets[t], offsets[t + 1], (int)k[t], codes);
+  if (st != ORC_OK) {
+    *status = st;
+    for (int i = 0; i < N; ++i) w[i] = 0.0;
+    return;
+  }
+  float uh[N];
+  dequant_codes(lat, seed, codes, 1, tile_id, uh);
+  for (int i = 0; i < N; ++i) w[i] = (double)uh[i];
+  fwht128_f64(w);
+  for (int i = 0; i < N; ++i) w[i] = (double)s[i] * ((double)c_dec * w[i]);
+}
+
+int orc_kv_attention(int lat, uint64_t seed, float alpha_k, const uint32_t *kw, const uint64_t *ko,
+                     const uint8_t *kk, uint64_t k_tile_base, float alpha_v, const uint32_t *vw,
+                     const uint64_t *vo, const uint8_t *vk, uint64_t v_tile_base, uint32_t n_heads,
+                     uint64_t seq, const float *q, uint32_t qph, float scale, double *out) {
+  if (lat_dim(lat) == 0 || !(alpha_k > 0.0f) || !(alpha_v > 0.0f) || qph == 0 || seq == 0) return ORC_ERR_ARG;
+  float s[N], c_enc, ck, cv;
+  orc_signs(seed, s);
+  orc_scales(alpha_k, &c_enc, &ck);
+  orc_scales(alpha_v, &c_enc, &cv);
+  double *sc = (double *)malloc(sizeof(double) * (size_t)seq * qph);
+  if (!sc) return ORC_ERR_ARG;
+  int status = ORC_OK;
+  for (uint32_t h = 0; h < n_heads; ++h) {
+    for (uint64_t j = 0; j < seq; ++j) {
+      const uint64_t t = (uint64_t)h * seq + j;
+      double kh[N];
+      recon_f64(lat, seed, s, ck, kw, ko, kk, t, k_tile_base + t, kh, &status);
+      for (uint32_t g = 0; g < qph; ++g) {
+        const float *qr = &q[((size_t)h * qph + g) * N];
+        double acc = 0.0;
+        for (int i = 0; i < N; ++i) acc += (double)qr[i] * kh[i];
+        sc[(size_t)g * seq + j] = (double)scale * acc;
+      }
+    }
+    for (uint32_t g = 0; g < qph; ++g) {
+      double *o = &out[((size_t)h * qph + g) * N];
+      const double *sg = &sc[(size_t)g * seq];
+      double m = sg[0];
+      for (uint64_t j = 1; j < seq; ++j) m = sg[j] > m ? sg[j] : m;
+      double l = 0.0;
+      for (int i = 0; i < N; ++i) o[i] = 0.0;
+      for (uint64_t j = 0; j < seq; ++j) {
+        const double pj = exp(sg[j] - m);
+        l += pj;
+        double vh[N];
+        recon_f64(lat, seed, s, cv, vw, vo, vk, (uint64_t)h * seq + j, v_tile_base + (uint64_t)h * seq + j, vh,
+                  &status);
+        for (int i = 0; i < N; ++i) o[i] += pj * vh[i];
+      }
+      for (int i = 0; i < N; ++i) o[i] /= l;
+    }
+  }
+  free(sc);
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Matrix-vector products with a compressed weight matrix, in fp64, by the    */
 /* plain definition y = W_hat x.  The weights are rows x cols with tiles of   */
 /* 128 along each row (tile t = r * (cols / 128) + b holds row r, columns     */

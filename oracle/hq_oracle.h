@@ -124,6 +124,13 @@ int orc_kv_scores(int lat, uint64_t seed, float alpha, const uint32_t *words,
                   uint64_t tiles_per_head, uint64_t tile_base, const float *q,
                   uint32_t qph, double *scores);
 
+/* Attention over dithered compressed keys and values, fp64: out[(h*qph+g)*128
+ * + i] = sum_t softmax_t(scale * q_{h,g} . k_hat_{h,t}) v_hat_{h,t}[i]. */
+int orc_kv_attention(int lat, uint64_t seed, float alpha_k, const uint32_t *kw, const uint64_t *ko,
+                     const uint8_t *kk, uint64_t k_tile_base, float alpha_v, const uint32_t *vw,
+                     const uint64_t *vo, const uint8_t *vk, uint64_t v_tile_base, uint32_t n_heads,
+                     uint64_t seq, const float *q, uint32_t qph, float scale, double *out);
+
 /* Matrix-vector products with a compressed (undithered) weight matrix, fp64:
  * y[j][r] = sum_c W_hat[r][c] x[j][c] with W_hat the reconstruction
  * D (c_dec H u_hat) in real arithmetic; tiles of 128 along the rows. */

@@ -83,6 +83,8 @@ def lib():
             "orc_kv_scores": (_i, [_i, _u64, _f, _p, _p, _p, _u32, _u64, _u64, _p, _u32, _p]),
             "orc_calibrate": (_i, [_i, _u64, _f, _p, _i, _u64, _i, _u64, _p, _p, _p]),
             "orc_gemv": (_i, [_i, _u64, _f, _p, _p, _p, _u64, _u64, _p, _u32, _p]),
+            "orc_kv_attention": (_i, [_i, _u64, _f, _p, _p, _p, _u64, _f, _p, _p, _p, _u64, _u32, _u64, _p,
+                                      _u32, _f, _p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -311,6 +313,20 @@ def gemv(lat: int, seed: int, alpha: float, words, offsets, k, rows: int, cols: 
     y = np.zeros(nb * rows, np.float64)
     st = lib().orc_gemv(lat, seed, alpha, _ptr(words), _ptr(offsets), _ptr(k), rows, cols, _ptr(x), nb, _ptr(y))
     return st, y.reshape(nb, rows)
+
+
+def kv_attention(lat: int, seed: int, alpha_k: float, kstream, k_tile_base: int, alpha_v: float, vstream,
+                 v_tile_base: int, n_heads: int, seq: int, q: np.ndarray, qph: int, scale: float):
+    """softmax(scale q . k_hat) v_hat per query in fp64; streams are (words, offsets, k).
+    Returns (status, out [n_heads*qph, 128])."""
+    kw, ko, kk = (np.ascontiguousarray(a, dtype=d) for a, d in zip(kstream, (np.uint32, np.uint64, np.uint8)))
+    vw, vo, vk = (np.ascontiguousarray(a, dtype=d) for a, d in zip(vstream, (np.uint32, np.uint64, np.uint8)))
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    assert q.size == n_heads * qph * TILE
+    out = np.zeros(n_heads * qph * TILE, np.float64)
+    st = lib().orc_kv_attention(lat, seed, alpha_k, _ptr(kw), _ptr(ko), _ptr(kk), k_tile_base, alpha_v, _ptr(vw),
+                                _ptr(vo), _ptr(vk), v_tile_base, n_heads, seq, _ptr(q), qph, scale, _ptr(out))
+    return st, out.reshape(n_heads * qph, TILE)
 
 
 def calibrate(lat: int, seed: int, bps: float, x: np.ndarray, dithered=False, tile_base=0):

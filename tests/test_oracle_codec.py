@@ -297,3 +297,49 @@ def test_gemv_batch_and_corrupt_tiles(orc):
     pbound = 2.0 ** -24 * (np.abs(x[:, 128:256]).astype(np.float64) @ np.abs(wd[1, 128:256])) + 1e-12
     assert np.all(np.abs(yc[:, 1] - (y[:, 1] - part)) <= pbound)
     np.testing.assert_array_equal(np.delete(yc, 1, axis=1), np.delete(y, 1, axis=1))
+
+
+def _kv_streams(orc, rng, H, S, lat, alpha_k, alpha_v):
+    k = rng.standard_normal((H * S, 128)).astype(np.float32)
+    v = rng.standard_normal((H * S, 128)).astype(np.float32)
+    st, kw, ko, kk = orc.encode(lat, SEED, alpha_k, k, dithered=True, tile_base=0)
+    assert st == 0
+    st, vw, vo, vk = orc.encode(lat, SEED, alpha_v, v, dithered=True, tile_base=H * S)
+    assert st == 0
+    st, vd = orc.decode(lat, SEED, alpha_v, vw, vo, vk, dithered=True, tile_base=H * S)
+    assert st == 0
+    return (kw, ko, kk), (vw, vo, vk), vd.reshape(H, S, 128).astype(np.float64)
+
+
+def test_attention_special_cases(orc):
+    """softmax(scale q.k_hat) v_hat: one key gives its value; scale 0 gives the
+    plain mean of the values; a very large scale gives the value of the key
+    with the largest fused score (kv_scores, computed in the rotated domain)."""
+    rng = np.random.default_rng(1600)
+    H, S, qph, lat = 2, 24, 3, 3
+    ak, av = 0.5, 0.4
+    ks, vs, vd = _kv_streams(orc, rng, H, S, lat, ak, av)
+    q = rng.standard_normal((H * qph, 128)).astype(np.float32)
+    tol = 64 * 2.0 ** -24 * np.abs(vd).max()  # the fp32 decode's rounding
+    # one key per head: the first tile of each head's stream is tile h*S, so
+    # use a stream of S = 1 tiles
+    ks1, vs1, vd1 = _kv_streams(orc, rng, H, 1, lat, ak, av)
+    st, o = orc.kv_attention(lat, SEED, ak, ks1, 0, av, vs1, H, H, 1, q, qph, 0.09)
+    assert st == 0
+    np.testing.assert_allclose(o.reshape(H, qph, 128), np.repeat(vd1, qph, axis=1), rtol=0, atol=tol)
+    # scale 0: uniform weights
+    st, o = orc.kv_attention(lat, SEED, ak, ks, 0, av, vs, H * S, H, S, q, qph, 0.0)
+    assert st == 0
+    want = np.repeat(vd.mean(axis=1)[:, None, :], qph, axis=1)
+    np.testing.assert_allclose(o.reshape(H, qph, 128), want, rtol=0, atol=tol)
+    # large scale: the arg-max key of the fused scores
+    st, sc = orc.kv_scores(lat, SEED, ak, *ks, H, S, 0, q, qph)
+    assert st == 0
+    st, o = orc.kv_attention(lat, SEED, ak, ks, 0, av, vs, H * S, H, S, q, qph, 1e4)
+    assert st == 0 and np.isfinite(o).all()
+    for h in range(H):
+        for g in range(qph):
+            row = sc[h * qph + g]
+            top = np.argsort(row)[-2:]
+            if (row[top[1]] - row[top[0]]) * 1e4 > 50:  # the runner-up's weight is below e^-50
+                np.testing.assert_allclose(o[h * qph + g], vd[h, top[1]], rtol=0, atol=tol)
