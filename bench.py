@@ -180,8 +180,19 @@ def workload_rows(hq, W, torch, np, iters):
                      bits, n_el // 128, {"bps": round(bits / n_el, 4),
                                          "scores_GBps": round(sc.numel() * 4 / (ts * 1e-3) / 1e9, 1)},
                      other_bytes=4.0 * (sc.numel() + q.numel())))
-    codec("KV bf16 [1,8,131072,128] V", v, 3, 1.7, dithered=True, tile_base=n_el // 128)
-    del k, v, q, sc
+    plan_v, enc_v, ws_v = codec("KV bf16 [1,8,131072,128] V", v, 3, 1.7, dithered=True, tile_base=n_el // 128)
+    aws = hq.attention_workspace(heads, seq, qph)
+    ao = torch.empty(heads * qph, 128, dtype=torch.float32, device=dev)
+    ta = _time(torch, lambda: hq.kv_attention(plan, enc, plan_v, enc_v, heads, seq, q, qph, 128 ** -0.5, aws,
+                                              out=ao), iters)
+    hq.check(aws)
+    bits_kv = bits + enc_v.total_bits()
+    rows.append(_row("KV bf16 [1,8,131072,128] K and V x 32 query heads", "kv_attention (fused decode, softmax, P.V)",
+                     ta, 2 * n_el, 0.0, bits_kv, 2 * n_el // 128,
+                     {"bps": round(bits_kv / (2 * n_el), 4),
+                      "kv_GBps_bf16_equiv": round(2 * n_el * 2 / (ta * 1e-3) / 1e9, 1)},
+                     other_bytes=4.0 * (q.numel() + ao.numel())))
+    del k, v, q, sc, aws, ao
     torch.cuda.empty_cache()
     return rows
 

@@ -154,6 +154,30 @@ hq_status hq_gemv(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
                   const uint64_t* offsets, const uint8_t* k, uint64_t rows, uint64_t cols,
                   const float* x, uint32_t nb, float* y, void* ws, void* stream);
 
+/* Attention of n_heads * qph queries over compressed keys and values, without
+ * materialising them [Methodology 4: the dithered KV cache; Methodology 1:
+ * the RHT is orthogonal, so q . k_hat = c_dec_K <H D q, u_hat_K> and
+ * sum_j p_j v_hat_j = D (c_dec_V H sum_j p_j u_hat_V,j)]:
+ *   out[h*qph + g] = sum_s softmax_s(scale * q_{h,g} . k_hat_{h,s}) v_hat_{h,s}
+ * for the keys and values of head h stored as tiles h*seq + s of one
+ * hq_kv_encode each (tile ids k_tile_base + that and v_tile_base + that).
+ * plan_k and plan_v hold each stream's alpha and must share lattice and seed.
+ * q: fp32 [n_heads*qph][128] (finite); out: fp32 [n_heads*qph][128];
+ * 1 <= qph <= 16; scale finite.  The weighted sums are formed in the rotated
+ * domain by work-groups of 256 keys (maximum, weights e^(s - m) and their sum
+ * per group) and combined per query in a fixed order, so results are
+ * deterministic.  ws: at least hq_kv_attention_workspace_bytes(n_heads, seq,
+ * qph) bytes, 16-byte aligned, zero-filled once.  Two stream-ordered
+ * launches.  Records that do not parse count as zero vectors (score
+ * scale * 0) and set HQ_ERR_CORRUPT. */
+size_t hq_kv_attention_workspace_bytes(uint32_t n_heads, uint64_t seq, uint32_t qph);
+hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_n_words,
+                          const uint64_t* k_offsets, const uint8_t* k_k, uint64_t k_tile_base,
+                          hq_plan_t plan_v, const uint32_t* v_words, uint64_t v_n_words,
+                          const uint64_t* v_offsets, const uint8_t* v_k, uint64_t v_tile_base,
+                          uint32_t n_heads, uint64_t seq, const float* q, uint32_t qph, float scale,
+                          float* out, void* ws, void* stream);
+
 /* Synchronise stream, return the lowest data error recorded in ws since the
  * last call, and clear it. */
 hq_status hq_status_sync(void* ws, void* stream);

@@ -48,6 +48,9 @@ _SIGNATURES = {
     "hq_kv_scores": (_i, [_p, _p, _u64, _p, _p, _u32, _u64, _u64, _p, _u32, _p, _p, _p]),
     "hq_gemv_workspace_bytes": (C.c_size_t, [_u64, _u64, _u32]),
     "hq_gemv": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _u32, _p, _p, _p]),
+    "hq_kv_attention_workspace_bytes": (C.c_size_t, [_u32, _u64, _u32]),
+    "hq_kv_attention": (_i, [_p, _p, _u64, _p, _p, _u64, _p, _p, _u64, _p, _p, _u64, _u32, _u64, _p, _u32, C.c_float,
+                             _p, _p, _p]),
     "hq_status_sync": (_i, [_p, _p]),
     "hq_status_str": (C.c_char_p, [_i]),
 }
@@ -252,6 +255,32 @@ def gemv(plan: Plan, enc: Encoded, rows: int, cols: int, x: torch.Tensor, ws: to
                        rows, cols, _dptr(x), nb, _dptr(y), _dptr(ws), _stream(stream))
     _check(rc, "gemv")
     return y
+
+
+def attention_workspace(n_heads: int, seq: int, qph: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for hq_kv_attention (the zero fill is required once)."""
+    n = int(lib().hq_kv_attention_workspace_bytes(n_heads, seq, qph))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def kv_attention(plan_k: Plan, enc_k: Encoded, plan_v: Plan, enc_v: Encoded, n_heads: int, seq: int,
+                 q: torch.Tensor, qph: int, scale: float, ws: torch.Tensor, out: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """hq_kv_attention: fp32 [n_heads*qph, 128] = softmax(scale q . k_hat) v_hat per query, without
+    materialising k_hat or v_hat (both streams dithered, seq tiles per head)."""
+    if q.dtype != torch.float32 or q.numel() != n_heads * qph * TILE:
+        raise ValueError("q must be fp32 [n_heads*qph, 128]")
+    if not (enc_k.dithered and enc_v.dithered):
+        raise ValueError("attention takes dithered key and value streams")
+    if enc_k.n_tiles < n_heads * seq or enc_v.n_tiles < n_heads * seq:
+        raise ValueError("the streams hold fewer than n_heads*seq tiles")
+    o = out if out is not None else torch.empty(n_heads * qph, TILE, dtype=torch.float32, device=q.device)
+    rc = lib().hq_kv_attention(plan_k.handle, _dptr(enc_k.words), enc_k.words.numel(), _dptr(enc_k.offsets),
+                               _dptr(enc_k.k), enc_k.tile_base, plan_v.handle, _dptr(enc_v.words),
+                               enc_v.words.numel(), _dptr(enc_v.offsets), _dptr(enc_v.k), enc_v.tile_base,
+                               n_heads, seq, _dptr(q), qph, scale, _dptr(o), _dptr(ws), _stream(stream))
+    _check(rc, "kv_attention")
+    return o
 
 
 def status_sync(ws: torch.Tensor, stream=None) -> int:

@@ -307,6 +307,52 @@ hq_status hq_gemv(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const
   return dev_err(hq::launch_gemv(plan->lattice, d, g, (hipStream_t)stream));
 }
 
+size_t hq_kv_attention_workspace_bytes(uint32_t n_heads, uint64_t seq, uint32_t qph) {
+  const uint64_t groups = (seq + hq::kAttnChunks * hq::kChunkTiles - 1) / (hq::kAttnChunks * hq::kChunkTiles);
+  return (size_t)(sizeof(hq::WsHeader) + 4ull * n_heads * groups * qph * hq::kAttnPart);
+}
+
+hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_n_words, const uint64_t* k_offsets,
+                          const uint8_t* k_k, uint64_t k_tile_base, hq_plan_t plan_v, const uint32_t* v_words,
+                          uint64_t v_n_words, const uint64_t* v_offsets, const uint8_t* v_k, uint64_t v_tile_base,
+                          uint32_t n_heads, uint64_t seq, const float* q, uint32_t qph, float scale, float* out,
+                          void* ws, void* stream) {
+  if (!plan_k || !plan_v) return HQ_ERR_ARG;
+  if (!plan_k->has_alpha || !plan_v->has_alpha) return HQ_ERR_NOALPHA;
+  if (plan_k->lattice != plan_v->lattice || plan_k->seed != plan_v->seed) return HQ_ERR_ARG;
+  if (qph == 0 || qph > 16 || !(scale == scale) || scale - scale != 0.0f) return HQ_ERR_ARG;
+  if (n_heads == 0) return HQ_OK;
+  if (seq == 0 || !k_words || !k_offsets || !k_k || !v_words || !v_offsets || !v_k || !q || !out || !ws)
+    return HQ_ERR_ARG;
+  if (((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+  const uint64_t groups = (seq + hq::kAttnChunks * hq::kChunkTiles - 1) / (hq::kAttnChunks * hq::kChunkTiles);
+  if (n_heads > 65535u || groups > 0x7FFFFFFFull || seq > (1ull << 40)) return HQ_ERR_ARG;
+  hq::AttnArgs a{};
+  a.kw = k_words;
+  a.kn = k_n_words;
+  a.ko = k_offsets;
+  a.kk = k_k;
+  a.ktb = k_tile_base;
+  a.ck = plan_k->c_dec;
+  a.vw = v_words;
+  a.vn = v_n_words;
+  a.vo = v_offsets;
+  a.vk = v_k;
+  a.vtb = v_tile_base;
+  a.cv = plan_v->c_dec;
+  uint32_t sl16[4];
+  fill_common(plan_k, sl16, a.sl32, a.key0, a.key1);
+  a.q = q;
+  a.qph = qph;
+  a.scale = scale;
+  a.seq = seq;
+  a.n_groups = (uint32_t)groups;
+  a.ws = (hq::WsHeader*)ws;
+  a.part = (float*)((char*)ws + sizeof(hq::WsHeader));
+  a.out = out;
+  return dev_err(hq::launch_attention(plan_k->lattice, a, n_heads, (hipStream_t)stream));
+}
+
 hq_status hq_status_sync(void* ws, void* stream) {
   if (!ws) return HQ_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;

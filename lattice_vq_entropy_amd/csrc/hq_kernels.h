@@ -82,7 +82,29 @@ struct GemvArgs {
 
 hipError_t launch_encode(int lat, bool dither, bool bf16, bool len_only, const EncArgs& a, hipStream_t st);
 hipError_t launch_decode(int lat, bool dither, int out, const DecArgs& a, dim3 grid, hipStream_t st);
+// Attention over compressed keys and values (both dithered, one lattice and
+// seed): per work-group one KV head, kAttnQ of its queries and kAttnChunks
+// chunks of 32 keys.
+constexpr uint32_t kAttnChunks = 8;
+constexpr uint32_t kAttnQ = 4;  // queries per work-group
+constexpr uint32_t kAttnPart = 2 + 128;  // per (head, group, query): max, sum, 128 weighted values
+struct AttnArgs {
+  const uint32_t* kw; uint64_t kn; const uint64_t* ko; const uint8_t* kk; uint64_t ktb; float ck;
+  const uint32_t* vw; uint64_t vn; const uint64_t* vo; const uint8_t* vk; uint64_t vtb; float cv;
+  uint32_t sl32[4];
+  uint32_t key0, key1;
+  const float* q;
+  uint32_t qph;
+  float scale;
+  uint64_t seq;
+  uint32_t n_groups;  // work-groups per head
+  float* part;        // [n_heads][n_groups][qph][kAttnPart]
+  float* out;         // [n_heads * qph][128]
+  WsHeader* ws;
+};
+
 hipError_t launch_gemv(int lat, const DecArgs& d, const GemvArgs& g, hipStream_t st);
+hipError_t launch_attention(int lat, const AttnArgs& a, uint32_t n_heads, hipStream_t st);
 hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
                         hipStream_t st);
 

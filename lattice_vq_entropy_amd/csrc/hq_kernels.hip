@@ -735,6 +735,52 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uin
   return true;
 }
 
+// Stream words [w_first, w_end) of a chunk into LDS from the 16-byte
+// boundary below its first record (s_stage[i] = word w_first + i), in uint4
+// loads all issued before the LDS stores; the words from w_end on read as
+// zero.  Every thread of the work-group calls it, after s_off[0..nt] is
+// visible; returns whether the span is sane (work-group uniform).
+__device__ __forceinline__ bool stage_chunk(const uint32_t* words, uint64_t n_words, const uint64_t* s_off,
+                                            uint32_t nt, uint32_t* s_stage, uint64_t& w_first, int tid) {
+  w_first = (s_off[0] >> 5) & ~3ull;
+  const uint64_t w_end = (s_off[nt] + 31) >> 5;
+  const bool span_ok = s_off[nt] >= s_off[0] && (w_end - w_first) <= (uint64_t)kStageWords - 8 && w_end <= n_words;
+  if (span_ok) {
+    const uint32_t n = (uint32_t)(w_end - w_first);
+    const uint32_t n4 = (n + 3) >> 2;
+    uint4 q[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const uint32_t i4 = (uint32_t)tid + 256u * j;
+      q[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (i4 < n4) {
+        const uint64_t wg = w_first + 4ull * i4;
+        if (wg + 4 <= n_words) {
+          q[j] = *reinterpret_cast<const uint4*>(words + wg);
+        } else {
+          q[j].x = words[wg];
+          if (4 * i4 + 1 < n) q[j].y = words[wg + 1];
+          if (4 * i4 + 2 < n) q[j].z = words[wg + 2];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const uint32_t i4 = (uint32_t)tid + 256u * j;
+      if (i4 <= n4) {  // one zero uint4 after the last
+        uint4 v4 = q[j];
+        const uint32_t i = 4 * i4;
+        if (i + 0 >= n) v4.x = 0u;
+        if (i + 1 >= n) v4.y = 0u;
+        if (i + 2 >= n) v4.z = 0u;
+        if (i + 3 >= n) v4.w = 0u;
+        reinterpret_cast<uint4*>(s_stage)[i4] = v4;
+      }
+    }
+  }
+  return span_ok;
+}
+
 template <int L, bool DITHER, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOutScores ? 1 : 8))) void decode_k(DecArgs a) {
   constexpr uint32_t RAW = Lat<L>::raw;
@@ -780,45 +826,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
     }
   }
   __syncthreads();
-  // stream words [w_first, w_end) into LDS from the 16-byte boundary below
-  // w_first (s_stage[i] = word w_first + i), in uint4 loads all issued
-  // before the LDS stores; the words from w_end on read as zero
-  const uint64_t w_first = (s_off[0] >> 5) & ~3ull;
-  const uint64_t w_end = (s_off[nt] + 31) >> 5;
-  const bool span_ok = s_off[nt] >= s_off[0] && (w_end - w_first) <= (uint64_t)kStageWords - 8 && w_end <= a.n_words;
-  if (span_ok) {
-    const uint32_t n = (uint32_t)(w_end - w_first);
-    const uint32_t n4 = (n + 3) >> 2;
-    uint4 q[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const uint32_t i4 = (uint32_t)tid + 256u * j;
-      q[j] = make_uint4(0u, 0u, 0u, 0u);
-      if (i4 < n4) {
-        const uint64_t wg = w_first + 4ull * i4;
-        if (wg + 4 <= a.n_words) {
-          q[j] = *reinterpret_cast<const uint4*>(a.words + wg);
-        } else {
-          q[j].x = a.words[wg];
-          if (4 * i4 + 1 < n) q[j].y = a.words[wg + 1];
-          if (4 * i4 + 2 < n) q[j].z = a.words[wg + 2];
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const uint32_t i4 = (uint32_t)tid + 256u * j;
-      if (i4 <= n4) {  // one zero uint4 after the last
-        uint4 v4 = q[j];
-        const uint32_t i = 4 * i4;
-        if (i + 0 >= n) v4.x = 0u;
-        if (i + 1 >= n) v4.y = 0u;
-        if (i + 2 >= n) v4.z = 0u;
-        if (i + 3 >= n) v4.w = 0u;
-        reinterpret_cast<uint4*>(s_stage)[i4] = v4;
-      }
-    }
-  }
+  uint64_t w_first;
+  const bool span_ok = stage_chunk(a.words, a.n_words, s_off, nt, s_stage, w_first, tid);
   __syncthreads();
 
   // output scale: the lane sign and c_dec, then the signs of D (bf16: on the
@@ -1025,6 +1034,272 @@ hipError_t launch_decode(int lat, bool dither, int out, const DecArgs& a, dim3 g
   HQ_DEC(0) HQ_DEC(1) HQ_DEC(2) HQ_DEC(3)
 #undef HQ_DEC
   return hipErrorInvalidValue;
+}
+
+// ===========================================================================
+// Attention over compressed keys and values
+// ===========================================================================
+// A copy of x that the compiler cannot see through: values derived from it
+// inside a loop are recomputed there instead of being hoisted and held in
+// registers for the whole loop.
+__device__ __forceinline__ int opaque_int(int x) {
+  int y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+
+// Parse the lane's 8 values of chunk slot `slot` from the staged stream and
+// subtract the tile's dither: u_hat in the rotated domain; zeros for a record
+// that does not parse (status 5) or a slot past the end.
+template <int L>
+__device__ __forceinline__ void attn_parse(const uint32_t* s_stage, const uint64_t* s_off, const uint32_t* s_k,
+                                           uint64_t w_first, bool span_ok, bool valid, int slot, uint64_t tile_id,
+                                           uint32_t key0, uint32_t key1, int v, int r, int lane, uint32_t* ust,
+                                           uint8_t* tb, WsHeader* ws, float pv[8]) {
+  constexpr uint32_t RAW = Lat<L>::raw;
+  constexpr uint32_t MAXREC = RAW + 128u * 23u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pv[i] = 0.0f;
+  if (!valid) return;
+  const uint64_t o0 = s_off[slot], o1 = s_off[slot + 1];
+  const uint32_t k = s_k[slot];
+  const uint64_t Lr = o1 - o0;
+  const bool ok = span_ok && k <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + k) && Lr <= MAXREC;
+  bool good = false;
+  if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, ust, tb, pv);
+  if (!good) {
+    if (r == 0) set_status(ws, 5);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = 0.0f;
+  } else {
+    float d[8];
+    dither_lane<L>(key0, key1, tile_id, v, d);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = pv[i] - d[i];
+  }
+}
+
+// Attention, step 1: one KV head (blockIdx.y), up to kAttnQ of its queries
+// (blockIdx.z) and a group of up to kAttnChunks chunks of 32 keys (blockIdx.x).  Phase 1: every key's score
+// s = scale * c_dec_K <H D q, u_hat_K> for the head's queries (rotated once)
+// into LDS.  Then per query the group maximum m, the weights e^(s - m) and
+// their sum l.  Phase 2: the values' u_hat_V weighted and summed in the
+// rotated domain.  Writes per query (m, l, 128 weighted sums).  Every lane
+// holds 8 coordinates of one tile per pass; the sums over tiles are per lane,
+// then over the 4 rows of a wave and the 4 waves, in a fixed order.  The two
+// phases keep only the value sums live across chunks.
+template <int L>
+__global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
+  constexpr uint32_t kKeys = kAttnChunks * kChunkTiles;  // keys per group
+  __shared__ __align__(16) uint32_t s_stage[kStageWords];
+  __shared__ uint64_t s_off[kChunkTiles + 1];
+  __shared__ uint32_t s_k[kChunkTiles];
+  __shared__ uint32_t s_ust[16][16];
+  __shared__ uint4 s_tb[16];
+  __shared__ float s_q[kAttnQ][kTile];
+  __shared__ float s_w[kAttnQ][kKeys];  // scores, then weights
+  __shared__ float s_ml[2][4][kAttnQ];  // per wave: maximum, then sum
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
+  const int v = lane_vector(r);
+  const int pslot = wv * 4 + grp;
+  const FwhtSigns fs = fwht_signs(v);
+  const uint64_t head = blockIdx.y;
+  const uint64_t s_first = (uint64_t)blockIdx.x * kKeys;  // first key of the group
+  const uint32_t nkeys = (uint32_t)(a.seq - s_first < (uint64_t)kKeys ? a.seq - s_first : kKeys);
+  const uint32_t nch = (nkeys + kChunkTiles - 1) / kChunkTiles;
+  const uint32_t q0 = blockIdx.z * kAttnQ;  // first query of this work-group
+  const uint32_t nq = a.qph - q0 < kAttnQ ? a.qph - q0 : kAttnQ;
+
+  if (wv == 0 && grp < (int)nq) {  // rotate the queries: q~ = H D q (row-uniform branch)
+    const float* qp = a.q + ((head * a.qph + q0 + grp) * kTile + 8 * v);
+    const uint32_t sm = lane_signs32(a.sl32, v);
+    float xq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xq[i] = __builtin_bit_cast(float, fbits(qp[i]) ^ ((sm << i) & 0x80000000u));
+    fwht_tile(xq, fs);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_q[grp][8 * v + i] = xq[i] * fs.lane_sign;
+  } else if (wv == 0) {  // unused query rows score zero
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_q[grp][8 * v + i] = 0.0f;
+  }
+  const float kscale = a.ck * a.scale;
+
+  // ---- phase 1: scores
+#pragma unroll 1
+  for (uint32_t cc = 0; cc < nch; ++cc) {
+    const uint64_t s0 = s_first + cc * kChunkTiles;
+    const uint32_t nt = (uint32_t)(a.seq - s0 < (uint64_t)kChunkTiles ? a.seq - s0 : kChunkTiles);
+    const uint64_t t_first = head * a.seq + s0;
+    __syncthreads();  // the previous chunk's span is parsed
+    if (tid <= (int)nt) s_off[tid] = a.ko[t_first + tid];
+    if (tid < (int)nt) s_k[tid] = a.kk[t_first + tid];
+    __syncthreads();
+    uint64_t w_first;
+    const bool span_ok = stage_chunk(a.kw, a.kn, s_off, nt, s_stage, w_first, tid);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int slot = p * 16 + pslot;
+      const bool valid = slot < (int)nt;
+      float pv[8];
+      attn_parse<L>(s_stage, s_off, s_k, w_first, span_ok, valid, slot, a.ktb + t_first + slot, a.key0, a.key1, v, r,
+                    lane, s_ust[pslot], reinterpret_cast<uint8_t*>(&s_tb[pslot]), a.ws, pv);
+#pragma unroll
+      for (int g = 0; g < (int)kAttnQ; ++g) {
+        float d = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d = __builtin_fmaf(s_q[g][8 * v + i], pv[i], d);
+        d = row_sum_f32(d);
+        if (r == 0 && valid) s_w[g][cc * kChunkTiles + slot] = d * kscale;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- group maximum, weights e^(s - m), their sum (thread i: key i)
+  float sg[kAttnQ];
+#pragma unroll
+  for (int g = 0; g < (int)kAttnQ; ++g) {
+    sg[g] = tid < (int)nkeys ? s_w[g][tid] : -__builtin_inff();
+    float mx = sg[g];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) s_ml[0][wv][g] = mx;
+  }
+  __syncthreads();
+  float mgrp[kAttnQ];
+#pragma unroll
+  for (int g = 0; g < (int)kAttnQ; ++g) {
+    mgrp[g] = __builtin_fmaxf(__builtin_fmaxf(s_ml[0][0][g], s_ml[0][1][g]), __builtin_fmaxf(s_ml[0][2][g], s_ml[0][3][g]));
+    const float w = tid < (int)nkeys ? __expf(sg[g] - mgrp[g]) : 0.0f;
+    if (tid < (int)kKeys) s_w[g][tid] = w;
+    float l = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+    if (lane == 0) s_ml[1][wv][g] = l;
+  }
+  // ---- phase 2: weighted value sums
+  float acc[kAttnQ][8];
+#pragma unroll
+  for (int g = 0; g < (int)kAttnQ; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
+#pragma unroll 1
+  for (uint32_t cc = 0; cc < nch; ++cc) {
+    const uint64_t s0 = s_first + cc * kChunkTiles;
+    const uint32_t nt = (uint32_t)(a.seq - s0 < (uint64_t)kChunkTiles ? a.seq - s0 : kChunkTiles);
+    const uint64_t t_first = head * a.seq + s0;
+    __syncthreads();  // weights visible; the previous chunk's span is parsed
+    if (tid <= (int)nt) s_off[tid] = a.vo[t_first + tid];
+    if (tid < (int)nt) s_k[tid] = a.vk[t_first + tid];
+    __syncthreads();
+    uint64_t w_first;
+    const bool span_ok = stage_chunk(a.vw, a.vn, s_off, nt, s_stage, w_first, tid);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int slot = p * 16 + pslot;
+      const bool valid = slot < (int)nt;
+      float pv[8];
+      attn_parse<L>(s_stage, s_off, s_k, w_first, span_ok, valid, slot, a.vtb + t_first + slot, a.key0, a.key1, v, r,
+                    lane, s_ust[pslot], reinterpret_cast<uint8_t*>(&s_tb[pslot]), a.ws, pv);
+      if (valid) {
+#pragma unroll
+        for (int g = 0; g < (int)kAttnQ; ++g) {
+          const float w = s_w[g][cc * kChunkTiles + slot];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[g][i] = __builtin_fmaf(w, pv[i], acc[g][i]);
+        }
+      }
+    }
+  }
+  // sums over the 4 rows of each wave (lanes r, r + 16, r + 32, r + 48 hold the
+  // same coordinates), then over the waves in LDS (the staging area is free)
+  __syncthreads();
+  float* s_red = reinterpret_cast<float*>(s_stage);  // [4 waves][kAttnQ][kTile]
+#pragma unroll
+  for (int g = 0; g < (int)kAttnQ; ++g) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = acc[g][i];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      if (grp == 0) s_red[(wv * kAttnQ + g) * kTile + 8 * v + i] = x;
+    }
+  }
+  __syncthreads();
+  float* part = a.part + ((head * a.n_groups + blockIdx.x) * a.qph + q0) * kAttnPart;
+  for (uint32_t idx = (uint32_t)tid; idx < nq * kTile; idx += 256u) {
+    const uint32_t g = idx / kTile, i = idx % kTile;
+    part[g * kAttnPart + 2 + i] = ((s_red[(0 * kAttnQ + g) * kTile + i] + s_red[(1 * kAttnQ + g) * kTile + i]) +
+                                   s_red[(2 * kAttnQ + g) * kTile + i]) + s_red[(3 * kAttnQ + g) * kTile + i];
+  }
+  if (tid < (int)nq) {
+    float mg = mgrp[0];
+#pragma unroll
+    for (int g = 1; g < (int)kAttnQ; ++g) mg = tid == g ? mgrp[g] : mg;
+    part[tid * kAttnPart] = mg;
+    part[tid * kAttnPart + 1] = ((s_ml[1][0][tid] + s_ml[1][1][tid]) + s_ml[1][2][tid]) + s_ml[1][3][tid];
+  }
+}
+
+// Attention, step 2: one work-group per query combines the groups of its head:
+// M = max m_c, L = sum l_c e^(m_c - M), A = sum acc_c e^(m_c - M) (threads
+// split the groups in two interleaved halves, each in order), then the output
+// out = D H (c_dec_V A / L) by one 16-lane row.
+__global__ __launch_bounds__(256) void attn_combine_k(AttnArgs a) {
+  __shared__ float s_red[4];
+  __shared__ float s_a[2][kTile];
+  __shared__ float s_l[2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t hg = blockIdx.x, head = hg / a.qph, g = hg % a.qph;
+  const uint32_t stride = a.qph * kAttnPart;
+  const float* P = a.part + ((uint64_t)head * a.n_groups * a.qph + g) * kAttnPart;
+  float mx = -__builtin_inff();
+  for (uint32_t c = (uint32_t)tid; c < a.n_groups; c += 256u) mx = __builtin_fmaxf(mx, P[(uint64_t)c * stride]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) s_red[wv] = mx;
+  __syncthreads();
+  const float M = __builtin_fmaxf(__builtin_fmaxf(s_red[0], s_red[1]), __builtin_fmaxf(s_red[2], s_red[3]));
+  const uint32_t i = (uint32_t)tid & 127u, half = (uint32_t)tid >> 7;
+  float acc = 0.0f, ls = 0.0f;
+  for (uint32_t c = half; c < a.n_groups; c += 2u) {
+    const float* pc = P + (uint64_t)c * stride;
+    const float e = __expf(pc[0] - M);
+    acc = __builtin_fmaf(e, pc[2 + i], acc);
+    ls = __builtin_fmaf(e, pc[1], ls);
+  }
+  s_a[half][i] = acc;
+  if (i == 0) s_l[half] = ls;
+  __syncthreads();
+  if (wv == 0) {  // row 0 of wave 0 transforms and stores; the other rows follow along
+    const int r = lane & 15, v = lane_vector(r);
+    const FwhtSigns fs = fwht_signs(v);
+    const float f = a.cv / (s_l[0] + s_l[1]);
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (s_a[0][8 * v + j] + s_a[1][8 * v + j]) * f;
+    fwht_tile(x, fs);
+    const uint32_t sm = lane_signs32(a.sl32, v);
+    if (lane < 16) {
+      float* o = a.out + (uint64_t)hg * kTile + 8 * v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = __builtin_bit_cast(float, fbits(x[j] * fs.lane_sign) ^ ((sm << j) & 0x80000000u));
+    }
+  }
+}
+
+hipError_t launch_attention(int lat, const AttnArgs& a, uint32_t n_heads, hipStream_t st) {
+  const dim3 grid(a.n_groups, n_heads, (a.qph + kAttnQ - 1) / kAttnQ);
+  if (lat == 0) hipLaunchKernelGGL(attn_k<0>, grid, dim3(256), 0, st, a);
+  else if (lat == 1) hipLaunchKernelGGL(attn_k<1>, grid, dim3(256), 0, st, a);
+  else if (lat == 2) hipLaunchKernelGGL(attn_k<2>, grid, dim3(256), 0, st, a);
+  else if (lat == 3) hipLaunchKernelGGL(attn_k<3>, grid, dim3(256), 0, st, a);
+  else return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_combine_k, dim3(n_heads * a.qph), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 // Matrix-vector products, step 1: the vectors' 128-column blocks rotated as

@@ -542,6 +542,23 @@ int orc_dequant_rotated(int lat, uint64_t seed, const uint32_t *words, uint64_t 
   return ORC_OK;
 }
 
+/* The rotated-domain values of n consecutive tiles (tile t has id tile_base +
+ * t), a loop over orc_dequant_rotated; a tile that does not parse is left
+ * zero and its status returned (the first such). */
+int orc_dequant_rotated_many(int lat, uint64_t seed, const uint32_t *words, const uint64_t *offsets,
+                             const uint8_t *k, uint64_t n, int dithered, uint64_t tile_base, float *uh) {
+  int status = ORC_OK;
+  for (uint64_t t = 0; t < n; ++t) {
+    int st = orc_dequant_rotated(lat, seed, words, offsets[t], offsets[t + 1], k[t], dithered, tile_base + t,
+                                 &uh[t * N]);
+    if (st != ORC_OK) {
+      memset(&uh[t * N], 0, sizeof(float) * N);
+      if (status == ORC_OK) status = st;
+    }
+  }
+  return status;
+}
+
 static uint16_t f32_to_bf16_rne(float f) {
   uint32_t b;
   memcpy(&b, &f, 4);

@@ -116,6 +116,8 @@ int orc_decode(int lat, uint64_t seed, float alpha, const uint32_t *words,
 /* Dequantised tile in the rotated domain, fp32: u_hat = embed(codes) - d. */
 int orc_dequant_rotated(int lat, uint64_t seed, const uint32_t *words, uint64_t off,
                         uint64_t end, int k, int dithered, uint64_t tile_id, float uh[128]);
+int orc_dequant_rotated_many(int lat, uint64_t seed, const uint32_t *words, const uint64_t *offsets,
+                             const uint8_t *k, uint64_t n, int dithered, uint64_t tile_base, float *uh);
 
 /* Fused-score reference in fp64: scores[h*qph+g][s] =
  * c_dec * < H D q_{h,g}, u_hat_{h,s} >. */

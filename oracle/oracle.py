@@ -80,6 +80,7 @@ def lib():
             "orc_parse_tile": (_i, [_i, _p, _u64, _u64, _i, _p]),
             "orc_decode": (_i, [_i, _u64, _f, _p, _p, _p, _u64, _i, _u64, _p, _i]),
             "orc_dequant_rotated": (_i, [_i, _u64, _p, _u64, _u64, _i, _i, _u64, _p]),
+            "orc_dequant_rotated_many": (_i, [_i, _u64, _p, _p, _p, _u64, _i, _u64, _p]),
             "orc_kv_scores": (_i, [_i, _u64, _f, _p, _p, _p, _u32, _u64, _u64, _p, _u32, _p]),
             "orc_calibrate": (_i, [_i, _u64, _f, _p, _i, _u64, _i, _u64, _p, _p, _p]),
             "orc_gemv": (_i, [_i, _u64, _f, _p, _p, _p, _u64, _u64, _p, _u32, _p]),
@@ -288,6 +289,18 @@ def dequant_rotated(lat: int, seed: int, words, off: int, end: int, k: int, dith
     st = lib().orc_dequant_rotated(lat, seed, _ptr(words), off, end, k, int(dithered), tile_id,
                                    _ptr(uh))
     return st, uh
+
+
+def dequant_rotated_many(lat: int, seed: int, words, offsets, k, n: int, dithered=False, tile_base=0):
+    """u_hat of tiles 0..n-1 of a stream, [n, 128] fp32 (zeros where a record does not parse)."""
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.uint64)
+    k = np.ascontiguousarray(k, dtype=np.uint8)
+    assert offsets.size >= n + 1 and k.size >= n
+    uh = np.zeros(n * TILE, np.float32)
+    st = lib().orc_dequant_rotated_many(lat, seed, _ptr(words), _ptr(offsets), _ptr(k), n, int(dithered),
+                                        tile_base, _ptr(uh))
+    return st, uh.reshape(n, TILE)
 
 
 def kv_scores(lat: int, seed: int, alpha: float, words, offsets, k, n_heads: int,

@@ -76,3 +76,23 @@ def test_argument_errors_are_synchronous(hq):
     assert L.hq_gemv(q.handle, D, 8, D, D, 2, 256, D, 1, D, D, None) == hq.ERR_NOALPHA
     # workspace: header, the rotated vectors (256-byte aligned), one fp32 per tile and vector
     assert L.hq_gemv_workspace_bytes(3, 256, 2) == 256 + 2048 + 4 * 2 * 3 * 2
+    # attention: both plans with alpha, same lattice and seed; qph 1..16; finite scale; pointers
+    pv = hq.Plan("E8", 4.0, 1).set_alpha(0.5)
+    pk = hq.Plan("E8", 2.0, 1).set_alpha(0.25)
+    args = lambda pk_, pv_, n_heads=2, seq=300, qd=D, qph=4, scale=0.1, ws=D: (
+        pk_.handle, D, 8, D, D, 0, pv_.handle, D, 8, D, D, 600, n_heads, seq, qd, qph, scale, D, ws, None)
+    A = L.hq_kv_attention
+    assert A(*args(pk, hq.Plan("E8", 4.0, 1))) == hq.ERR_NOALPHA
+    assert A(*args(pk, hq.Plan("E8", 4.0, 2).set_alpha(0.5))) == hq.ERR_ARG       # another seed
+    assert A(*args(pk, hq.Plan("D4", 4.0, 1).set_alpha(0.5))) == hq.ERR_ARG       # another lattice
+    assert A(*args(pk, pv, qph=0)) == hq.ERR_ARG
+    assert A(*args(pk, pv, qph=17)) == hq.ERR_ARG
+    assert A(*args(pk, pv, scale=float("inf"))) == hq.ERR_ARG
+    assert A(*args(pk, pv, scale=float("nan"))) == hq.ERR_ARG
+    assert A(*args(pk, pv, qd=None)) == hq.ERR_ARG
+    assert A(*args(pk, pv, seq=0)) == hq.ERR_ARG
+    assert A(*args(pk, pv, ws=C.c_void_p(4104))) == hq.ERR_ARG                      # misaligned workspace
+    assert A(*args(pk, pv, n_heads=0)) == hq.OK                                      # no heads: nothing to do
+    # workspace: header, then per head, group of 256 keys and query the maximum, the sum and 128 values
+    assert L.hq_kv_attention_workspace_bytes(2, 300, 4) == 256 + 4 * 2 * 2 * 4 * 130
+    assert L.hq_kv_attention_workspace_bytes(8, 131072, 4) == 256 + 4 * 8 * 512 * 4 * 130
