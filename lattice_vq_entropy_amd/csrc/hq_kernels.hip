@@ -1080,25 +1080,26 @@ __device__ __forceinline__ void attn_parse(const uint32_t* s_stage, const uint64
 }
 
 // Attention, step 1: one KV head (blockIdx.y), up to kAttnQ of its queries
-// (blockIdx.z) and a group of up to kAttnChunks chunks of 32 keys (blockIdx.x).  Phase 1: every key's score
-// s = scale * c_dec_K <H D q, u_hat_K> for the head's queries (rotated once)
-// into LDS.  Then per query the group maximum m, the weights e^(s - m) and
-// their sum l.  Phase 2: the values' u_hat_V weighted and summed in the
-// rotated domain.  Writes per query (m, l, 128 weighted sums).  Every lane
-// holds 8 coordinates of one tile per pass; the sums over tiles are per lane,
-// then over the 4 rows of a wave and the 4 waves, in a fixed order.  The two
-// phases keep only the value sums live across chunks.
+// (blockIdx.z) and a group of up to kAttnChunks chunks of 32 keys (blockIdx.x).
+// Phase 1: every key's score s = scale * c_dec_K <H D q, u_hat_K> for the
+// queries (rotated once) into LDS.  Then per query the group maximum m, the
+// weights e^(s - m) and their sum l.  Phase 2: the values' u_hat_V weighted
+// and summed in the rotated domain: each pass's 16 parsed vectors go through
+// LDS, and thread (i, half) adds coordinate i of the keys of its half of the
+// pass for every query, so the running sums take 4 registers per thread.
+// Writes per query (m, l, 128 weighted sums).  All sums run in a fixed order.
 template <int L>
 __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   constexpr uint32_t kKeys = kAttnChunks * kChunkTiles;  // keys per group
+  static_assert(kAttnQ == 4, "one float4 of weights per key");
   __shared__ __align__(16) uint32_t s_stage[kStageWords];
   __shared__ uint64_t s_off[kChunkTiles + 1];
   __shared__ uint32_t s_k[kChunkTiles];
   __shared__ uint32_t s_ust[16][16];
   __shared__ uint4 s_tb[16];
-  __shared__ float s_q[kAttnQ][kTile];
-  __shared__ float s_w[kAttnQ][kKeys];  // scores, then weights
-  __shared__ float s_ml[2][4][kAttnQ];  // per wave: maximum, then sum
+  __shared__ __align__(16) float s_qv[16][kTile];  // rotated queries (phase 1), a pass's values (phase 2)
+  __shared__ float4 s_w[kKeys];                    // per key: the queries' scores, then weights
+  __shared__ float s_ml[2][4][kAttnQ];            // per wave: maximum, then sum
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
   const int v = lane_vector(r);
@@ -1110,6 +1111,9 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   const uint32_t nch = (nkeys + kChunkTiles - 1) / kChunkTiles;
   const uint32_t q0 = blockIdx.z * kAttnQ;  // first query of this work-group
   const uint32_t nq = a.qph - q0 < kAttnQ ? a.qph - q0 : kAttnQ;
+  float* s_wf = reinterpret_cast<float*>(s_w);
+  float (*s_q)[kTile] = s_qv;
+  float (*s_v)[kTile] = s_qv;
 
   if (wv == 0 && grp < (int)nq) {  // rotate the queries: q~ = H D q (row-uniform branch)
     const float* qp = a.q + ((head * a.qph + q0 + grp) * kTile + 8 * v);
@@ -1129,6 +1133,10 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   // ---- phase 1: scores
 #pragma unroll 1
   for (uint32_t cc = 0; cc < nch; ++cc) {
+    // lane indices from an opaque copy of the thread index: what the parse
+    // derives from them is recomputed per chunk instead of held across the loop
+    const int tid = opaque_int(threadIdx.x), lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
+    const int v = lane_vector(r), pslot = wv * 4 + grp;
     const uint64_t s0 = s_first + cc * kChunkTiles;
     const uint32_t nt = (uint32_t)(a.seq - s0 < (uint64_t)kChunkTiles ? a.seq - s0 : kChunkTiles);
     const uint64_t t_first = head * a.seq + s0;
@@ -1139,7 +1147,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
     uint64_t w_first;
     const bool span_ok = stage_chunk(a.kw, a.kn, s_off, nt, s_stage, w_first, tid);
     __syncthreads();
-#pragma unroll
+#pragma unroll 1
     for (int p = 0; p < kPasses; ++p) {
       const int slot = p * 16 + pslot;
       const bool valid = slot < (int)nt;
@@ -1152,41 +1160,42 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) d = __builtin_fmaf(s_q[g][8 * v + i], pv[i], d);
         d = row_sum_f32(d);
-        if (r == 0 && valid) s_w[g][cc * kChunkTiles + slot] = d * kscale;
+        if (r == 0 && valid) s_wf[(cc * kChunkTiles + slot) * kAttnQ + g] = d * kscale;
       }
     }
   }
   __syncthreads();
-  // ---- group maximum, weights e^(s - m), their sum (thread i: key i)
-  float sg[kAttnQ];
+  // ---- group maximum, weights e^(s - m) (zero past the last key), their sum (thread i: key i)
+  const float4 s4 = tid < (int)nkeys ? s_w[tid] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const float sg[kAttnQ] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
   for (int g = 0; g < (int)kAttnQ; ++g) {
-    sg[g] = tid < (int)nkeys ? s_w[g][tid] : -__builtin_inff();
-    float mx = sg[g];
+    float mx = tid < (int)nkeys ? sg[g] : -__builtin_inff();
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
     if (lane == 0) s_ml[0][wv][g] = mx;
   }
   __syncthreads();
-  float mgrp[kAttnQ];
+  float mgrp[kAttnQ], wt[kAttnQ];
 #pragma unroll
   for (int g = 0; g < (int)kAttnQ; ++g) {
     mgrp[g] = __builtin_fmaxf(__builtin_fmaxf(s_ml[0][0][g], s_ml[0][1][g]), __builtin_fmaxf(s_ml[0][2][g], s_ml[0][3][g]));
-    const float w = tid < (int)nkeys ? __expf(sg[g] - mgrp[g]) : 0.0f;
-    if (tid < (int)kKeys) s_w[g][tid] = w;
-    float l = w;
+    wt[g] = tid < (int)nkeys ? __expf(sg[g] - mgrp[g]) : 0.0f;
+    float l = wt[g];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
     if (lane == 0) s_ml[1][wv][g] = l;
   }
+  s_w[tid] = make_float4(wt[0], wt[1], wt[2], wt[3]);  // 256 threads, kKeys = 256 keys
+
   // ---- phase 2: weighted value sums
-  float acc[kAttnQ][8];
-#pragma unroll
-  for (int g = 0; g < (int)kAttnQ; ++g)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
+  float acc[kAttnQ] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 1
   for (uint32_t cc = 0; cc < nch; ++cc) {
+    // lane indices from an opaque copy of the thread index: what the parse
+    // derives from them is recomputed per chunk instead of held across the loop
+    const int tid = opaque_int(threadIdx.x), lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
+    const int v = lane_vector(r), pslot = wv * 4 + grp;
     const uint64_t s0 = s_first + cc * kChunkTiles;
     const uint32_t nt = (uint32_t)(a.seq - s0 < (uint64_t)kChunkTiles ? a.seq - s0 : kChunkTiles);
     const uint64_t t_first = head * a.seq + s0;
@@ -1197,43 +1206,44 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
     uint64_t w_first;
     const bool span_ok = stage_chunk(a.vw, a.vn, s_off, nt, s_stage, w_first, tid);
     __syncthreads();
-#pragma unroll
+#pragma unroll 1
     for (int p = 0; p < kPasses; ++p) {
       const int slot = p * 16 + pslot;
       const bool valid = slot < (int)nt;
       float pv[8];
       attn_parse<L>(s_stage, s_off, s_k, w_first, span_ok, valid, slot, a.vtb + t_first + slot, a.key0, a.key1, v, r,
                     lane, s_ust[pslot], reinterpret_cast<uint8_t*>(&s_tb[pslot]), a.ws, pv);
-      if (valid) {
+      float4* vr = reinterpret_cast<float4*>(&s_v[pslot][8 * v]);  // zeros past the last key
+      vr[0] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+      vr[1] = make_float4(pv[4], pv[5], pv[6], pv[7]);
+      __syncthreads();
+      const int ci = tid & (kTile - 1), half = tid >> 7;
 #pragma unroll
-        for (int g = 0; g < (int)kAttnQ; ++g) {
-          const float w = s_w[g][cc * kChunkTiles + slot];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[g][i] = __builtin_fmaf(w, pv[i], acc[g][i]);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int row = half * 8 + j;
+        const float4 w = s_w[cc * kChunkTiles + p * 16 + row];  // zero past the last key
+        const float x = s_v[row][ci];
+        acc[0] = __builtin_fmaf(w.x, x, acc[0]);
+        acc[1] = __builtin_fmaf(w.y, x, acc[1]);
+        acc[2] = __builtin_fmaf(w.z, x, acc[2]);
+        acc[3] = __builtin_fmaf(w.w, x, acc[3]);
       }
+      __syncthreads();  // s_v is rewritten by the next pass
     }
   }
-  // sums over the 4 rows of each wave (lanes r, r + 16, r + 32, r + 48 hold the
-  // same coordinates), then over the waves in LDS (the staging area is free)
-  __syncthreads();
-  float* s_red = reinterpret_cast<float*>(s_stage);  // [4 waves][kAttnQ][kTile]
+  // the two halves' sums (the value staging area is free)
+  const int ci = tid & (kTile - 1), half = tid >> 7;
+  float* s_red = &s_v[0][0];  // [kAttnQ][kTile]
+  if (half == 1) {
 #pragma unroll
-  for (int g = 0; g < (int)kAttnQ; ++g) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float x = acc[g][i];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      if (grp == 0) s_red[(wv * kAttnQ + g) * kTile + 8 * v + i] = x;
-    }
+    for (int g = 0; g < (int)kAttnQ; ++g) s_red[g * kTile + ci] = acc[g];
   }
   __syncthreads();
   float* part = a.part + ((head * a.n_groups + blockIdx.x) * a.qph + q0) * kAttnPart;
-  for (uint32_t idx = (uint32_t)tid; idx < nq * kTile; idx += 256u) {
-    const uint32_t g = idx / kTile, i = idx % kTile;
-    part[g * kAttnPart + 2 + i] = ((s_red[(0 * kAttnQ + g) * kTile + i] + s_red[(1 * kAttnQ + g) * kTile + i]) +
-                                   s_red[(2 * kAttnQ + g) * kTile + i]) + s_red[(3 * kAttnQ + g) * kTile + i];
+  if (half == 0) {
+#pragma unroll
+    for (int g = 0; g < (int)kAttnQ; ++g)
+      if (g < (int)nq) part[g * kAttnPart + 2 + ci] = acc[g] + s_red[g * kTile + ci];
   }
   if (tid < (int)nq) {
     float mg = mgrp[0];
@@ -1244,43 +1254,66 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   }
 }
 
-// Attention, step 2: one work-group per query combines the groups of its head:
-// M = max m_c, L = sum l_c e^(m_c - M), A = sum acc_c e^(m_c - M) (threads
-// split the groups in two interleaved halves, each in order), then the output
-// out = D H (c_dec_V A / L) by one 16-lane row.
-__global__ __launch_bounds__(256) void attn_combine_k(AttnArgs a) {
-  __shared__ float s_red[4];
-  __shared__ float s_a[2][kTile];
-  __shared__ float s_l[2];
+// Attention, step 2: one work-group of 1024 threads per query combines the
+// groups of its head: M = max m_c, L = sum l_c e^(m_c - M), A = sum acc_c
+// e^(m_c - M).  Thread (slice, i) sums coordinate i over the groups c = slice
+// mod 8 in order; the 8 slices are then added as a fixed pairwise tree.  The
+// output out = D H (c_dec_V A / L) is formed by one 16-lane row.
+__global__ __launch_bounds__(1024) void attn_combine_k(AttnArgs a) {
+  __shared__ float s_red[16];
+  __shared__ float s_a[8][kTile];
+  __shared__ float s_l[8];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t hg = blockIdx.x, head = hg / a.qph, g = hg % a.qph;
   const uint32_t stride = a.qph * kAttnPart;
   const float* P = a.part + ((uint64_t)head * a.n_groups * a.qph + g) * kAttnPart;
   float mx = -__builtin_inff();
-  for (uint32_t c = (uint32_t)tid; c < a.n_groups; c += 256u) mx = __builtin_fmaxf(mx, P[(uint64_t)c * stride]);
+  for (uint32_t c = (uint32_t)tid; c < a.n_groups; c += 1024u) mx = __builtin_fmaxf(mx, P[(uint64_t)c * stride]);
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
   if (lane == 0) s_red[wv] = mx;
   __syncthreads();
-  const float M = __builtin_fmaxf(__builtin_fmaxf(s_red[0], s_red[1]), __builtin_fmaxf(s_red[2], s_red[3]));
-  const uint32_t i = (uint32_t)tid & 127u, half = (uint32_t)tid >> 7;
+  float M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) M = __builtin_fmaxf(M, s_red[w]);
+  const uint32_t i = (uint32_t)tid & 127u, slice = (uint32_t)tid >> 7;
   float acc = 0.0f, ls = 0.0f;
-  for (uint32_t c = half; c < a.n_groups; c += 2u) {
-    const float* pc = P + (uint64_t)c * stride;
-    const float e = __expf(pc[0] - M);
-    acc = __builtin_fmaf(e, pc[2 + i], acc);
-    ls = __builtin_fmaf(e, pc[1], ls);
+  constexpr int kB = 16;  // groups whose loads are issued together
+#pragma unroll 1
+  for (uint32_t c0 = slice; c0 < a.n_groups; c0 += 8u * kB) {
+    float gm[kB], gl[kB], gx[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const uint32_t c = c0 + 8u * b;
+      const bool in = c < a.n_groups;
+      const float* pc = P + (uint64_t)(in ? c : a.n_groups - 1u) * stride;  // loads stay in bounds
+      const float m = pc[0], l = pc[1], x = pc[2 + i];
+      gm[b] = in ? m : -__builtin_inff();  // weight e^(-inf) = 0 past the last group
+      gl[b] = in ? l : 0.0f;
+      gx[b] = in ? x : 0.0f;
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const float e = __expf(gm[b] - M);
+      acc = __builtin_fmaf(e, gx[b], acc);
+      ls = __builtin_fmaf(e, gl[b], ls);
+    }
   }
-  s_a[half][i] = acc;
-  if (i == 0) s_l[half] = ls;
+  s_a[slice][i] = acc;
+  if (i == 0) s_l[slice] = ls;
   __syncthreads();
   if (wv == 0) {  // row 0 of wave 0 transforms and stores; the other rows follow along
     const int r = lane & 15, v = lane_vector(r);
     const FwhtSigns fs = fwht_signs(v);
-    const float f = a.cv / (s_l[0] + s_l[1]);
+    const float l = ((s_l[0] + s_l[1]) + (s_l[2] + s_l[3])) + ((s_l[4] + s_l[5]) + (s_l[6] + s_l[7]));
+    const float f = a.cv / l;
     float x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (s_a[0][8 * v + j] + s_a[1][8 * v + j]) * f;
+    for (int j = 0; j < 8; ++j) {
+      const int c = 8 * v + j;
+      x[j] = (((s_a[0][c] + s_a[1][c]) + (s_a[2][c] + s_a[3][c])) + ((s_a[4][c] + s_a[5][c]) + (s_a[6][c] + s_a[7][c]))) *
+             f;
+    }
     fwht_tile(x, fs);
     const uint32_t sm = lane_signs32(a.sl32, v);
     if (lane < 16) {
@@ -1298,7 +1331,7 @@ hipError_t launch_attention(int lat, const AttnArgs& a, uint32_t n_heads, hipStr
   else if (lat == 2) hipLaunchKernelGGL(attn_k<2>, grid, dim3(256), 0, st, a);
   else if (lat == 3) hipLaunchKernelGGL(attn_k<3>, grid, dim3(256), 0, st, a);
   else return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_combine_k, dim3(n_heads * a.qph), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(attn_combine_k, dim3(n_heads * a.qph), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
