@@ -109,6 +109,22 @@ hq_status hq_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_ti
                     uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k,
                     void* ws, void* stream);
 
+/* Append n_tiles tiles of x to a stream that holds n_prev tiles: the new
+ * records start at bit offsets[n_prev] (read on the device, so the call stays
+ * asynchronous), the existing bits below it are kept, and offsets[n_prev ..
+ * n_prev + n_tiles] and k[n_prev .. n_prev + n_tiles - 1] are written.  The
+ * result is the stream that one hq_encode of both inputs, concatenated, would
+ * give [Methodology 3: records are independent and abut].  cap_words counts
+ * from word 0.  n_prev = 0 is hq_encode.  hq_kv_append: the dithered variant;
+ * tile_base is the tile id of the first appended tile (for a continued KV
+ * stream, the previous tile_base + n_prev). */
+hq_status hq_append(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint32_t* words,
+                    uint64_t cap_words, uint64_t* offsets, uint8_t* k, uint64_t n_prev, void* ws,
+                    void* stream);
+hq_status hq_kv_append(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles,
+                       uint64_t tile_base, uint32_t* words, uint64_t cap_words, uint64_t* offsets,
+                       uint8_t* k, uint64_t n_prev, void* ws, void* stream);
+
 /* Decode n_tiles tiles into y (fp32 or bf16).  n_words bounds the reads of
  * words. */
 hq_status hq_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words,

@@ -48,6 +48,8 @@ _SIGNATURES = {
     "hq_kv_scores": (_i, [_p, _p, _u64, _p, _p, _u32, _u64, _u64, _p, _u32, _p, _p, _p]),
     "hq_gemv_workspace_bytes": (C.c_size_t, [_u64, _u64, _u32]),
     "hq_gemv": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _u32, _p, _p, _p]),
+    "hq_append": (_i, [_p, _p, _i, _u64, _p, _u64, _p, _p, _u64, _p, _p]),
+    "hq_kv_append": (_i, [_p, _p, _i, _u64, _u64, _p, _u64, _p, _p, _u64, _p, _p]),
     "hq_kv_attention_workspace_bytes": (C.c_size_t, [_u32, _u64, _u32]),
     "hq_kv_attention": (_i, [_p, _p, _u64, _p, _p, _u64, _p, _p, _u64, _p, _p, _u64, _u32, _u64, _p, _u32, C.c_float,
                              _p, _p, _p]),
@@ -172,9 +174,11 @@ class Plan:
 class Encoded:
     """Bitstream, per-tile bit offsets and Rice parameters of one encode."""
 
-    def __init__(self, words, offsets, k, n_tiles, tile_base=0, dithered=False):
+    def __init__(self, words, offsets, k, n_tiles, tile_base=0, dithered=False, storage=None):
         self.words, self.offsets, self.k = words, offsets, k
         self.n_tiles, self.tile_base, self.dithered = n_tiles, tile_base, dithered
+        # the whole buffers (offsets and k may have room for appended tiles)
+        self.storage = storage if storage is not None else (words, offsets, k)
 
     def total_bits(self) -> int:
         return int(self.offsets[-1].item())
@@ -203,7 +207,25 @@ def encode(plan: Plan, x: torch.Tensor, ws: torch.Tensor, out=None, dithered: bo
         rc = lib().hq_encode(plan.handle, _dptr(x), _dtype_code(x), n, _dptr(words), cap, _dptr(offsets),
                              _dptr(k), _dptr(ws), _stream(stream))
     _check(rc, "encode")
-    return Encoded(words, offsets, k, n, tile_base, dithered)
+    return Encoded(words, offsets[:n + 1], k[:max(n, 1)], n, tile_base, dithered, storage=(words, offsets, k))
+
+
+def append(plan: Plan, enc: Encoded, x: torch.Tensor, ws: torch.Tensor, stream=None) -> Encoded:
+    """hq_append / hq_kv_append: the tiles of enc followed by those of x, in enc's buffers
+    (allocate them with room, e.g. alloc_stream(plan, capacity_tiles), and encode into them)."""
+    n, n_prev = _n_tiles(x), enc.n_tiles
+    words, offsets, k = enc.storage
+    if offsets.numel() < n_prev + n + 1 or k.numel() < n_prev + n:
+        raise ValueError("the stream's buffers have no room for the appended tiles")
+    if enc.dithered:
+        rc = lib().hq_kv_append(plan.handle, _dptr(x), _dtype_code(x), n, enc.tile_base + n_prev, _dptr(words),
+                                words.numel(), _dptr(offsets), _dptr(k), n_prev, _dptr(ws), _stream(stream))
+    else:
+        rc = lib().hq_append(plan.handle, _dptr(x), _dtype_code(x), n, _dptr(words), words.numel(), _dptr(offsets),
+                             _dptr(k), n_prev, _dptr(ws), _stream(stream))
+    _check(rc, "append")
+    m = n_prev + n
+    return Encoded(words, offsets[:m + 1], k[:max(m, 1)], m, enc.tile_base, enc.dithered, storage=enc.storage)
 
 
 def decode(plan: Plan, enc: Encoded, ws: torch.Tensor, out: torch.Tensor | None = None,

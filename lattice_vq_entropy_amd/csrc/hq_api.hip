@@ -76,7 +76,7 @@ void fill_common(const hq_plan_s* p, uint32_t sl16[4], uint32_t sl32[4], uint32_
 
 hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, bool dither,
                       uint64_t tile_base, uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k,
-                      void* ws, void* stream, bool len_only) {
+                      void* ws, void* stream, bool len_only, bool append = false) {
   if (!plan) return HQ_ERR_ARG;
   if (!plan->has_alpha) return HQ_ERR_NOALPHA;
   if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_ARG;
@@ -84,7 +84,7 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   hipStream_t st = (hipStream_t)stream;
   if (!len_only && !offsets) return HQ_ERR_ARG;
   if (n_tiles == 0) {
-    if (len_only) return HQ_OK;
+    if (len_only || append) return HQ_OK;
     return dev_err(hipMemsetAsync(offsets, 0, sizeof(uint64_t), st));
   }
   if (!x) return HQ_ERR_ARG;
@@ -112,6 +112,7 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   a.tailw = (uint32_t*)((char*)ws + lay.tailw);
   a.stage = (uint32_t*)((char*)ws + lay.stage);
   a.partials = (unsigned long long*)a.E;
+  a.base = append ? offsets : nullptr;
   return dev_err(hq::launch_encode(plan->lattice, dither, dtype == HQ_BF16, len_only, a, st));
 }
 
@@ -220,6 +221,21 @@ hq_status hq_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_ti
 hq_status hq_kv_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint64_t tile_base,
                        uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k, void* ws, void* stream) {
   return encode_impl(plan, x, dtype, n_tiles, true, tile_base, words, cap_words, offsets, k, ws, stream, false);
+}
+
+hq_status hq_append(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint32_t* words,
+                    uint64_t cap_words, uint64_t* offsets, uint8_t* k, uint64_t n_prev, void* ws, void* stream) {
+  if (!offsets || !k) return HQ_ERR_ARG;
+  return encode_impl(plan, x, dtype, n_tiles, false, 0, words, cap_words, offsets + n_prev, k + n_prev, ws, stream,
+                     false, n_prev > 0);
+}
+
+hq_status hq_kv_append(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint64_t tile_base,
+                       uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k, uint64_t n_prev, void* ws,
+                       void* stream) {
+  if (!offsets || !k) return HQ_ERR_ARG;
+  return encode_impl(plan, x, dtype, n_tiles, true, tile_base, words, cap_words, offsets + n_prev, k + n_prev, ws,
+                     stream, false, n_prev > 0);
 }
 
 hq_status hq_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets,

@@ -30,6 +30,7 @@ struct EncArgs {
   uint32_t* tailw;   // last 32 stream bits of each chunk
   uint32_t* stage;   // kSlotWords staging words per chunk
   unsigned long long* partials;  // length-only pass: bits per chunk
+  const uint64_t* base;  // append: the existing stream's end bit (device), else null
 };
 
 struct PlaceArgs {
@@ -44,6 +45,7 @@ struct PlaceArgs {
   uint32_t* words;
   uint64_t cap_words;
   uint64_t* offsets;
+  const uint64_t* base;  // append: the existing stream's end bit (device), else null
 };
 
 struct DecArgs {

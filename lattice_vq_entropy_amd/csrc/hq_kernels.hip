@@ -344,8 +344,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 8 : 
 // 64 entries, E to an even count.  Up to kScanRegs uint4 per thread (n up to
 // 32 Ki chunks); longer inputs read the rest of the strip twice.
 constexpr uint32_t kScanRegs = 8;
-__global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, uint64_t* E, uint64_t cap_words,
-                                               WsHeader* ws) {
+__global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, uint64_t* E) {
   __shared__ uint64_t s_w[16];
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t per = (n + 4095u) / 4096u;  // uint4 per thread
@@ -420,18 +419,17 @@ __global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, 
     const uint32_t i = lo + 4u * j;
     if (i < n) put4(i, *reinterpret_cast<const uint4*>(agg + i));
   }
-  if (lo < n && lo + 4u * per >= n) {
-    E[n] = run;
-    if ((run + 31) / 32 > cap_words) atomicOr(&ws->status, 1u << 4);
-  }
+  if (lo < n && lo + 4u * per >= n) E[n] = run;
 }
 
 // Encode, step 3 of 3: one chunk per work-group.  The chunk's staged bits go
-// to stream bits [E[c], E[c+1]) with a funnel shift, four words per thread
-// (one uint4 staging load, issued with the offset loads before they arrive);
-// the word shared with the predecessor takes the predecessor's last 32 bits,
-// recorded by step 1, so every stream word is written exactly once.  Also the
-// per-tile offsets.  SELF_SCAN (inputs of at most kSelfScanChunks chunks):
+// to stream bits [B + E[c], B + E[c+1]) with a funnel shift, four words per
+// thread (one uint4 staging load, issued with the offset loads before they
+// arrive); the word shared with the predecessor takes the predecessor's last
+// 32 bits, recorded by step 1, so every stream word is written exactly once.
+// B is 0, or when appending to an existing stream its end bit: then the first
+// chunk's first word keeps the existing bits below B.  Also the per-tile
+// offsets, and the capacity check.  SELF_SCAN (inputs of at most kSelfScanChunks chunks):
 // step 2 is skipped and every work-group sums the bit counts of the chunks
 // before its own (all reads of one small array that the L2 serves), which
 // costs less than a launch of the scan.
@@ -462,7 +460,11 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   const bool spec = 4u * tid < kSpecWords;
   const uint4 c0 = spec ? *reinterpret_cast<const uint4*>(st + 4u * tid) : make_uint4(0u, 0u, 0u, 0u);
   uint32_t p0 = (spec && tid) ? st[4u * tid - 1u] : 0u;
-  const uint32_t tw = chunk > 0 ? a.tailw[chunk - 1] : 0u;  // work-group uniform
+  const uint64_t B = a.base ? *a.base : 0ull;  // work-group uniform
+  uint32_t tw;                                 // work-group uniform
+  if (chunk > 0) tw = a.tailw[chunk - 1];
+  else if ((B & 31) && (B >> 5) < a.cap_words) tw = a.words[B >> 5] << (32u - (uint32_t)(B & 31));  // bits below B
+  else tw = 0u;  // (B past the capacity fails the capacity check below)
   if (tid == 0) p0 = tw;
   uint64_t E, E1;
   if constexpr (SELF_SCAN) {
@@ -487,13 +489,13 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
     const uint32_t wsum = wave_sum_u32(part);
     if ((tid & 63) == 0) s_part[tid >> 6] = wsum;
     __syncthreads();
-    E = (uint64_t)s_part[0] + s_part[1] + s_part[2] + s_part[3];  // at most 8192 * 94720 bits
+    E = B + s_part[0] + s_part[1] + s_part[2] + s_part[3];  // the sum: at most 8192 * 94720 bits
     E1 = E + A;
-    if (tid == 0 && chunk == a.n_chunks - 1 && (E1 + 31) / 32 > a.cap_words) atomicOr(&a.ws->status, 1u << 4);
   } else {
-    E = a.E[chunk];
-    E1 = a.E[chunk + 1];
+    E = B + a.E[chunk];
+    E1 = B + a.E[chunk + 1];
   }
+  if (tid == 0 && chunk == a.n_chunks - 1 && (E1 + 31) / 32 > a.cap_words) atomicOr(&a.ws->status, 1u << 4);
   const uint64_t t = (uint64_t)chunk * kChunkTiles + tid;
   const uint32_t lc = (tid < kChunkTiles && t < a.n_tiles) ? a.loc[t] : 0u;
   if (tid < kChunkTiles && t < a.n_tiles) {
@@ -985,7 +987,7 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   hipLaunchKernelGGL((encode_k<L, DITHER, BF16, false>), grid, dim3(256), 0, st, a);
   const bool self_scan = a.n_chunks <= kSelfScanChunks;
   if (!self_scan)
-    hipLaunchKernelGGL(scan_k, dim3(1), dim3(1024), 0, st, (const uint32_t*)a.agg, a.n_chunks, a.E, a.cap_words, a.ws);
+    hipLaunchKernelGGL(scan_k, dim3(1), dim3(1024), 0, st, (const uint32_t*)a.agg, a.n_chunks, a.E);
   PlaceArgs pa;
   pa.agg = a.agg;
   pa.ws = a.ws;
@@ -998,6 +1000,7 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   pa.words = a.words;
   pa.cap_words = a.cap_words;
   pa.offsets = a.offsets;
+  pa.base = a.base;
   if (self_scan)
     hipLaunchKernelGGL(place_k<true>, grid, dim3(256), 0, st, pa);
   else

@@ -62,6 +62,10 @@ def test_argument_errors_are_synchronous(hq):
     assert L.hq_encode(p.handle, None, 5, 4, None, 0, None, None, C.c_void_p(256), None) == hq.ERR_ARG
     assert L.hq_decode(p.handle, None, 0, None, None, 4, None, 0, None, None) == hq.ERR_ARG
     assert L.hq_kv_scores(p.handle, None, 0, None, None, 1, 1, 0, None, 17, None, None, None) == hq.ERR_ARG
+    D = C.c_void_p(4096)
+    assert L.hq_append(p.handle, D, 1, 4, D, 8, None, D, 2, D, None) == hq.ERR_ARG       # no offsets
+    assert L.hq_kv_append(p.handle, D, 1, 4, 0, D, 8, D, None, 2, D, None) == hq.ERR_ARG  # no k
+    assert L.hq_append(p.handle, D, 1, 0, D, 8, D, D, 2, D, None) == hq.OK              # nothing to append
     assert L.hq_status_sync(None, None) == hq.ERR_ARG
     assert hq.status_str(hq.ERR_CORRUPT) == "corrupt stream"
     # matrix-vector products: shape and batch limits, null and misaligned pointers
