@@ -194,6 +194,46 @@ hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_
                           uint32_t n_heads, uint64_t seq, const float* q, uint32_t qph, float scale,
                           float* out, void* ws, void* stream);
 
+/* Compact side information [Methodology 3: the offsets and Rice parameters
+ * are the side information of the stream]: per chunk of 32 tiles one 96-byte
+ * record, 3 bytes per tile instead of 9:
+ *   bytes [0, 8)   uint64 bit offset of the chunk's first record
+ *   bytes [8, 72)  uint16 end of the chunk's record j minus that offset
+ *   bytes [72, 92) the chunk's 32 Rice parameters, 5 bits each, LSB first
+ *   bytes [92, 96) zero
+ * Entries past the last tile are zero.  side: hq_side_bytes(n_tiles) bytes,
+ * 16-byte aligned, device memory.  hq_side_pack reads offsets[0..n_tiles]
+ * and k; a chunk whose records span 2^16 bits or more (about 16 bits per
+ * scalar) cannot be packed and sets HQ_ERR_CAPACITY in ws.  hq_side_unpack
+ * writes offsets[0..n_tiles] and k[0..n_tiles-1].  Both asynchronous. */
+size_t hq_side_bytes(uint64_t n_tiles);
+hq_status hq_side_pack(const uint64_t* offsets, const uint8_t* k, uint64_t n_tiles, void* side,
+                       void* ws, void* stream);
+hq_status hq_side_unpack(const void* side, uint64_t n_tiles, uint64_t* offsets, uint8_t* k,
+                         void* stream);
+
+/* Container header: 64 bytes in HOST memory that make a stream
+ * self-describing (the plan, the KV tile base, sizes), little-endian:
+ *   0 magic "HQS1" | 4 version u16 = 1 | 6 lattice u8 | 7 flags u8 (bit 0
+ *   dithered, bit 1 compact side information) | 8 tile u32 = 128 | 12 alpha
+ *   f32 | 16 target bps f32 | 20 zero u32 | 24 seed u64 | 32 tile_base u64 |
+ *   40 n_tiles u64 | 48 total bits u64 | 56 zero u32 | 60 CRC-32 (IEEE 802.3)
+ *   of bytes 0..59.
+ * hq_header_read returns HQ_ERR_CORRUPT for a wrong magic, version, checksum
+ * or field; hq_plan_from_header makes the plan (alpha set) that decodes the
+ * stream. */
+#define HQ_HEADER_BYTES 64
+typedef struct {
+  hq_lattice lattice;
+  int dithered, compact_side, tile;
+  float alpha, bps;
+  uint64_t seed, tile_base, n_tiles, total_bits;
+} hq_header_info;
+hq_status hq_header_write(hq_plan_t plan, int dithered, uint64_t tile_base, uint64_t n_tiles,
+                          uint64_t total_bits, int compact_side, void* out);
+hq_status hq_header_read(const void* in, hq_header_info* info);
+hq_status hq_plan_from_header(const void* in, hq_plan_t* out);
+
 /* Synchronise stream, return the lowest data error recorded in ws since the
  * last call, and clear it. */
 hq_status hq_status_sync(void* ws, void* stream);

@@ -53,9 +53,24 @@ _SIGNATURES = {
     "hq_kv_attention_workspace_bytes": (C.c_size_t, [_u32, _u64, _u32]),
     "hq_kv_attention": (_i, [_p, _p, _u64, _p, _p, _u64, _p, _p, _u64, _p, _p, _u64, _u32, _u64, _p, _u32, C.c_float,
                              _p, _p, _p]),
+    "hq_side_bytes": (C.c_size_t, [_u64]),
+    "hq_side_pack": (_i, [_p, _p, _u64, _p, _p, _p]),
+    "hq_side_unpack": (_i, [_p, _u64, _p, _p, _p]),
+    "hq_header_write": (_i, [_p, _i, _u64, _u64, _u64, _i, _p]),
+    "hq_header_read": (_i, [_p, _p]),
+    "hq_plan_from_header": (_i, [_p, C.POINTER(_p)]),
     "hq_status_sync": (_i, [_p, _p]),
     "hq_status_str": (C.c_char_p, [_i]),
 }
+
+HEADER_BYTES = 64
+
+
+class HeaderInfo(C.Structure):
+    """hq_header_info."""
+    _fields_ = [("lattice", C.c_int), ("dithered", C.c_int), ("compact_side", C.c_int), ("tile", C.c_int),
+                ("alpha", C.c_float), ("bps", C.c_float), ("seed", C.c_uint64), ("tile_base", C.c_uint64),
+                ("n_tiles", C.c_uint64), ("total_bits", C.c_uint64)]
 
 
 def header_functions() -> list[str]:
@@ -130,6 +145,18 @@ class Plan:
         _check(lib().hq_plan(lat, tile, float(bps), int(seed), C.byref(h)), "hq_plan")
         self._h = h
         self.lattice, self.bps, self.seed = lat, float(bps), int(seed)
+
+    @classmethod
+    def from_header(cls, header: bytes) -> "Plan":
+        """hq_plan_from_header: the plan recorded in a 64-byte container header."""
+        info = header_read(header)
+        buf = C.create_string_buffer(bytes(header[:HEADER_BYTES]), HEADER_BYTES)
+        h = C.c_void_p(0)
+        _check(lib().hq_plan_from_header(buf, C.byref(h)), "hq_plan_from_header")
+        self = cls.__new__(cls)
+        self._h = h
+        self.lattice, self.bps, self.seed = int(info.lattice), float(info.bps), int(info.seed)
+        return self
 
     def __del__(self):
         if getattr(self, "_h", None) and _lib is not None:
@@ -303,6 +330,87 @@ def kv_attention(plan_k: Plan, enc_k: Encoded, plan_v: Plan, enc_v: Encoded, n_h
                                n_heads, seq, _dptr(q), qph, scale, _dptr(o), _dptr(ws), _stream(stream))
     _check(rc, "kv_attention")
     return o
+
+
+def side_pack(enc: Encoded, ws: torch.Tensor, stream=None) -> torch.Tensor:
+    """hq_side_pack: the compact side information of enc (uint8, 96 bytes per 32 tiles)."""
+    n = enc.n_tiles
+    side = torch.empty(max(int(lib().hq_side_bytes(n)), 16), dtype=torch.uint8, device=enc.words.device)
+    _check(lib().hq_side_pack(_dptr(enc.offsets), _dptr(enc.k), n, _dptr(side), _dptr(ws), _stream(stream)),
+           "side_pack")
+    return side
+
+
+def side_unpack(side: torch.Tensor, n_tiles: int, stream=None):
+    """hq_side_unpack: (offsets int64 [n+1], k uint8 [n]) from compact side information."""
+    offsets = torch.empty(n_tiles + 1, dtype=torch.int64, device=side.device)
+    k = torch.empty(max(n_tiles, 1), dtype=torch.uint8, device=side.device)
+    _check(lib().hq_side_unpack(_dptr(side), n_tiles, _dptr(offsets), _dptr(k), _stream(stream)), "side_unpack")
+    return offsets, k
+
+
+def header_write(plan: Plan, enc: Encoded, compact_side: bool = True) -> bytes:
+    """hq_header_write for enc (synchronises to read its total bit count)."""
+    buf = C.create_string_buffer(HEADER_BYTES)
+    _check(lib().hq_header_write(plan.handle, int(enc.dithered), enc.tile_base, enc.n_tiles, enc.total_bits(),
+                                 int(compact_side), buf), "header_write")
+    return buf.raw
+
+
+def header_read(header: bytes) -> HeaderInfo:
+    if len(header) < HEADER_BYTES:
+        raise ValueError("a container header is 64 bytes")
+    info = HeaderInfo()
+    buf = C.create_string_buffer(bytes(header[:HEADER_BYTES]), HEADER_BYTES)
+    _check(lib().hq_header_read(buf, C.byref(info)), "header_read")
+    return info
+
+
+def save(plan: Plan, enc: Encoded, ws: torch.Tensor, compact_side: bool = True) -> bytes:
+    """The stream as one self-describing byte string: the 64-byte header, the
+    side information (compact, or uint64 offsets then uint8 k padded to 8
+    bytes), then the used stream words."""
+    head = header_write(plan, enc, compact_side)
+    if compact_side:
+        side = side_pack(enc, ws)
+        check(ws)
+        side_b = side[: int(lib().hq_side_bytes(enc.n_tiles))].cpu().numpy().tobytes()
+    else:
+        n = enc.n_tiles
+        kb = enc.k[:n].cpu().numpy().tobytes()
+        side_b = enc.offsets.cpu().numpy().tobytes() + kb + bytes(-len(kb) % 8)
+    words = enc.words[: enc.used_words()].cpu().numpy().tobytes()
+    return head + side_b + words
+
+
+def load(data: bytes, device="cuda", extra_tiles: int = 0):
+    """(plan, Encoded) from save()'s bytes; extra_tiles leaves room to append."""
+    import numpy as np
+    info = header_read(data)
+    plan = Plan.from_header(data)
+    n, total = int(info.n_tiles), int(info.total_bits)
+    pos = HEADER_BYTES
+    words = torch.zeros(max(plan.bound_words(n + extra_tiles), 1), dtype=torch.int32, device=device)
+    offsets = torch.empty(n + extra_tiles + 1, dtype=torch.int64, device=device)
+    k = torch.empty(max(n + extra_tiles, 1), dtype=torch.uint8, device=device)
+    if info.compact_side:
+        nb = int(lib().hq_side_bytes(n))
+        side = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
+        side[:nb].copy_(torch.from_numpy(np.frombuffer(data, np.uint8, nb, pos).copy()))
+        o, kk = side_unpack(side, n)
+        offsets[: n + 1].copy_(o)
+        k[:n].copy_(kk[:n])
+        pos += nb
+    else:
+        offsets[: n + 1].copy_(torch.from_numpy(np.frombuffer(data, np.int64, n + 1, pos).copy()))
+        pos += 8 * (n + 1)
+        k[:n].copy_(torch.from_numpy(np.frombuffer(data, np.uint8, n, pos).copy()))
+        pos += n + (-n % 8)
+    nw = (total + 31) // 32
+    words[:nw].copy_(torch.from_numpy(np.frombuffer(data, np.int32, nw, pos).copy()))
+    enc = Encoded(words, offsets[: n + 1], k[: max(n, 1)], n, int(info.tile_base), bool(info.dithered),
+                  storage=(words, offsets, k))
+    return plan, enc
 
 
 def status_sync(ws: torch.Tensor, stream=None) -> int:

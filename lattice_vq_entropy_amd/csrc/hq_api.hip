@@ -165,6 +165,41 @@ hq_status rate_at(hq_plan_s* p, float a, const void* x, hq_dtype dtype, uint64_t
   return HQ_OK;
 }
 
+// Container header fields, little-endian whatever the host.
+constexpr uint32_t kHeaderMagic = 0x31535148u;  // "HQS1"
+constexpr uint32_t kHeaderVersion = 1;
+
+void put_le(uint8_t* p, int n, uint64_t v) {
+  for (int i = 0; i < n; ++i) p[i] = (uint8_t)(v >> (8 * i));
+}
+
+uint64_t get_le(const uint8_t* p, int n) {
+  uint64_t v = 0;
+  for (int i = 0; i < n; ++i) v |= (uint64_t)p[i] << (8 * i);
+  return v;
+}
+
+// CRC-32 of IEEE 802.3 (reflected polynomial 0xEDB88320, initial value and
+// final xor 0xFFFFFFFF), one 256-entry table built on first use.
+struct CrcTable {
+  uint32_t t[256];
+  CrcTable() {
+    for (uint32_t i = 0; i < 256; ++i) {
+      uint32_t c = i;
+      for (int b = 0; b < 8; ++b) c = (c & 1u) ? 0xEDB88320u ^ (c >> 1) : c >> 1;
+      t[i] = c;
+    }
+  }
+};
+
+uint32_t crc32_ieee(const uint8_t* p, size_t n) {
+  static const CrcTable tab;  // initialised once, thread-safely
+  const uint32_t* table = tab.t;
+  uint32_t c = 0xFFFFFFFFu;
+  for (size_t i = 0; i < n; ++i) c = table[(c ^ p[i]) & 0xFFu] ^ (c >> 8);
+  return c ^ 0xFFFFFFFFu;
+}
+
 }  // namespace
 
 extern "C" {
@@ -367,6 +402,85 @@ hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_
   a.part = (float*)((char*)ws + sizeof(hq::WsHeader));
   a.out = out;
   return dev_err(hq::launch_attention(plan_k->lattice, a, n_heads, (hipStream_t)stream));
+}
+
+size_t hq_side_bytes(uint64_t n_tiles) { return (size_t)(96ull * ((n_tiles + 31) / 32)); }
+
+hq_status hq_side_pack(const uint64_t* offsets, const uint8_t* k, uint64_t n_tiles, void* side, void* ws,
+                       void* stream) {
+  if (n_tiles == 0) return HQ_OK;
+  if (!offsets || !k || !side || !ws) return HQ_ERR_ARG;
+  if (((uintptr_t)side & 15u) != 0 || ((uintptr_t)offsets & 7u) != 0) return HQ_ERR_ARG;
+  if ((n_tiles + 255) / 256 > 0x7FFFFFFFull) return HQ_ERR_ARG;
+  return dev_err(hq::launch_side(true, offsets, k, nullptr, n_tiles, (uint8_t*)side, nullptr, nullptr,
+                                 (hq::WsHeader*)ws, (hipStream_t)stream));
+}
+
+hq_status hq_side_unpack(const void* side, uint64_t n_tiles, uint64_t* offsets, uint8_t* k, void* stream) {
+  if (!offsets) return HQ_ERR_ARG;
+  if (n_tiles == 0) return dev_err(hipMemsetAsync(offsets, 0, sizeof(uint64_t), (hipStream_t)stream));
+  if (!side || !k) return HQ_ERR_ARG;
+  if (((uintptr_t)side & 15u) != 0 || ((uintptr_t)offsets & 7u) != 0) return HQ_ERR_ARG;
+  if ((n_tiles + 255) / 256 > 0x7FFFFFFFull) return HQ_ERR_ARG;
+  return dev_err(hq::launch_side(false, nullptr, nullptr, (const uint8_t*)side, n_tiles, nullptr, offsets, k, nullptr,
+                                 (hipStream_t)stream));
+}
+
+hq_status hq_header_write(hq_plan_t plan, int dithered, uint64_t tile_base, uint64_t n_tiles, uint64_t total_bits,
+                          int compact_side, void* out) {
+  if (!plan || !out) return HQ_ERR_ARG;
+  if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  uint8_t h[HQ_HEADER_BYTES] = {};
+  put_le(h + 0, 4, kHeaderMagic);
+  put_le(h + 4, 2, kHeaderVersion);
+  h[6] = (uint8_t)plan->lattice;
+  h[7] = (uint8_t)((dithered ? 1u : 0u) | (compact_side ? 2u : 0u));
+  put_le(h + 8, 4, 128u);
+  uint32_t ab, bb;
+  std::memcpy(&ab, &plan->alpha, 4);
+  std::memcpy(&bb, &plan->bps, 4);
+  put_le(h + 12, 4, ab);
+  put_le(h + 16, 4, bb);
+  put_le(h + 24, 8, plan->seed);
+  put_le(h + 32, 8, tile_base);
+  put_le(h + 40, 8, n_tiles);
+  put_le(h + 48, 8, total_bits);
+  put_le(h + 60, 4, crc32_ieee(h, 60));
+  std::memcpy(out, h, HQ_HEADER_BYTES);
+  return HQ_OK;
+}
+
+hq_status hq_header_read(const void* in, hq_header_info* info) {
+  if (!in || !info) return HQ_ERR_ARG;
+  const uint8_t* h = (const uint8_t*)in;
+  if (get_le(h + 0, 4) != kHeaderMagic || get_le(h + 4, 2) != kHeaderVersion) return HQ_ERR_CORRUPT;
+  if (get_le(h + 60, 4) != crc32_ieee(h, 60)) return HQ_ERR_CORRUPT;
+  if (!lattice_ok(h[6]) || (h[7] & ~3u) != 0 || get_le(h + 8, 4) != 128u) return HQ_ERR_CORRUPT;
+  const uint32_t ab = (uint32_t)get_le(h + 12, 4), bb = (uint32_t)get_le(h + 16, 4);
+  std::memcpy(&info->alpha, &ab, 4);
+  std::memcpy(&info->bps, &bb, 4);
+  if (!(info->alpha > 0.0f) || !std::isfinite(info->alpha) || !(info->bps > 0.0f) || !std::isfinite(info->bps))
+    return HQ_ERR_CORRUPT;
+  info->lattice = (hq_lattice)h[6];
+  info->dithered = h[7] & 1u;
+  info->compact_side = (h[7] >> 1) & 1u;
+  info->tile = 128;
+  info->seed = get_le(h + 24, 8);
+  info->tile_base = get_le(h + 32, 8);
+  info->n_tiles = get_le(h + 40, 8);
+  info->total_bits = get_le(h + 48, 8);
+  return HQ_OK;
+}
+
+hq_status hq_plan_from_header(const void* in, hq_plan_t* out) {
+  if (!out) return HQ_ERR_ARG;
+  *out = nullptr;
+  hq_header_info info;
+  hq_status s = hq_header_read(in, &info);
+  if (s != HQ_OK) return s;
+  s = hq_plan(info.lattice, info.tile, info.bps, info.seed, out);
+  if (s != HQ_OK) return s;
+  return hq_plan_set_alpha(*out, info.alpha);
 }
 
 hq_status hq_status_sync(void* ws, void* stream) {

@@ -107,6 +107,9 @@ struct AttnArgs {
 
 hipError_t launch_gemv(int lat, const DecArgs& d, const GemvArgs& g, hipStream_t st);
 hipError_t launch_attention(int lat, const AttnArgs& a, uint32_t n_heads, hipStream_t st);
+hipError_t launch_side(bool pack, const uint64_t* offsets_in, const uint8_t* k_in, const uint8_t* side_in,
+                       uint64_t n, uint8_t* side_out, uint64_t* offsets_out, uint8_t* k_out, WsHeader* ws,
+                       hipStream_t st);
 hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
                         hipStream_t st);
 

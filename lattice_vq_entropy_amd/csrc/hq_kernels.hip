@@ -1400,6 +1400,64 @@ hipError_t launch_gemv(int lat, const DecArgs& d, const GemvArgs& g, hipStream_t
   return hipGetLastError();
 }
 
+// ===========================================================================
+// Compact side information: per chunk of 32 tiles a 96-byte record
+//   [0, 8)   uint64 bit offset of the chunk's first record
+//   [8, 72)  uint16 end of record j minus that offset, j = 0..31
+//   [72, 92) the 32 Rice parameters, 5 bits each, LSB first
+//   [92, 96) zero
+// (entries past the last tile are zero): 3 bytes per tile instead of 9.
+// ===========================================================================
+__global__ __launch_bounds__(256) void side_pack_k(const uint64_t* offsets, const uint8_t* kin, uint64_t n,
+                                                   uint8_t* side, WsHeader* ws) {
+  __shared__ uint32_t s_kw[8][5];
+  const uint32_t tid = threadIdx.x, j = tid & 31u, cl = tid >> 5;
+  const uint64_t t = (uint64_t)blockIdx.x * 256u + tid, c = t >> 5;
+  const uint64_t n_chunks = (n + 31) >> 5;
+  if (tid < 40) (&s_kw[0][0])[tid] = 0u;
+  __syncthreads();
+  const bool in_chunk = c < n_chunks, valid = t < n;
+  uint8_t* rec = side + c * 96u;
+  if (in_chunk) {
+    const uint64_t base = offsets[c << 5];
+    const uint64_t delta = valid ? offsets[t + 1] - base : 0ull;
+    if (valid && delta > 0xFFFFull) set_status(ws, 4);
+    reinterpret_cast<uint16_t*>(rec + 8)[j] = (uint16_t)delta;
+    if (j == 0) *reinterpret_cast<uint64_t*>(rec) = base;
+    const uint32_t kk = valid ? (uint32_t)kin[t] & 31u : 0u, p = 5u * j;
+    atomicOr(&s_kw[cl][p >> 5], kk << (p & 31u));
+    if ((p & 31u) > 27u) atomicOr(&s_kw[cl][(p >> 5) + 1u], kk >> (32u - (p & 31u)));
+  }
+  __syncthreads();
+  if (in_chunk && j < 6) reinterpret_cast<uint32_t*>(rec + 72)[j] = j < 5 ? s_kw[cl][j] : 0u;
+}
+
+__global__ __launch_bounds__(256) void side_unpack_k(const uint8_t* side, uint64_t n, uint64_t* offsets,
+                                                     uint8_t* kout) {
+  const uint64_t t = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  if (t >= n) return;
+  const uint32_t j = (uint32_t)(t & 31u);
+  const uint8_t* rec = side + (t >> 5) * 96u;
+  const uint64_t base = *reinterpret_cast<const uint64_t*>(rec);
+  const uint16_t* d = reinterpret_cast<const uint16_t*>(rec + 8);
+  offsets[t] = j == 0 ? base : base + d[j - 1];
+  if (t == n - 1) offsets[n] = base + d[j];
+  const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec + 72);
+  const uint32_t p = 5u * j;
+  uint32_t kk = kw[p >> 5] >> (p & 31u);
+  if ((p & 31u) > 27u) kk |= kw[(p >> 5) + 1u] << (32u - (p & 31u));
+  kout[t] = (uint8_t)(kk & 31u);
+}
+
+hipError_t launch_side(bool pack, const uint64_t* offsets_in, const uint8_t* k_in, const uint8_t* side_in,
+                       uint64_t n, uint8_t* side_out, uint64_t* offsets_out, uint8_t* k_out, WsHeader* ws,
+                       hipStream_t st) {
+  const dim3 grid((uint32_t)((n + 255) / 256));
+  if (pack) hipLaunchKernelGGL(side_pack_k, grid, dim3(256), 0, st, offsets_in, k_in, n, side_out, ws);
+  else hipLaunchKernelGGL(side_unpack_k, grid, dim3(256), 0, st, side_in, n, offsets_out, k_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
                         hipStream_t st) {
   uint64_t blocks = (n + 255) / 256;

@@ -860,3 +860,76 @@ int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,
   if (iters_out) *iters_out = iters;
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Serialized form of a stream.  The pages define none: the stream, its      */
+/* offsets and Rice parameters and the plan are the whole state [HQ-explainer,*/
+/* Methodology 3: the side information of each tile is its offset and k].    */
+/* These write the library's container layout from its specification: the   */
+/* 64-byte header and the compact side information (96 bytes per 32 tiles). */
+/* ------------------------------------------------------------------------ */
+
+/* CRC-32 of IEEE 802.3, bit by bit: reflected polynomial 0xEDB88320,
+ * register preset to all ones, final complement. */
+uint32_t orc_crc32(const uint8_t *p, size_t n) {
+  uint32_t c = 0xFFFFFFFFu;
+  for (size_t i = 0; i < n; ++i) {
+    c ^= p[i];
+    for (int b = 0; b < 8; ++b) c = (c >> 1) ^ (0xEDB88320u & (0u - (c & 1u)));
+  }
+  return ~c;
+}
+
+static void le_store(uint8_t *p, uint64_t v, int n) {
+  for (int i = 0; i < n; ++i) p[i] = (uint8_t)((v >> (8 * i)) & 0xFFu);
+}
+
+/* magic "HQS1", version 1, lattice, flags (1 dithered, 2 compact side),
+ * tile 128, alpha and bps as fp32 bits, seed, tile base, tile count, total
+ * bits, CRC-32 of bytes 0..59 at 60; reserved fields zero. */
+void orc_header_write(int lat, uint64_t seed, float alpha, float bps, int dithered, int compact, uint64_t tile_base,
+                      uint64_t n_tiles, uint64_t total_bits, uint8_t out[64]) {
+  uint32_t ab, bb;
+  memset(out, 0, 64);
+  memcpy(&ab, &alpha, 4);
+  memcpy(&bb, &bps, 4);
+  out[0] = 'H'; out[1] = 'Q'; out[2] = 'S'; out[3] = '1';
+  le_store(out + 4, 1, 2);
+  out[6] = (uint8_t)lat;
+  out[7] = (uint8_t)((dithered ? 1 : 0) + (compact ? 2 : 0));
+  le_store(out + 8, 128, 4);
+  le_store(out + 12, ab, 4);
+  le_store(out + 16, bb, 4);
+  le_store(out + 24, seed, 8);
+  le_store(out + 32, tile_base, 8);
+  le_store(out + 40, n_tiles, 8);
+  le_store(out + 48, total_bits, 8);
+  le_store(out + 60, orc_crc32(out, 60), 4);
+}
+
+/* Per chunk of 32 tiles: the chunk's first offset (8 bytes), each tile's end
+ * offset minus it (2 bytes each), the 32 Rice parameters as 5-bit fields
+ * (bit 5j + b of the 160-bit field is bit b of k of tile j), 4 zero bytes.
+ * Entries past the last tile stay zero.  Returns ORC_ERR_CAPACITY when a
+ * difference does not fit 16 bits. */
+int orc_side_pack(const uint64_t *offsets, const uint8_t *k, uint64_t n, uint8_t *out) {
+  const uint64_t chunks = (n + 31) / 32;
+  int status = ORC_OK;
+  memset(out, 0, (size_t)(96 * chunks));
+  for (uint64_t c = 0; c < chunks; ++c) {
+    uint8_t *rec = out + 96 * c;
+    const uint64_t base = offsets[32 * c];
+    le_store(rec, base, 8);
+    for (uint64_t j = 0; j < 32 && 32 * c + j < n; ++j) {
+      const uint64_t t = 32 * c + j;
+      const uint64_t d = offsets[t + 1] - base;
+      if (d > 65535u) status = ORC_ERR_CAPACITY;
+      le_store(rec + 8 + 2 * j, d & 0xFFFFu, 2);
+      for (int b = 0; b < 5; ++b) {
+        const uint64_t bit = 5 * j + (uint64_t)b;
+        if ((k[t] >> b) & 1u) rec[72 + bit / 8] |= (uint8_t)(1u << (bit % 8));
+      }
+    }
+  }
+  return status;
+}

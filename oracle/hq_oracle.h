@@ -28,6 +28,7 @@
  */
 #ifndef HQ_ORACLE_H
 #define HQ_ORACLE_H
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -141,6 +142,10 @@ int orc_gemv(int lat, uint64_t seed, float alpha, const uint32_t *words, const u
 
 /* Rate calibration: bisection on log2(alpha) for the payload rate
  * (bits per scalar).  Returns an ORC_ status. */
+uint32_t orc_crc32(const uint8_t *p, size_t n);
+void orc_header_write(int lat, uint64_t seed, float alpha, float bps, int dithered, int compact, uint64_t tile_base,
+                      uint64_t n_tiles, uint64_t total_bits, uint8_t out[64]);
+int orc_side_pack(const uint64_t *offsets, const uint8_t *k, uint64_t n, uint8_t *out);
 int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,
                   uint64_t n_tiles, int dithered, uint64_t tile_base,
                   float *alpha_out, double *bps_out, int *iters_out);

@@ -83,6 +83,9 @@ def lib():
             "orc_dequant_rotated_many": (_i, [_i, _u64, _p, _p, _p, _u64, _i, _u64, _p]),
             "orc_kv_scores": (_i, [_i, _u64, _f, _p, _p, _p, _u32, _u64, _u64, _p, _u32, _p]),
             "orc_calibrate": (_i, [_i, _u64, _f, _p, _i, _u64, _i, _u64, _p, _p, _p]),
+            "orc_crc32": (C.c_uint32, [_p, C.c_size_t]),
+            "orc_header_write": (None, [_i, _u64, _f, _f, _i, _i, _u64, _u64, _u64, _p]),
+            "orc_side_pack": (_i, [_p, _p, _u64, _p]),
             "orc_gemv": (_i, [_i, _u64, _f, _p, _p, _p, _u64, _u64, _p, _u32, _p]),
             "orc_kv_attention": (_i, [_i, _u64, _f, _p, _p, _p, _u64, _f, _p, _p, _p, _u64, _u32, _u64, _p,
                                       _u32, _f, _p]),
@@ -349,3 +352,26 @@ def calibrate(lat: int, seed: int, bps: float, x: np.ndarray, dithered=False, ti
     st = lib().orc_calibrate(lat, seed, bps, _ptr(xa), dt, n_tiles, int(dithered), tile_base,
                              C.byref(a), C.byref(r), C.byref(it))
     return st, a.value, r.value, it.value
+
+
+def crc32(data: bytes) -> int:
+    buf = np.frombuffer(bytes(data), np.uint8).copy() if len(data) else np.zeros(1, np.uint8)
+    return int(lib().orc_crc32(_ptr(buf), len(data)))
+
+
+def header(lat: int, seed: int, alpha: float, bps: float, dithered: bool, compact: bool, tile_base: int,
+           n_tiles: int, total_bits: int) -> bytes:
+    out = np.zeros(64, np.uint8)
+    lib().orc_header_write(lat, seed, alpha, bps, int(dithered), int(compact), tile_base, n_tiles, total_bits,
+                           _ptr(out))
+    return out.tobytes()
+
+
+def side_pack(offsets, k):
+    """(status, bytes) of the compact side information of a stream's offsets [n+1] and k [n]."""
+    offsets = np.ascontiguousarray(offsets, dtype=np.uint64)
+    k = np.ascontiguousarray(k, dtype=np.uint8)
+    n = offsets.size - 1
+    out = np.zeros(max(96 * ((n + 31) // 32), 1), np.uint8)
+    st = lib().orc_side_pack(_ptr(offsets), _ptr(k if k.size else np.zeros(1, np.uint8)), n, _ptr(out))
+    return st, out[: 96 * ((n + 31) // 32)].tobytes()
