@@ -118,7 +118,7 @@ def workload_rows(hq, W, torch, np, iters):
                          extra))
         return plan, enc, ws
 
-    def gemv(name, w, lat, bps, nbs=(1, 8)):
+    def gemv(name, w, lat, bps, nbs=(1, 8), nbs_mfma=(8, 32, 64)):
         """Fused decode + matrix-vector products with the compressed matrix,
         beside the dense bf16 product of the uncompressed matrix (context)."""
         rows_, cols_ = w.shape
@@ -142,6 +142,22 @@ def workload_rows(hq, W, torch, np, iters):
                      n_tiles, {"lattice": "ZA2D4E8"[[0, 1, 3, 5][lat]:[1, 3, 5, 7][lat]], "bps": round(bits / n_el, 4),
                                "weights_GBps_bf16_equiv": round(n_el * 2 / (tg * 1e-3) / 1e9, 1),
                                "dense_bf16_matmul_ms": round(td, 5)},
+                     other_bytes=4.0 * nb * (rows_ + cols_))
+            del r["GBps_in"]
+            rows.append(r)
+        for nb in nbs_mfma:
+            xv = torch.randn(nb, cols_, generator=torch.Generator(device=dev).manual_seed(100 + nb), device=dev)
+            gws = hq.gemm_workspace(rows_, cols_, nb)
+            y = torch.empty(nb, rows_, dtype=torch.float32, device=dev)
+            tg = _time(torch, lambda: hq.gemm(plan, enc, rows_, cols_, xv, gws, out=y), iters)
+            hq.check(gws)
+            xb = xv.to(torch.bfloat16)
+            td = _time(torch, lambda: torch.matmul(xb, w.t()), iters)
+            r = _row(name, f"gemm (fused decode + bf16 MFMA), {nb} vectors", tg, n_el, 0.0, bits, n_tiles,
+                     {"lattice": "ZA2D4E8"[[0, 1, 3, 5][lat]:[1, 3, 5, 7][lat]], "bps": round(bits / n_el, 4),
+                      "weights_GBps_bf16_equiv": round(n_el * 2 / (tg * 1e-3) / 1e9, 1),
+                      "TFLOPs": round(2.0 * nb * n_el / (tg * 1e-3) / 1e12, 2),
+                      "dense_bf16_matmul_ms": round(td, 5)},
                      other_bytes=4.0 * nb * (rows_ + cols_))
             del r["GBps_in"]
             rows.append(r)

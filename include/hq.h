@@ -170,6 +170,25 @@ hq_status hq_gemv(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
                   const uint64_t* offsets, const uint8_t* k, uint64_t rows, uint64_t cols,
                   const float* x, uint32_t nb, float* y, void* ws, void* stream);
 
+/* Matrix products with a compressed weight matrix on the matrix cores, for
+ * 1 to 64 vectors: y[j*rows + r] = sum_c W_hat[r][c] x[j*cols + c], W_hat as
+ * for hq_gemv (undithered Z, D4 or E8 stream; A2, whose codes are not
+ * integers, returns HQ_ERR_ARG).  Per 128-column block, c_dec <u_hat, H D x_b>
+ * [Methodology 1] for all vectors and 32 rows at a time is a dense product of
+ * the rotated vectors with the integer codes: both are split into two bf16
+ * pieces (x~ = hi + lo to within 2^-16 |x~|; codes exactly below 2^16) and
+ * hi*Uh + hi*Ul + lo*Uh is accumulated in fp32 by bf16 MFMA, so the result is
+ * within a few 2^-16 of the products' magnitudes plus fp32 accumulation.  The
+ * column blocks are split over work-groups and the splits summed in a fixed
+ * order (deterministic).  x: fp32 [nb][cols], 16-byte aligned; y: fp32
+ * [nb][rows]; ws: hq_gemm_workspace_bytes(rows, cols, nb) bytes, 16-byte
+ * aligned, zero-filled once.  Two or three stream-ordered launches.  Corrupt
+ * records count as zeros and set HQ_ERR_CORRUPT. */
+size_t hq_gemm_workspace_bytes(uint64_t rows, uint64_t cols, uint32_t nb);
+hq_status hq_gemm(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
+                  const uint64_t* offsets, const uint8_t* k, uint64_t rows, uint64_t cols,
+                  const float* x, uint32_t nb, float* y, void* ws, void* stream);
+
 /* Attention of n_heads * qph queries over compressed keys and values, without
  * materialising them [Methodology 4: the dithered KV cache; Methodology 1:
  * the RHT is orthogonal, so q . k_hat = c_dec_K <H D q, u_hat_K> and

@@ -48,6 +48,8 @@ _SIGNATURES = {
     "hq_kv_scores": (_i, [_p, _p, _u64, _p, _p, _u32, _u64, _u64, _p, _u32, _p, _p, _p]),
     "hq_gemv_workspace_bytes": (C.c_size_t, [_u64, _u64, _u32]),
     "hq_gemv": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _u32, _p, _p, _p]),
+    "hq_gemm_workspace_bytes": (C.c_size_t, [_u64, _u64, _u32]),
+    "hq_gemm": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _u32, _p, _p, _p]),
     "hq_append": (_i, [_p, _p, _i, _u64, _p, _u64, _p, _p, _u64, _p, _p]),
     "hq_kv_append": (_i, [_p, _p, _i, _u64, _u64, _p, _u64, _p, _p, _u64, _p, _p]),
     "hq_kv_attention_workspace_bytes": (C.c_size_t, [_u32, _u64, _u32]),
@@ -303,6 +305,27 @@ def gemv(plan: Plan, enc: Encoded, rows: int, cols: int, x: torch.Tensor, ws: to
     rc = lib().hq_gemv(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),
                        rows, cols, _dptr(x), nb, _dptr(y), _dptr(ws), _stream(stream))
     _check(rc, "gemv")
+    return y
+
+
+def gemm_workspace(rows: int, cols: int, nb: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for hq_gemm (the zero fill is required once)."""
+    n = int(lib().hq_gemm_workspace_bytes(rows, cols, nb))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def gemm(plan: Plan, enc: Encoded, rows: int, cols: int, x: torch.Tensor, ws: torch.Tensor,
+         out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """hq_gemm: fp32 [nb, rows] = x W_hat^T on the matrix cores (x fp32 [nb, cols], nb <= 64)."""
+    if x.dtype != torch.float32 or not x.is_contiguous() or x.numel() % cols:
+        raise ValueError("x must be contiguous fp32 [nb, cols]")
+    if enc.dithered:
+        raise ValueError("matrix products take an undithered weight stream")
+    nb = x.numel() // cols
+    y = out if out is not None else torch.empty(nb, rows, dtype=torch.float32, device=x.device)
+    rc = lib().hq_gemm(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),
+                       rows, cols, _dptr(x), nb, _dptr(y), _dptr(ws), _stream(stream))
+    _check(rc, "gemm")
     return y
 
 

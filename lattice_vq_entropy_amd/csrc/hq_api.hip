@@ -358,6 +358,67 @@ hq_status hq_gemv(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const
   return dev_err(hq::launch_gemv(plan->lattice, d, g, (hipStream_t)stream));
 }
 
+namespace {
+struct GemmShape {
+  uint32_t nbp, splits, per;
+  uint64_t xp_bytes, part_bytes;
+};
+GemmShape gemm_shape(uint64_t rows, uint64_t cols, uint32_t nb) {
+  GemmShape g{};
+  const uint64_t nblk = cols / 128, ntn = (rows + 31) / 32;
+  g.nbp = nb <= 32 ? 32u : 64u;
+  uint64_t want = ntn >= 2048 ? 1 : (2048 + ntn - 1) / ntn;  // about 2048 work-groups
+  if (want > nblk) want = nblk;
+  if (want < 1) want = 1;
+  g.per = (uint32_t)((nblk + want - 1) / want);
+  g.splits = g.per ? (uint32_t)((nblk + g.per - 1) / g.per) : 1u;
+  g.xp_bytes = hq::ws_align(2ull * 2ull * g.nbp * cols);
+  g.part_bytes = g.splits > 1 ? 4ull * g.splits * g.nbp * rows : 0ull;
+  return g;
+}
+}  // namespace
+
+size_t hq_gemm_workspace_bytes(uint64_t rows, uint64_t cols, uint32_t nb) {
+  const GemmShape g = gemm_shape(rows, cols, nb);
+  return (size_t)(sizeof(hq::WsHeader) + g.xp_bytes + g.part_bytes);
+}
+
+hq_status hq_gemm(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets, const uint8_t* k,
+                  uint64_t rows, uint64_t cols, const float* x, uint32_t nb, float* y, void* ws, void* stream) {
+  if (!plan) return HQ_ERR_ARG;
+  if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (plan->lattice == HQ_A2) return HQ_ERR_ARG;  // its codes are not integers
+  if (cols == 0 || cols % 128 || nb == 0 || nb > hq::kGemmMaxVec) return HQ_ERR_ARG;
+  if (rows == 0) return HQ_OK;
+  if (!words || !offsets || !k || !x || !y || !ws) return HQ_ERR_ARG;
+  if (((uintptr_t)x & 15u) != 0 || ((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+  const uint64_t nblk = cols / 128;
+  if (rows > 0x7FFFFFFFull || nblk > 0xFFFFFFFFull || rows * nblk / nblk != rows || (uint64_t)nb * rows > 0xFFFFFFFFull)
+    return HQ_ERR_ARG;
+  const GemmShape sh = gemm_shape(rows, cols, nb);
+  if (sh.splits > 65535u) return HQ_ERR_ARG;
+  hq::GemmArgs g{};
+  g.words = words;
+  g.n_words = n_words;
+  g.offsets = offsets;
+  g.k = k;
+  g.ws = (hq::WsHeader*)ws;
+  g.x = x;
+  g.xp = (uint16_t*)((char*)ws + sizeof(hq::WsHeader));
+  g.part = (float*)((char*)ws + sizeof(hq::WsHeader) + sh.xp_bytes);
+  g.y = y;
+  g.rows = (uint32_t)rows;
+  g.nblk = (uint32_t)nblk;
+  g.nb = nb;
+  g.nbp = sh.nbp;
+  g.splits = sh.splits;
+  g.per = sh.per;
+  uint32_t sl16[4], k0, k1;
+  fill_common(plan, sl16, g.sl32, k0, k1);
+  g.c_dec = plan->c_dec;
+  return dev_err(hq::launch_gemm(plan->lattice, g, (hipStream_t)stream));
+}
+
 size_t hq_kv_attention_workspace_bytes(uint32_t n_heads, uint64_t seq, uint32_t qph) {
   const uint64_t groups = (seq + hq::kAttnChunks * hq::kChunkTiles - 1) / (hq::kAttnChunks * hq::kChunkTiles);
   return (size_t)(sizeof(hq::WsHeader) + 4ull * n_heads * groups * qph * hq::kAttnPart);

@@ -106,6 +106,23 @@ struct AttnArgs {
 };
 
 hipError_t launch_gemv(int lat, const DecArgs& d, const GemvArgs& g, hipStream_t st);
+
+// Matrix products with MFMA: up to kGemmMaxVec vectors; weights in tiles of
+// 32 rows x one 128-column block per step.
+constexpr uint32_t kGemmMaxVec = 64;
+constexpr uint32_t kGemmRecWords = 96;  // staging per tile: a record spans at most 94 words
+struct GemmArgs {
+  const uint32_t* words; uint64_t n_words; const uint64_t* offsets; const uint8_t* k;
+  WsHeader* ws;
+  const float* x;        // nb x cols
+  uint16_t* xp;          // bf16 pieces [2][nbp][cols] of H D x per block: hi, then lo
+  float* part;           // [splits][nbp][rows] when splits > 1
+  float* y;              // nb x rows
+  uint32_t rows, nblk, nb, nbp, splits, per;  // per: column blocks per split
+  uint32_t sl32[4];
+  float c_dec;
+};
+hipError_t launch_gemm(int lat, const GemmArgs& g, hipStream_t st);
 hipError_t launch_attention(int lat, const AttnArgs& a, uint32_t n_heads, hipStream_t st);
 hipError_t launch_side(bool pack, const uint64_t* offsets_in, const uint8_t* k_in, const uint8_t* side_in,
                        uint64_t n, uint8_t* side_out, uint64_t* offsets_out, uint8_t* k_out, WsHeader* ws,

@@ -1401,6 +1401,242 @@ hipError_t launch_gemv(int lat, const DecArgs& d, const GemvArgs& g, hipStream_t
 }
 
 // ===========================================================================
+// Matrix products Y = X W_hat^T with matrix cores
+// ===========================================================================
+// Each tile adds c_dec <u_hat, H D x_b> to its row's products, so Y is c_dec
+// times the product of the rotated vectors (nb x cols) with the rotated codes
+// U (rows x cols, integers for Z, D4 and E8), a dense contraction: bf16 MFMA
+// 32x32x16 with fp32 accumulation.  Both operands are split into two bf16
+// pieces, x~ = hi + lo (+ at most 2^-16 |x~|) and u = Uh + Ul (exact below
+// 2^16), and hi Uh + hi Ul + lo Uh is accumulated (products of bf16 values
+// are exact in fp32).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split_bf16(const float x[8], uint4& hi, uint4& lo) {
+  const f32x8_t f = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  const bf16x8_t h = __builtin_convertvector(f, bf16x8_t);
+  const f32x8_t hf = __builtin_convertvector(h, f32x8_t);
+  const bf16x8_t l = __builtin_convertvector(f - hf, bf16x8_t);  // x - hi is exact in fp32
+  hi = __builtin_bit_cast(uint4, h);
+  lo = __builtin_bit_cast(uint4, l);
+}
+
+// Step 1: the vectors' blocks rotated as the weights were (x~ = H D x, the
+// butterfly of the decoder) and split; vector rows nb..nbp-1 are zero.
+__global__ __launch_bounds__(256) void rotx_split_k(GemmArgs g) {
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15;
+  const int v = lane_vector(r);
+  const uint32_t q = blockIdx.x * 16u + (uint32_t)(tid >> 4);  // (vector, block) of nbp x nblk
+  const bool ok = q < g.nbp * g.nblk;
+  const uint32_t j = ok ? q / g.nblk : 0u, blk = ok ? q % g.nblk : 0u;
+  const bool in = ok && j < g.nb;
+  const uint64_t src = ((uint64_t)(in ? j : 0u) * g.nblk + blk) * kTile + 8 * v;
+  float xv[8];
+  const float4 x0 = *reinterpret_cast<const float4*>(g.x + src);
+  const float4 x1 = *reinterpret_cast<const float4*>(g.x + src + 4);
+  xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
+  xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
+  const uint32_t sm = lane_signs32(g.sl32, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xv[i] = __builtin_bit_cast(float, fbits(xv[i]) ^ ((sm << i) & 0x80000000u));
+  const FwhtSigns fs = fwht_signs(v);
+  fwht_tile(xv, fs);  // every lane of the row takes part (cross-lane stages)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xv[i] = in ? xv[i] * fs.lane_sign : 0.0f;
+  if (ok) {
+    uint4 hi, lo;
+    split_bf16(xv, hi, lo);
+    const uint64_t dst = ((uint64_t)j * g.nblk + blk) * kTile + 8 * v;
+    const uint64_t piece = (uint64_t)g.nbp * g.nblk * kTile;
+    *reinterpret_cast<uint4*>(g.xp + dst) = hi;
+    *reinterpret_cast<uint4*>(g.xp + piece + dst) = lo;
+  }
+}
+
+// Step 2: one work-group per 32 weight rows (blockIdx.x) and split of the
+// column blocks (blockIdx.y).  Per block: the 32 tiles (one per row) are
+// parsed, one per 16-lane row slot in two passes, each record staged in the
+// slot's own LDS area; their codes, split, go to LDS as the B operand; then
+// wave w accumulates K steps 2w and 2w+1 of the block for every 32-vector M
+// tile.  The four waves' sums are added in a fixed order at the end.
+template <int L, int NMT>
+__global__ __launch_bounds__(256) void gemm_k(GemmArgs g) {
+  constexpr uint32_t RAW = Lat<L>::raw;
+  constexpr uint32_t MAXREC = RAW + 128u * 23u;
+  constexpr int kBS = kTile + 8;  // B row stride (bf16): conflict-free 16-byte reads
+  __shared__ __align__(16) uint32_t s_rec[16][kGemmRecWords];
+  __shared__ uint32_t s_ust[16][16];
+  __shared__ uint4 s_tb[16];
+  __shared__ uint64_t s_o[33];
+  __shared__ uint64_t s_o1[32];
+  __shared__ uint32_t s_k[32];
+  __shared__ __align__(16) uint16_t s_B[2][32][kBS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
+  const int v = lane_vector(r), pslot = wv * 4 + grp;
+  const uint32_t r0 = blockIdx.x * 32u;
+  const uint32_t b_lo = blockIdx.y * g.per;
+  const uint32_t b_hi = b_lo + g.per < g.nblk ? b_lo + g.per : g.nblk;
+  f32x16_t acc0 = {}, acc1 = {};
+  const uint64_t piece = (uint64_t)g.nbp * g.nblk * kTile;
+  // the 32 tiles' offsets and Rice parameters, loaded one block ahead
+  const bool row_in = tid < 32 && r0 + tid < g.rows;
+  const uint64_t t_row = (uint64_t)(r0 + (tid & 31)) * g.nblk;
+  uint64_t nx_o = 0, nx_o1 = 0;
+  uint32_t nx_k = 0;
+  if (row_in && b_lo < b_hi) {
+    nx_o = g.offsets[t_row + b_lo];
+    nx_o1 = g.offsets[t_row + b_lo + 1];
+    nx_k = g.k[t_row + b_lo];
+  }
+
+#pragma unroll 1
+  for (uint32_t b = b_lo; b < b_hi; ++b) {
+    if (tid < 32) {
+      s_o[tid] = nx_o;
+      s_o1[tid] = nx_o1;
+      s_k[tid] = nx_k;
+    }
+    __syncthreads();  // (also: the previous block's B operand is consumed)
+    if (row_in && b + 1 < b_hi) {
+      nx_o = g.offsets[t_row + b + 1];
+      nx_o1 = g.offsets[t_row + b + 2];
+      nx_k = g.k[t_row + b + 1];
+    }
+    // lane indices from an opaque copy of the thread index: what the parse
+    // derives from them is recomputed per block instead of held across the loop
+    const int tid = opaque_int(threadIdx.x), lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
+    const int v = lane_vector(r), pslot = wv * 4 + grp;
+#pragma unroll 1
+    for (int p = 0; p < 2; ++p) {
+      const int i = p * 16 + pslot;  // tile row within the 32
+      const bool valid = r0 + (uint32_t)i < g.rows;
+      const uint64_t o0 = s_o[i], o1 = s_o1[i];
+      const uint32_t kk = s_k[i];
+      const uint64_t Lr = o1 - o0;
+      const uint64_t w_first = o0 >> 5, w_end = (o1 + 31) >> 5;
+      const bool ok = valid && o1 >= o0 && kk <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + kk) && Lr <= MAXREC &&
+                      w_end <= g.n_words;
+      const uint32_t n = ok ? (uint32_t)(w_end - w_first) : 0u;  // <= 94
+      uint32_t* sr = s_rec[pslot];
+#pragma unroll
+      for (int q = 0; q < (int)kGemmRecWords / 16; ++q) {
+        const uint32_t w = (uint32_t)r + 16u * q;
+        sr[w] = w < n ? g.words[w_first + w] : 0u;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = 0.0f;
+      bool good = false;
+      if (ok) good = parse_lane<L>(sr, (uint32_t)(o0 & 31u), (uint32_t)Lr, kk, v, r, lane, s_ust[pslot],
+                                   reinterpret_cast<uint8_t*>(&s_tb[pslot]), pv);
+      if (valid && !good) {
+        if (r == 0) set_status(g.ws, 5);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = 0.0f;
+      }
+      uint4 hi, lo;
+      split_bf16(pv, hi, lo);
+      *reinterpret_cast<uint4*>(&s_B[0][i][8 * v]) = hi;
+      *reinterpret_cast<uint4*>(&s_B[1][i][8 * v]) = lo;
+    }
+    __syncthreads();
+    // matrix cores: B[k][j] = code k of row r0 + j (lane j + 32 (k / 8), element k % 8)
+    const int bj = lane & 31, bk = 8 * (lane >> 5);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int k0 = 16 * (2 * wv + st);
+      const bf16x8_t Bh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&s_B[0][bj][k0 + bk]));
+      const bf16x8_t Bl = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&s_B[1][bj][k0 + bk]));
+      // A[i][k] = x~ of vector 32 mt + i (lane i + 32 (k / 8), element k % 8)
+      const uint64_t ai = (uint64_t)bj * g.nblk * kTile + (uint64_t)b * kTile + k0 + bk;
+      {
+        const bf16x8_t Ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(g.xp + ai));
+        const bf16x8_t Al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(g.xp + piece + ai));
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah, Bh, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah, Bl, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al, Bh, acc0, 0, 0, 0);
+      }
+      if constexpr (NMT > 1) {
+        const uint64_t a1 = ai + (uint64_t)32 * g.nblk * kTile;
+        const bf16x8_t Ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(g.xp + a1));
+        const bf16x8_t Al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(g.xp + piece + a1));
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah, Bh, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah, Bl, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al, Bh, acc1, 0, 0, 0);
+      }
+    }
+  }
+  // the four waves' sums, per M tile, through LDS (the B area is free):
+  // D[i][j] sits in lane j + 32 ((i / 4) % 2), register 4 (i / 8) + i % 4
+  float* s_red = reinterpret_cast<float*>(&s_B[0][0][0]);  // [4 waves][32][32]
+#pragma unroll
+  for (uint32_t mt = 0; mt < (uint32_t)NMT; ++mt) {
+    const f32x16_t a = mt == 0 ? acc0 : acc1;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = 8 * (q / 4) + 4 * (lane >> 5) + (q % 4), j = lane & 31;
+      s_red[(wv * 32 + i) * 32 + j] = a[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e, i = idx >> 5, j = idx & 31;
+      const float sum = ((s_red[(0 * 32 + i) * 32 + j] + s_red[(1 * 32 + i) * 32 + j]) + s_red[(2 * 32 + i) * 32 + j]) +
+                        s_red[(3 * 32 + i) * 32 + j];
+      const uint32_t m = 32u * mt + (uint32_t)i, row = r0 + (uint32_t)j;
+      if (row < g.rows) {
+        if (g.splits == 1) {
+          if (m < g.nb) g.y[(uint64_t)m * g.rows + row] = sum * g.c_dec;
+        } else {
+          g.part[((uint64_t)blockIdx.y * g.nbp + m) * g.rows + row] = sum;
+        }
+      }
+    }
+  }
+}
+
+// Step 3 (more than one split): y = c_dec * (the splits' sums in order).
+__global__ __launch_bounds__(256) void gemm_sum_k(GemmArgs g) {
+  const uint64_t q = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  if (q >= (uint64_t)g.nb * g.rows) return;
+  const uint64_t stride = (uint64_t)g.nbp * g.rows;
+  float s = g.part[q];
+  for (uint32_t sp = 1; sp < g.splits; ++sp) s += g.part[sp * stride + q];
+  g.y[q] = s * g.c_dec;
+}
+
+hipError_t launch_gemm(int lat, const GemmArgs& g, hipStream_t st) {
+  const uint32_t nq = g.nbp * g.nblk;
+  hipLaunchKernelGGL(rotx_split_k, dim3((nq + 15u) / 16u), dim3(256), 0, st, g);
+  const dim3 grid((g.rows + 31u) / 32u, g.splits);
+  const bool two = g.nbp > 32u;
+  if (lat == 0) {
+    if (two) hipLaunchKernelGGL((gemm_k<0, 2>), grid, dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((gemm_k<0, 1>), grid, dim3(256), 0, st, g);
+  } else if (lat == 2) {
+    if (two) hipLaunchKernelGGL((gemm_k<2, 2>), grid, dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((gemm_k<2, 1>), grid, dim3(256), 0, st, g);
+  } else if (lat == 3) {
+    if (two) hipLaunchKernelGGL((gemm_k<3, 2>), grid, dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((gemm_k<3, 1>), grid, dim3(256), 0, st, g);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  if (g.splits > 1) {
+    const uint64_t n = (uint64_t)g.nb * g.rows;
+    hipLaunchKernelGGL(gemm_sum_k, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, g);
+  }
+  return hipGetLastError();
+}
+
+// ===========================================================================
 // Compact side information: per chunk of 32 tiles a 96-byte record
 //   [0, 8)   uint64 bit offset of the chunk's first record
 //   [8, 72)  uint16 end of record j minus that offset, j = 0..31
