@@ -402,7 +402,7 @@ def main():
         },
         "encode": {"ms": round(enc_ms, 5), "GBps_bf16_in": round(bf16_bytes / (enc_ms * 1e-3) / 1e9, 1),
                    "GBps_algorithmic": round(enc_gbs, 1), "hbm_frac": round(enc_gbs / HBM_PEAK_GBS, 4),
-                   "kernels": "encode_k + place_k (+ scan_k above 8192 chunks)"},
+                   "kernels": "encode_k + place_k (+ blocksum_k above 8192 chunks)"},
         "decode": {"ms": round(dec_ms, 5), "GBps_bf16_in": round(bf16_bytes / (dec_ms * 1e-3) / 1e9, 1),
                    "GBps_algorithmic": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                    "kernels": "decode_k"},

@@ -35,7 +35,8 @@
  *   - No call waits on another work-group's progress; encode is two
  *     stream-ordered launches (pack per chunk, then placement, which sums the
  *     bit counts of the chunks before its own) up to 8192 chunks of 32 tiles,
- *     and three above (a scan of the chunk bit counts between them).  Encode
+ *     and three above (the bit counts of blocks of 1024 chunks between them;
+ *     placement then adds the blocks' totals and its own block's counts).  Encode
  *     and decode allocate nothing and can be captured in a HIP graph.
  *   - Tensors are row-major; every 128 consecutive elements form one tile
  *     (weights: tiles along rows; KV [B, H, S, 128]: one tile per vector).

@@ -46,6 +46,8 @@ struct PlaceArgs {
   uint64_t cap_words;
   uint64_t* offsets;
   const uint64_t* base;  // append: the existing stream's end bit (device), else null
+  const uint32_t* eloc;      // above the self-scan limit: chunk offsets within blocks of 1024
+  const uint64_t* blockpre;  // and the bits of the blocks before each block
 };
 
 struct DecArgs {

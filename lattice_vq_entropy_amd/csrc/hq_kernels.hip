@@ -337,89 +337,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 8 : 
   }
 }
 
-// Encode, step 2 of 3: exclusive scan of the chunk bit counts into the chunk
-// offsets E[0..n] (E[n] = total), by one work-group of 1024 threads.  Thread
-// i owns the strip of 4*per consecutive counts starting at 4*per*i, loaded
-// once (all loads in flight together) and kept in registers; agg is padded to
-// 64 entries, E to an even count.  Up to kScanRegs uint4 per thread (n up to
-// 32 Ki chunks); longer inputs read the rest of the strip twice.
-constexpr uint32_t kScanRegs = 8;
-__global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, uint64_t* E) {
+// Encode, step 2 of 3 (more than kSelfScanChunks chunks), first part: per
+// block of 1024 chunks (one work-group, four counts per thread) the chunks'
+// exclusive offsets within the block, Eloc[c] (32-bit: at most 1024 * 94720
+// bits), and the block's total T[b].
+constexpr uint32_t kScanBlock = 1024;
+__global__ __launch_bounds__(256) void blocksum_k(const uint32_t* agg, uint32_t n, uint32_t* Eloc, uint64_t* T) {
+  __shared__ uint32_t s_w[4];
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, i = blockIdx.x * kScanBlock + 4u * tid;
+  uint4 g = make_uint4(0u, 0u, 0u, 0u);
+  if (i < n) g = *reinterpret_cast<const uint4*>(agg + i);  // agg is padded to 64 entries
+  if (i + 1 >= n) g.y = 0u;
+  if (i + 2 >= n) g.z = 0u;
+  if (i + 3 >= n) g.w = 0u;
+  const uint32_t t = g.x + g.y + g.z + g.w;
+  uint32_t x = t;  // inclusive scan over the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if ((int)lane >= o) x += y;
+  }
+  if (lane == 63) s_w[wv] = x;
+  __syncthreads();
+  uint32_t run = x - t;
+#pragma unroll
+  for (uint32_t w = 0; w < 3; ++w) run += w < wv ? s_w[w] : 0u;
+  if (i < n) {
+    const uint4 e = make_uint4(run, run + g.x, run + g.x + g.y, run + g.x + g.y + g.z);
+    *reinterpret_cast<uint4*>(Eloc + i) = e;  // Eloc is padded like agg
+  }
+  if (tid == 0) T[blockIdx.x] = (uint64_t)s_w[0] + s_w[1] + s_w[2] + s_w[3];
+}
+
+// Encode, step 2 of 3, second part: the block totals T[0..nb) replaced in place by their
+// exclusive prefix sums, by one work-group of 1024 threads (1024 blocks per
+// round, a carry between rounds).
+__global__ __launch_bounds__(1024) void blockscan_k(uint64_t* T, uint32_t nb) {
   __shared__ uint64_t s_w[16];
+  __shared__ uint64_t s_carry;
   const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint32_t per = (n + 4095u) / 4096u;  // uint4 per thread
-  const uint32_t lo = tid * per * 4u;
-  uint4 q[kScanRegs];
-  uint64_t sum = 0;
-#pragma unroll
-  for (uint32_t j = 0; j < kScanRegs; ++j) {
-    const uint32_t i = lo + 4u * j;
-    q[j] = (j < per && i < n) ? *reinterpret_cast<const uint4*>(agg + i) : make_uint4(0u, 0u, 0u, 0u);
-  }
-  for (uint32_t j = kScanRegs; j < per; ++j) {  // long inputs only
-    const uint32_t i = lo + 4u * j;
-    if (i < n) {
-      const uint4 t = *reinterpret_cast<const uint4*>(agg + i);
-      sum += (uint64_t)t.x + (i + 1 < n ? t.y : 0u) + (i + 2 < n ? t.z : 0u) + (i + 3 < n ? t.w : 0u);
-    }
-  }
-#pragma unroll
-  for (uint32_t j = 0; j < kScanRegs; ++j) {
-    const uint32_t i = lo + 4u * j;
-    sum += (uint64_t)(i < n ? q[j].x : 0u) + (i + 1 < n ? q[j].y : 0u) + (i + 2 < n ? q[j].z : 0u) +
-           (i + 3 < n ? q[j].w : 0u);
-  }
-  // inclusive scan over the wave: 32-bit row scans joined over the rows while
-  // a wave's total stays below 2^32 (4 * per counts of at most 32 * 2960 bits
-  // on each of 64 lanes), else 64-bit shuffles
-  uint64_t x;
-  if (per <= 128u) {
-    uint32_t y = row_scan_u32((uint32_t)sum);
-    const uint32_t t0 = __builtin_amdgcn_readlane(y, 15), t1 = __builtin_amdgcn_readlane(y, 31),
-                   t2 = __builtin_amdgcn_readlane(y, 47);
-    const uint32_t row = lane >> 4;
-    y += (row > 0u ? t0 : 0u) + (row > 1u ? t1 : 0u) + (row > 2u ? t2 : 0u);
-    x = y;
-  } else {
-    x = sum;
+  if (tid == 0) s_carry = 0;
+  for (uint32_t base = 0; base < nb; base += 1024u) {  // (uniform)
+    const uint32_t i = base + tid;
+    const uint64_t t = i < nb ? T[i] : 0ull;
+    uint64_t x = t;  // inclusive scan over the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint64_t y = __shfl_up(x, o);
       if ((int)lane >= o) x += y;
     }
-  }
-  if (lane == 63) s_w[wv] = x;
-  __syncthreads();
-  // plus the totals of the earlier waves (independent LDS reads)
-  uint64_t run = x - sum;
+    if (lane == 63) s_w[wv] = x;
+    __syncthreads();  // (also: s_carry of the previous round is final)
+    uint64_t run = s_carry + x - t;
 #pragma unroll
-  for (uint32_t w = 0; w < 15; ++w) run += w < wv ? s_w[w] : 0ull;
-  // writes four offsets from the counts t at i (i a multiple of 4, E + i
-  // 16-byte aligned) and advances run
-  auto put4 = [&](uint32_t i, const uint4& t) {
-    const uint64_t e0 = run, e1 = e0 + t.x, e2 = e1 + t.y, e3 = e2 + t.z;
-    if (i + 3 < n) {
-      reinterpret_cast<ulonglong2*>(E + i)[0] = make_ulonglong2(e0, e1);
-      reinterpret_cast<ulonglong2*>(E + i)[1] = make_ulonglong2(e2, e3);
-      run = e3 + t.w;
-    } else {  // the strip holding the last count
-      const uint32_t r = n - i;
-      E[i] = e0;
-      if (r > 1) E[i + 1] = e1;
-      if (r > 2) E[i + 2] = e2;
-      run = r == 1 ? e1 : r == 2 ? e2 : e3;
-    }
-  };
-#pragma unroll
-  for (uint32_t j = 0; j < kScanRegs; ++j) {
-    const uint32_t i = lo + 4u * j;
-    if (j < per && i < n) put4(i, q[j]);
+    for (uint32_t w = 0; w < 15; ++w) run += w < wv ? s_w[w] : 0ull;
+    if (i < nb) T[i] = run;
+    __syncthreads();  // every thread has read s_w and s_carry
+    if (tid == 1023) s_carry = run + t;
   }
-  for (uint32_t j = kScanRegs; j < per; ++j) {
-    const uint32_t i = lo + 4u * j;
-    if (i < n) put4(i, *reinterpret_cast<const uint4*>(agg + i));
-  }
-  if (lo < n && lo + 4u * per >= n) E[n] = run;
 }
 
 // Encode, step 3 of 3: one chunk per work-group.  The chunk's staged bits go
@@ -429,10 +404,11 @@ __global__ __launch_bounds__(1024) void scan_k(const uint32_t* agg, uint32_t n, 
 // 32 bits, recorded by step 1, so every stream word is written exactly once.
 // B is 0, or when appending to an existing stream its end bit: then the first
 // chunk's first word keeps the existing bits below B.  Also the per-tile
-// offsets, and the capacity check.  SELF_SCAN (inputs of at most kSelfScanChunks chunks):
-// step 2 is skipped and every work-group sums the bit counts of the chunks
-// before its own (all reads of one small array that the L2 serves), which
-// costs less than a launch of the scan.
+// offsets, and the capacity check.  Each work-group forms E[c] itself: up to
+// kSelfScanChunks chunks (SELF_SCAN) as the sum of the bit counts of the
+// chunks before its own (all reads of one small array that the L2 serves), so
+// step 2 is skipped; above that as the bits of the blocks of 1024 chunks
+// before its own (step 2) plus the counts in its block before it.
 constexpr uint32_t kSelfScanChunks = 8192;
 template <bool SELF_SCAN>
 __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
@@ -491,9 +467,9 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
     __syncthreads();
     E = B + s_part[0] + s_part[1] + s_part[2] + s_part[3];  // the sum: at most 8192 * 94720 bits
     E1 = E + A;
-  } else {
-    E = B + a.E[chunk];
-    E1 = B + a.E[chunk + 1];
+  } else {  // the block's prefix plus the offset within the block (uniform loads)
+    E = B + a.blockpre[chunk >> 10] + a.eloc[chunk];
+    E1 = E + a.agg[chunk];
   }
   if (tid == 0 && chunk == a.n_chunks - 1 && (E1 + 31) / 32 > a.cap_words) atomicOr(&a.ws->status, 1u << 4);
   const uint64_t t = (uint64_t)chunk * kChunkTiles + tid;
@@ -986,8 +962,15 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   }
   hipLaunchKernelGGL((encode_k<L, DITHER, BF16, false>), grid, dim3(256), 0, st, a);
   const bool self_scan = a.n_chunks <= kSelfScanChunks;
-  if (!self_scan)
-    hipLaunchKernelGGL(scan_k, dim3(1), dim3(1024), 0, st, (const uint32_t*)a.agg, a.n_chunks, a.E);
+  // step 2 (two-level): Eloc (u32 per chunk, padded to a multiple of 4) at
+  // the start of the E region, the block prefixes (u64) after it
+  uint32_t* eloc = reinterpret_cast<uint32_t*>(a.E);
+  uint64_t* blockpre = a.E + ((a.n_chunks + 3) / 4) * 2;
+  if (!self_scan) {
+    const uint32_t nb = (a.n_chunks + kScanBlock - 1) / kScanBlock;
+    hipLaunchKernelGGL(blocksum_k, dim3(nb), dim3(256), 0, st, (const uint32_t*)a.agg, a.n_chunks, eloc, blockpre);
+    hipLaunchKernelGGL(blockscan_k, dim3(1), dim3(1024), 0, st, blockpre, nb);
+  }
   PlaceArgs pa;
   pa.agg = a.agg;
   pa.ws = a.ws;
@@ -1001,6 +984,8 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   pa.cap_words = a.cap_words;
   pa.offsets = a.offsets;
   pa.base = a.base;
+  pa.eloc = eloc;
+  pa.blockpre = blockpre;
   if (self_scan)
     hipLaunchKernelGGL(place_k<true>, grid, dim3(256), 0, st, pa);
   else
