@@ -583,6 +583,7 @@ hq_status hq_calibrate(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n
                        uint64_t tile_base, void* ws, void* stream, float* alpha_out, double* bps_out) {
   if (!plan || !x || !ws || n_tiles == 0) return HQ_ERR_ARG;
   if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_ARG;
+  if (((uintptr_t)x & 15u) != 0 || ((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;
   hq::WsHeader* h = (hq::WsHeader*)ws;
   const uint64_t n = n_tiles * 128ull;

@@ -919,33 +919,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
 }
 
 // Sum of squares (fp64) for the calibration start point: one partial per
-// work-group (no same-address atomics), reduced in a fixed order.
+// work-group (no same-address atomics), reduced in a fixed order.  16-byte
+// loads (8 bf16 or 4 fp32 values), four in flight per thread.
+__device__ __forceinline__ double sumsq_u4(const uint4& w, int bf16) {
+  const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (bf16) {
+      const double lo = (double)__builtin_bit_cast(float, q[j] << 16);
+      const double hi = (double)__builtin_bit_cast(float, q[j] & 0xFFFF0000u);
+      acc = __builtin_fma(lo, lo, acc);
+      acc = __builtin_fma(hi, hi, acc);
+    } else {
+      const double f = (double)__builtin_bit_cast(float, q[j]);
+      acc = __builtin_fma(f, f, acc);
+    }
+  }
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void sumsq_k(const void* x, int bf16, uint64_t n, double* partials) {
   __shared__ double s_w[4];
+  const uint4* p = reinterpret_cast<const uint4*>(x);
+  const uint64_t n4 = bf16 ? n / 8 : n / 4;  // n is a multiple of 128
+  const uint64_t stride = (uint64_t)gridDim.x * 256u;
   double acc = 0.0;
-  for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (uint64_t)gridDim.x * 256) {
-    float f = bf16 ? __builtin_bit_cast(float, (uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16)
-                   : reinterpret_cast<const float*>(x)[i];
-    acc += (double)f * (double)f;
+  uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    const uint4 w0 = p[i], w1 = p[i + stride], w2 = p[i + 2 * stride], w3 = p[i + 3 * stride];
+    acc += ((sumsq_u4(w0, bf16) + sumsq_u4(w1, bf16)) + (sumsq_u4(w2, bf16) + sumsq_u4(w3, bf16)));
   }
+  for (; i < n4; i += stride) acc += sumsq_u4(p[i], bf16);
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
   if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = acc;
   __syncthreads();
   if (threadIdx.x == 0) partials[blockIdx.x] = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
 }
 
+// One work-group of 1024 threads sums p[0..n) in a fixed order (eight loads
+// in flight per thread).
 template <typename T>
-__global__ __launch_bounds__(256) void reduce_k(const T* p, uint32_t n, T* out) {
-  __shared__ T s[256];
+__global__ __launch_bounds__(1024) void reduce_k(const T* p, uint32_t n, T* out) {
+  __shared__ T s[1024];
+  const uint32_t tid = threadIdx.x;
   T acc = 0;
-  for (uint32_t i = threadIdx.x; i < n; i += 256) acc += p[i];
-  s[threadIdx.x] = acc;
+  uint32_t i = tid;
+  for (; i + 7u * 1024u < n; i += 8u * 1024u) {
+    T v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = p[i + 1024u * j];
+    acc += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  }
+  for (; i < n; i += 1024u) acc += p[i];
+  s[tid] = acc;
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if ((int)threadIdx.x < w) s[threadIdx.x] += s[threadIdx.x + w];
+  for (int w = 512; w >= 1; w >>= 1) {
+    if ((int)tid < w) s[tid] += s[tid + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *out = s[0];
+  if (tid == 0) *out = s[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -956,7 +989,7 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   const dim3 grid(a.n_chunks);
   if (len_only) {
     hipLaunchKernelGGL((encode_k<L, DITHER, BF16, true>), grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(reduce_k<unsigned long long>, dim3(1), dim3(256), 0, st,
+    hipLaunchKernelGGL(reduce_k<unsigned long long>, dim3(1), dim3(1024), 0, st,
                        (const unsigned long long*)a.partials, a.n_chunks, &a.ws->bits);
     return hipGetLastError();
   }
@@ -1685,7 +1718,7 @@ hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, 
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks == 0) blocks = 1;
   hipLaunchKernelGGL(sumsq_k, dim3((uint32_t)blocks), dim3(256), 0, st, x, bf16 ? 1 : 0, n, partials);
-  hipLaunchKernelGGL(reduce_k<double>, dim3(1), dim3(256), 0, st, (const double*)partials, (uint32_t)blocks, out);
+  hipLaunchKernelGGL(reduce_k<double>, dim3(1), dim3(1024), 0, st, (const double*)partials, (uint32_t)blocks, out);
   return hipGetLastError();
 }
 
