@@ -92,6 +92,113 @@ void orc_rht_forward(const float x[128], const float s[128], float c_enc, float 
 }
 
 /* ------------------------------------------------------------------------ */
+/* The second rotation of Methodology 1: a Haar-uniform random orthogonal   */
+/* 128 x 128 matrix Q (the "QJL" rotation the explainer compares with the   */
+/* RHT for the KV cache; paper abstract, item (i)).  Reading of the recipe:  */
+/* the QR factor with positive diagonal R of a matrix of independent        */
+/* standard normals is Haar distributed [Mezzadri, Notices AMS 54 (2007)].  */
+/*   G[i][j] = g[128 i + j]; pair p = 0..8191 of g from Philox4x32-10       */
+/*   (counter (p, 0, 0, "HAAR"), key = seed): u1 = (r0 + 1) / 2^32,        */
+/*   u2 = r1 / 2^32, g[2p] = sqrt(-2 ln u1) cos(2 pi u2), g[2p+1] = ... sin  */
+/*   (Box-Muller), in double;                                               */
+/*   Q = Gram-Schmidt of the columns of G (modified form, dot products and  */
+/*   updates in index order, double), which gives R_jj > 0; rounded to fp32. */
+/* The rotated tile is u = Q x / alpha, computed as u_i = fl32(t_i c_enc)   */
+/* with t_i the fp32 fma chain over j = 0..127 of Q[i][j] x_j and            */
+/* c_enc = fp32(1 / alpha) (Q is orthonormal: no 1/sqrt(n)); the inverse is */
+/* x_i = fl32(t'_i c_dec), t'_i the fp32 fma chain of Q[j][i] u_j, c_dec =  */
+/* alpha.                                                                   */
+/* ------------------------------------------------------------------------ */
+#define ORC_TAG_HAAR 0x48414152u /* "HAAR" */
+
+void orc_haar(uint64_t seed, float q32[128 * 128]) {
+  double *g = (double *)malloc(sizeof(double) * N * N);
+  double *q = (double *)malloc(sizeof(double) * N * N);
+  double v[N];
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  for (uint32_t p = 0; p < N * N / 2; ++p) {
+    const uint32_t ctr[4] = {p, 0u, 0u, ORC_TAG_HAAR};
+    uint32_t r[4];
+    orc_philox4x32_10(ctr, key, r);
+    const double u1 = ((double)r[0] + 1.0) / 4294967296.0;
+    const double u2 = (double)r[1] / 4294967296.0;
+    const double rad = sqrt(-2.0 * log(u1)), ang = 6.283185307179586 * u2;
+    g[2 * p] = rad * cos(ang);
+    g[2 * p + 1] = rad * sin(ang);
+  }
+  for (int j = 0; j < N; ++j) {
+    for (int i = 0; i < N; ++i) v[i] = g[i * N + j];
+    for (int c = 0; c < j; ++c) {
+      double r = 0.0;
+      for (int i = 0; i < N; ++i) r = r + q[i * N + c] * v[i];
+      for (int i = 0; i < N; ++i) v[i] = v[i] - r * q[i * N + c];
+    }
+    double nrm = 0.0;
+    for (int i = 0; i < N; ++i) nrm = nrm + v[i] * v[i];
+    nrm = sqrt(nrm);
+    for (int i = 0; i < N; ++i) q[i * N + j] = v[i] / nrm;
+  }
+  for (int i = 0; i < N * N; ++i) q32[i] = (float)q[i];
+  free(g);
+  free(q);
+}
+
+/* The rotation of a plan: the RHT (signs s, c_enc = 1/(alpha sqrt n)) or the
+ * Haar matrix (c_enc = 1/alpha). */
+typedef struct {
+  int haar;
+  float s[N];
+  float c_enc, c_dec;
+  float *q; /* haar: 128 x 128, row-major */
+} rot_ctx;
+
+static int ctx_init(rot_ctx *r, int rot, uint64_t seed, float alpha) {
+  r->haar = rot;
+  r->q = NULL;
+  if (rot == 0) {
+    orc_signs(seed, r->s);
+    orc_scales(alpha, &r->c_enc, &r->c_dec);
+    return ORC_OK;
+  }
+  if (rot != 1) return ORC_ERR_ARG;
+  r->q = (float *)malloc(sizeof(float) * N * N);
+  if (!r->q) return ORC_ERR_ARG;
+  orc_haar(seed, r->q);
+  r->c_enc = (float)(1.0 / (double)alpha);
+  r->c_dec = alpha;
+  return ORC_OK;
+}
+
+static void ctx_free(rot_ctx *r) { free(r->q); }
+
+static void ctx_forward(const rot_ctx *r, const float x[N], float u[N]) {
+  if (!r->haar) {
+    orc_rht_forward(x, r->s, r->c_enc, u);
+    return;
+  }
+  for (int i = 0; i < N; ++i) {
+    float t = 0.0f;
+    for (int j = 0; j < N; ++j) t = fmaf(r->q[i * N + j], x[j], t);
+    u[i] = t * r->c_enc;
+  }
+}
+
+static void ctx_inverse(const rot_ctx *r, float v[N]) {
+  if (!r->haar) {
+    orc_fwht128(v);
+    for (int i = 0; i < N; ++i) v[i] = r->s[i] * (v[i] * r->c_dec);
+    return;
+  }
+  float out[N];
+  for (int i = 0; i < N; ++i) {
+    float t = 0.0f;
+    for (int j = 0; j < N; ++j) t = fmaf(r->q[j * N + i], v[j], t);
+    out[i] = t * r->c_dec;
+  }
+  memcpy(v, out, sizeof(out));
+}
+
+/* ------------------------------------------------------------------------ */
 /* Nearest points [HQ-explainer, Methodology 2; SPLAG ch. 20]               */
 /* Integer embeddings (reading): Z; D4 = {x in Z^4 : sum even};             */
 /* E8 as 2E8 = {x in Z^8 : all x_i of one parity, sum = 0 mod 4}            */
@@ -343,13 +450,13 @@ static float load_elem(const void *x, int dtype, uint64_t i) {
   return ((const float *)x)[i];
 }
 
-static int quantize_tile_s(int lat, uint64_t seed, const float s[128], float c_enc,
+static int quantize_tile_s(int lat, uint64_t seed, const rot_ctx *r,
                            const float x[128], int dithered, uint64_t tile_id,
                            int32_t codes[128]) {
   for (int i = 0; i < N; ++i)
     if (!isfinite(x[i])) return ORC_ERR_NONFINITE;
   float u[N];
-  orc_rht_forward(x, s, c_enc, u);
+  ctx_forward(r, x, u);
   if (dithered) {
     float d[N];
     orc_dither(lat, seed, tile_id, d);
@@ -365,10 +472,9 @@ static int quantize_tile_s(int lat, uint64_t seed, const float s[128], float c_e
 int orc_quantize_tile(int lat, uint64_t seed, float alpha, const float x[128],
                       int dithered, uint64_t tile_id, int32_t codes[128]) {
   if (lat_dim(lat) == 0 || !(alpha > 0.0f) || !isfinite(alpha)) return ORC_ERR_ARG;
-  float s[N], c_enc, c_dec;
-  orc_signs(seed, s);
-  orc_scales(alpha, &c_enc, &c_dec);
-  return quantize_tile_s(lat, seed, s, c_enc, x, dithered, tile_id, codes);
+  rot_ctx r;
+  ctx_init(&r, 0, seed, alpha);
+  return quantize_tile_s(lat, seed, &r, x, dithered, tile_id, codes);
 }
 
 /* Codes of a tile -> zigzag symbols (vector-major) and raw bits. */
@@ -424,11 +530,17 @@ uint64_t orc_write_record_codes(int lat, const int32_t codes[128], uint32_t *wor
 int orc_encode(int lat, uint64_t seed, float alpha, const void *x, int dtype,
                uint64_t n_tiles, int dithered, uint64_t tile_base,
                uint32_t *words, uint64_t cap_words, uint64_t *offsets, uint8_t *k) {
+  return orc_encode_r(lat, seed, alpha, 0, x, dtype, n_tiles, dithered, tile_base, words, cap_words,
+                      offsets, k);
+}
+
+int orc_encode_r(int lat, uint64_t seed, float alpha, int rot, const void *x, int dtype,
+                 uint64_t n_tiles, int dithered, uint64_t tile_base,
+                 uint32_t *words, uint64_t cap_words, uint64_t *offsets, uint8_t *k) {
   if (lat_dim(lat) == 0 || !(alpha > 0.0f) || !isfinite(alpha)) return ORC_ERR_ARG;
   if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
-  float s[N], c_enc, c_dec;
-  orc_signs(seed, s);
-  orc_scales(alpha, &c_enc, &c_dec);
+  rot_ctx r;
+  if (ctx_init(&r, rot, seed, alpha) != ORC_OK) return ORC_ERR_ARG;
   int status = ORC_OK;
   uint64_t off = 0, zeroed = 0; /* words [0, zeroed) have been cleared */
   offsets[0] = 0;
@@ -437,8 +549,11 @@ int orc_encode(int lat, uint64_t seed, float alpha, const void *x, int dtype,
     int32_t codes[N];
     uint32_t m[N], raw;
     for (int i = 0; i < N; ++i) xt[i] = load_elem(x, dtype, t * N + (uint64_t)i);
-    int st = quantize_tile_s(lat, seed, s, c_enc, xt, dithered, tile_base + t, codes);
-    if (st != ORC_OK) return st;
+    int st = quantize_tile_s(lat, seed, &r, xt, dithered, tile_base + t, codes);
+    if (st != ORC_OK) {
+      ctx_free(&r);
+      return st;
+    }
     int raw_bits = tile_symbols(lat, codes, m, &raw);
     int kt = orc_rice_kstar(m, raw_bits);
     uint64_t L = orc_rice_len(m, kt, raw_bits);
@@ -454,26 +569,35 @@ int orc_encode(int lat, uint64_t seed, float alpha, const void *x, int dtype,
     off = end;
     offsets[t + 1] = off;
   }
+  ctx_free(&r);
   return status;
 }
 
 int orc_total_bits(int lat, uint64_t seed, float alpha, const void *x, int dtype,
                    uint64_t n_tiles, int dithered, uint64_t tile_base, uint64_t *bits) {
+  return orc_total_bits_r(lat, seed, alpha, 0, x, dtype, n_tiles, dithered, tile_base, bits);
+}
+
+int orc_total_bits_r(int lat, uint64_t seed, float alpha, int rot, const void *x, int dtype,
+                     uint64_t n_tiles, int dithered, uint64_t tile_base, uint64_t *bits) {
   if (lat_dim(lat) == 0 || !(alpha > 0.0f) || !isfinite(alpha)) return ORC_ERR_ARG;
-  float s[N], c_enc, c_dec;
-  orc_signs(seed, s);
-  orc_scales(alpha, &c_enc, &c_dec);
+  rot_ctx r;
+  if (ctx_init(&r, rot, seed, alpha) != ORC_OK) return ORC_ERR_ARG;
   uint64_t total = 0;
   for (uint64_t t = 0; t < n_tiles; ++t) {
     float xt[N];
     int32_t codes[N];
     uint32_t m[N], raw;
     for (int i = 0; i < N; ++i) xt[i] = load_elem(x, dtype, t * N + (uint64_t)i);
-    int st = quantize_tile_s(lat, seed, s, c_enc, xt, dithered, tile_base + t, codes);
-    if (st != ORC_OK) return st;
+    int st = quantize_tile_s(lat, seed, &r, xt, dithered, tile_base + t, codes);
+    if (st != ORC_OK) {
+      ctx_free(&r);
+      return st;
+    }
     int raw_bits = tile_symbols(lat, codes, m, &raw);
     total += orc_rice_len(m, orc_rice_kstar(m, raw_bits), raw_bits);
   }
+  ctx_free(&r);
   *bits = total;
   return ORC_OK;
 }
@@ -570,11 +694,16 @@ static uint16_t f32_to_bf16_rne(float f) {
 int orc_decode(int lat, uint64_t seed, float alpha, const uint32_t *words,
                const uint64_t *offsets, const uint8_t *k, uint64_t n_tiles,
                int dithered, uint64_t tile_base, void *y, int dtype) {
+  return orc_decode_r(lat, seed, alpha, 0, words, offsets, k, n_tiles, dithered, tile_base, y, dtype);
+}
+
+int orc_decode_r(int lat, uint64_t seed, float alpha, int rot, const uint32_t *words,
+                 const uint64_t *offsets, const uint8_t *k, uint64_t n_tiles,
+                 int dithered, uint64_t tile_base, void *y, int dtype) {
   if (lat_dim(lat) == 0 || !(alpha > 0.0f) || !isfinite(alpha)) return ORC_ERR_ARG;
   if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
-  float s[N], c_enc, c_dec;
-  orc_signs(seed, s);
-  orc_scales(alpha, &c_enc, &c_dec);
+  rot_ctx r;
+  if (ctx_init(&r, rot, seed, alpha) != ORC_OK) return ORC_ERR_ARG;
   int status = ORC_OK;
   for (uint64_t t = 0; t < n_tiles; ++t) {
     int32_t codes[N];
@@ -585,14 +714,14 @@ int orc_decode(int lat, uint64_t seed, float alpha, const uint32_t *words,
       for (int i = 0; i < N; ++i) v[i] = 0.0f;
     } else {
       dequant_codes(lat, seed, codes, dithered, tile_base + t, v);
-      orc_fwht128(v);
-      for (int i = 0; i < N; ++i) v[i] = s[i] * (v[i] * c_dec);
+      ctx_inverse(&r, v);
     }
     for (int i = 0; i < N; ++i) {
       if (dtype == ORC_BF16) ((uint16_t *)y)[t * N + (uint64_t)i] = f32_to_bf16_rne(v[i]);
       else ((float *)y)[t * N + (uint64_t)i] = v[i];
     }
   }
+  ctx_free(&r);
   return status;
 }
 
@@ -789,10 +918,10 @@ int orc_gemv(int lat, uint64_t seed, float alpha, const uint32_t *words, const u
 /* until it is within 0.002 bps, at most 40 times.  The fp32 alpha with the  */
 /* closest rate wins; ties go to the larger alpha.                           */
 /* ------------------------------------------------------------------------ */
-static double rate_at(int lat, uint64_t seed, float a, const void *x, int dtype,
+static double rate_at(int lat, uint64_t seed, float a, int rot, const void *x, int dtype,
                       uint64_t n_tiles, int dithered, uint64_t tile_base, int *st) {
   uint64_t bits = 0;
-  *st = orc_total_bits(lat, seed, a, x, dtype, n_tiles, dithered, tile_base, &bits);
+  *st = orc_total_bits_r(lat, seed, a, rot, x, dtype, n_tiles, dithered, tile_base, &bits);
   if (*st == ORC_ERR_RANGE) return INFINITY; /* step too fine: treat as too many bits */
   return (double)bits / ((double)n_tiles * (double)N);
 }
@@ -800,6 +929,13 @@ static double rate_at(int lat, uint64_t seed, float a, const void *x, int dtype,
 int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,
                   uint64_t n_tiles, int dithered, uint64_t tile_base,
                   float *alpha_out, double *bps_out, int *iters_out) {
+  return orc_calibrate_r(lat, seed, bps, 0, x, dtype, n_tiles, dithered, tile_base, alpha_out, bps_out,
+                         iters_out);
+}
+
+int orc_calibrate_r(int lat, uint64_t seed, float bps, int rot, const void *x, int dtype,
+                    uint64_t n_tiles, int dithered, uint64_t tile_base,
+                    float *alpha_out, double *bps_out, int *iters_out) {
   if (lat_dim(lat) == 0 || n_tiles == 0 || !(bps > 0.0f)) return ORC_ERR_ARG;
   double ss = 0.0;
   uint64_t n = n_tiles * (uint64_t)N;
@@ -827,7 +963,7 @@ int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,
   } while (0)
   for (int g = 0; g < 16; ++g) { /* lo must give a rate >= target */
     float a = (float)exp2(lo);
-    double r = rate_at(lat, seed, a, x, dtype, n_tiles, dithered, tile_base, &st);
+    double r = rate_at(lat, seed, a, rot, x, dtype, n_tiles, dithered, tile_base, &st);
     ++iters;
     if (st != ORC_OK && st != ORC_ERR_RANGE) return st;
     if (st == ORC_OK) CONSIDER(a, r);
@@ -836,7 +972,7 @@ int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,
   }
   for (int g = 0; g < 16; ++g) { /* hi must give a rate <= target */
     float a = (float)exp2(hi);
-    double r = rate_at(lat, seed, a, x, dtype, n_tiles, dithered, tile_base, &st);
+    double r = rate_at(lat, seed, a, rot, x, dtype, n_tiles, dithered, tile_base, &st);
     ++iters;
     if (st != ORC_OK && st != ORC_ERR_RANGE) return st;
     if (st == ORC_OK) CONSIDER(a, r);
@@ -846,7 +982,7 @@ int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,
   for (int it = 0; it < 40 && best_err > 0.002; ++it) {
     double mid = 0.5 * (lo + hi);
     float a = (float)exp2(mid);
-    double r = rate_at(lat, seed, a, x, dtype, n_tiles, dithered, tile_base, &st);
+    double r = rate_at(lat, seed, a, rot, x, dtype, n_tiles, dithered, tile_base, &st);
     ++iters;
     if (st != ORC_OK && st != ORC_ERR_RANGE) return st;
     if (st == ORC_OK) CONSIDER(a, r);

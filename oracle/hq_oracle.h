@@ -142,6 +142,20 @@ int orc_gemv(int lat, uint64_t seed, float alpha, const uint32_t *words, const u
 
 /* Rate calibration: bisection on log2(alpha) for the payload rate
  * (bits per scalar).  Returns an ORC_ status. */
+/* Haar rotation variant (rot = 1; rot = 0 is the RHT): the matrix and the
+ * codec calls with a rotation argument. */
+void orc_haar(uint64_t seed, float q32[128 * 128]);
+int orc_encode_r(int lat, uint64_t seed, float alpha, int rot, const void *x, int dtype,
+                 uint64_t n_tiles, int dithered, uint64_t tile_base,
+                 uint32_t *words, uint64_t cap_words, uint64_t *offsets, uint8_t *k);
+int orc_total_bits_r(int lat, uint64_t seed, float alpha, int rot, const void *x, int dtype,
+                     uint64_t n_tiles, int dithered, uint64_t tile_base, uint64_t *bits);
+int orc_decode_r(int lat, uint64_t seed, float alpha, int rot, const uint32_t *words,
+                 const uint64_t *offsets, const uint8_t *k, uint64_t n_tiles,
+                 int dithered, uint64_t tile_base, void *y, int dtype);
+int orc_calibrate_r(int lat, uint64_t seed, float bps, int rot, const void *x, int dtype,
+                    uint64_t n_tiles, int dithered, uint64_t tile_base,
+                    float *alpha_out, double *bps_out, int *iters_out);
 uint32_t orc_crc32(const uint8_t *p, size_t n);
 void orc_header_write(int lat, uint64_t seed, float alpha, float bps, int dithered, int compact, uint64_t tile_base,
                       uint64_t n_tiles, uint64_t total_bits, uint8_t out[64]);

@@ -83,6 +83,11 @@ def lib():
             "orc_dequant_rotated_many": (_i, [_i, _u64, _p, _p, _p, _u64, _i, _u64, _p]),
             "orc_kv_scores": (_i, [_i, _u64, _f, _p, _p, _p, _u32, _u64, _u64, _p, _u32, _p]),
             "orc_calibrate": (_i, [_i, _u64, _f, _p, _i, _u64, _i, _u64, _p, _p, _p]),
+            "orc_haar": (None, [_u64, _p]),
+            "orc_encode_r": (_i, [_i, _u64, _f, _i, _p, _i, _u64, _i, _u64, _p, _u64, _p, _p]),
+            "orc_total_bits_r": (_i, [_i, _u64, _f, _i, _p, _i, _u64, _i, _u64, _p]),
+            "orc_decode_r": (_i, [_i, _u64, _f, _i, _p, _p, _p, _u64, _i, _u64, _p, _i]),
+            "orc_calibrate_r": (_i, [_i, _u64, _f, _i, _p, _i, _u64, _i, _u64, _p, _p, _p]),
             "orc_crc32": (C.c_uint32, [_p, C.c_size_t]),
             "orc_header_write": (None, [_i, _u64, _f, _f, _i, _i, _u64, _u64, _u64, _p]),
             "orc_side_pack": (_i, [_p, _p, _u64, _p]),
@@ -239,8 +244,9 @@ def bound_words(lat: int, n_tiles: int) -> int:
 
 
 def encode(lat: int, seed: int, alpha: float, x: np.ndarray, dithered=False, tile_base=0,
-           cap_words: int | None = None):
-    """Returns (status, words, offsets, k).  x: fp32 or bf16 bits, size % 128 == 0."""
+           cap_words: int | None = None, rot: int = 0):
+    """Returns (status, words, offsets, k).  x: fp32 or bf16 bits, size % 128 == 0.
+    rot: 0 the RHT, 1 the Haar rotation."""
     xa, dt = _as_input(x)
     n_tiles = xa.size // TILE
     assert xa.size == n_tiles * TILE
@@ -248,18 +254,18 @@ def encode(lat: int, seed: int, alpha: float, x: np.ndarray, dithered=False, til
     words = np.zeros(max(cap, 1), np.uint32)
     offsets = np.zeros(n_tiles + 1, np.uint64)
     k = np.zeros(max(n_tiles, 1), np.uint8)
-    st = lib().orc_encode(lat, seed, alpha, _ptr(xa), dt, n_tiles, int(dithered), tile_base,
-                          _ptr(words), cap, _ptr(offsets), _ptr(k))
+    st = lib().orc_encode_r(lat, seed, alpha, rot, _ptr(xa), dt, n_tiles, int(dithered), tile_base,
+                            _ptr(words), cap, _ptr(offsets), _ptr(k))
     nwords = (int(offsets[-1]) + 31) // 32
     return st, words[:min(nwords, cap)], offsets, k[:n_tiles]
 
 
-def total_bits(lat: int, seed: int, alpha: float, x: np.ndarray, dithered=False, tile_base=0):
+def total_bits(lat: int, seed: int, alpha: float, x: np.ndarray, dithered=False, tile_base=0, rot: int = 0):
     xa, dt = _as_input(x)
     n_tiles = xa.size // TILE
     bits = C.c_uint64(0)
-    st = lib().orc_total_bits(lat, seed, alpha, _ptr(xa), dt, n_tiles, int(dithered), tile_base,
-                              C.byref(bits))
+    st = lib().orc_total_bits_r(lat, seed, alpha, rot, _ptr(xa), dt, n_tiles, int(dithered), tile_base,
+                                C.byref(bits))
     return st, bits.value
 
 
@@ -271,7 +277,7 @@ def parse_tile(lat: int, words: np.ndarray, off: int, end: int, k: int):
 
 
 def decode(lat: int, seed: int, alpha: float, words, offsets, k, dithered=False, tile_base=0,
-           out_dtype=F32):
+           out_dtype=F32, rot: int = 0):
     words = np.ascontiguousarray(words, dtype=np.uint32)
     if words.size == 0:
         words = np.zeros(1, np.uint32)
@@ -279,9 +285,9 @@ def decode(lat: int, seed: int, alpha: float, words, offsets, k, dithered=False,
     k = np.ascontiguousarray(k, dtype=np.uint8)
     n_tiles = offsets.size - 1
     y = np.zeros(n_tiles * TILE, np.float32 if out_dtype == F32 else np.uint16)
-    st = lib().orc_decode(lat, seed, alpha, _ptr(words), _ptr(offsets),
-                          _ptr(k if k.size else np.zeros(1, np.uint8)), n_tiles,
-                          int(dithered), tile_base, _ptr(y), out_dtype)
+    st = lib().orc_decode_r(lat, seed, alpha, rot, _ptr(words), _ptr(offsets),
+                            _ptr(k if k.size else np.zeros(1, np.uint8)), n_tiles,
+                            int(dithered), tile_base, _ptr(y), out_dtype)
     return st, y
 
 
@@ -345,13 +351,20 @@ def kv_attention(lat: int, seed: int, alpha_k: float, kstream, k_tile_base: int,
     return st, out.reshape(n_heads * qph, TILE)
 
 
-def calibrate(lat: int, seed: int, bps: float, x: np.ndarray, dithered=False, tile_base=0):
+def calibrate(lat: int, seed: int, bps: float, x: np.ndarray, dithered=False, tile_base=0, rot: int = 0):
     xa, dt = _as_input(x)
     n_tiles = xa.size // TILE
     a, r, it = C.c_float(0), C.c_double(0), C.c_int(0)
-    st = lib().orc_calibrate(lat, seed, bps, _ptr(xa), dt, n_tiles, int(dithered), tile_base,
-                             C.byref(a), C.byref(r), C.byref(it))
+    st = lib().orc_calibrate_r(lat, seed, bps, rot, _ptr(xa), dt, n_tiles, int(dithered), tile_base,
+                               C.byref(a), C.byref(r), C.byref(it))
     return st, a.value, r.value, it.value
+
+
+def haar(seed: int) -> np.ndarray:
+    """The Haar rotation of a seed: fp32 [128, 128], u = Q x."""
+    q = np.zeros(TILE * TILE, np.float32)
+    lib().orc_haar(seed, _ptr(q))
+    return q.reshape(TILE, TILE)
 
 
 def crc32(data: bytes) -> int:
