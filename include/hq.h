@@ -79,6 +79,26 @@ typedef struct hq_plan_s* hq_plan_t;
  * hq_calibrate.  The plan is host memory owned by the library. */
 hq_status hq_plan(hq_lattice lattice, int tile, float bps, uint64_t seed, hq_plan_t* out);
 
+/* The rotation of Methodology 1 [and the Haar-uniform "QJL" rotation the
+ * explainer compares it with for the KV cache]: kind 0 = the RHT H D (the
+ * default), kind 1 = a Haar-distributed random orthogonal Q made from the
+ * plan's seed (Gram-Schmidt of Philox/Box-Muller normals in double, rounded to
+ * fp32).  With Q: u = fl32(t c_enc), t_i the fp32 fma chain over j of
+ * Q[i][j] x_j in index order, c_enc = fp32(1/alpha); decode x = fl32(t'
+ * alpha), t' the chain of Q[j][i] u_j.  Kind 1 needs dev_buf: hq_rotation_bytes()
+ * bytes of caller-owned device memory, 16-byte aligned, kept for the plan's
+ * life (the call uploads Q^T and Q and synchronises stream).  Encode, decode,
+ * their KV and append variants and calibration follow the plan; hq_kv_scores,
+ * hq_gemv, hq_gemm and hq_kv_attention (which fold the RHT into the other
+ * operand) return HQ_ERR_ARG for a Haar plan.  The workspace of a Haar plan is
+ * larger (hq_workspace_bytes counts 512 bytes per tile more).
+ * hq_plan_get_rotation: the kind, and if q is not NULL the Haar matrix of the
+ * plan's seed (128 x 128 fp32, row-major, host memory; computed on the host,
+ * whatever the current kind). */
+size_t hq_rotation_bytes(void);
+hq_status hq_plan_set_rotation(hq_plan_t plan, int kind, void* dev_buf, void* stream);
+hq_status hq_plan_get_rotation(hq_plan_t plan, int* kind, float* q);
+
 /* Fix the lattice scale alpha (> 0, finite) [Methodology 2]. */
 hq_status hq_plan_set_alpha(hq_plan_t plan, float alpha);
 
@@ -235,17 +255,19 @@ hq_status hq_side_unpack(const void* side, uint64_t n_tiles, uint64_t* offsets, 
 /* Container header: 64 bytes in HOST memory that make a stream
  * self-describing (the plan, the KV tile base, sizes), little-endian:
  *   0 magic "HQS1" | 4 version u16 = 1 | 6 lattice u8 | 7 flags u8 (bit 0
- *   dithered, bit 1 compact side information) | 8 tile u32 = 128 | 12 alpha
+ *   dithered, bit 1 compact side information, bit 2 Haar rotation) | 8 tile
+ *   u32 = 128 | 12 alpha
  *   f32 | 16 target bps f32 | 20 zero u32 | 24 seed u64 | 32 tile_base u64 |
  *   40 n_tiles u64 | 48 total bits u64 | 56 zero u32 | 60 CRC-32 (IEEE 802.3)
  *   of bytes 0..59.
  * hq_header_read returns HQ_ERR_CORRUPT for a wrong magic, version, checksum
  * or field; hq_plan_from_header makes the plan (alpha set) that decodes the
- * stream. */
+ * stream (for a Haar rotation, hq_plan_set_rotation must follow). */
 #define HQ_HEADER_BYTES 64
 typedef struct {
   hq_lattice lattice;
   int dithered, compact_side, tile;
+  int rotation;  /* 1: the Haar rotation (hq_plan_set_rotation) */
   float alpha, bps;
   uint64_t seed, tile_base, n_tiles, total_bits;
 } hq_header_info;

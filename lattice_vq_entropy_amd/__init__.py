@@ -55,6 +55,9 @@ _SIGNATURES = {
     "hq_kv_attention_workspace_bytes": (C.c_size_t, [_u32, _u64, _u32]),
     "hq_kv_attention": (_i, [_p, _p, _u64, _p, _p, _u64, _p, _p, _u64, _p, _p, _u64, _u32, _u64, _p, _u32, C.c_float,
                              _p, _p, _p]),
+    "hq_rotation_bytes": (C.c_size_t, []),
+    "hq_plan_set_rotation": (_i, [_p, _i, _p, _p]),
+    "hq_plan_get_rotation": (_i, [_p, C.POINTER(_i), _p]),
     "hq_side_bytes": (C.c_size_t, [_u64]),
     "hq_side_pack": (_i, [_p, _p, _u64, _p, _p, _p]),
     "hq_side_unpack": (_i, [_p, _u64, _p, _p, _p]),
@@ -71,7 +74,7 @@ HEADER_BYTES = 64
 class HeaderInfo(C.Structure):
     """hq_header_info."""
     _fields_ = [("lattice", C.c_int), ("dithered", C.c_int), ("compact_side", C.c_int), ("tile", C.c_int),
-                ("alpha", C.c_float), ("bps", C.c_float), ("seed", C.c_uint64), ("tile_base", C.c_uint64),
+                ("rotation", C.c_int), ("alpha", C.c_float), ("bps", C.c_float), ("seed", C.c_uint64), ("tile_base", C.c_uint64),
                 ("n_tiles", C.c_uint64), ("total_bits", C.c_uint64)]
 
 
@@ -168,6 +171,26 @@ class Plan:
     @property
     def handle(self):
         return self._h
+
+    def set_rotation(self, kind: int, device="cuda", stream=None):
+        """hq_plan_set_rotation: 0 the RHT, 1 the Haar rotation (its device copy is
+        held by this object for the plan's life)."""
+        buf = None
+        if kind == 1:
+            buf = torch.empty(int(lib().hq_rotation_bytes()), dtype=torch.uint8, device=device)
+        _check(lib().hq_plan_set_rotation(self._h, int(kind), _dptr(buf), _stream(stream) if buf is not None
+                                          else C.c_void_p(0)), "hq_plan_set_rotation")
+        self._rot_buf = buf
+        return self
+
+    def rotation(self):
+        """(kind, the Haar matrix of the plan's seed as fp32 [128, 128])."""
+        import numpy as np
+        kind = C.c_int(0)
+        q = np.zeros(TILE * TILE, np.float32)
+        _check(lib().hq_plan_get_rotation(self._h, C.byref(kind), q.ctypes.data_as(C.c_void_p)),
+               "hq_plan_get_rotation")
+        return kind.value, q.reshape(TILE, TILE)
 
     def set_alpha(self, alpha: float):
         _check(lib().hq_plan_set_alpha(self._h, float(alpha)), "hq_plan_set_alpha")
@@ -411,6 +434,8 @@ def load(data: bytes, device="cuda", extra_tiles: int = 0):
     import numpy as np
     info = header_read(data)
     plan = Plan.from_header(data)
+    if info.rotation:
+        plan.set_rotation(1, device=device)
     n, total = int(info.n_tiles), int(info.total_bits)
     pos = HEADER_BYTES
     words = torch.zeros(max(plan.bound_words(n + extra_tiles), 1), dtype=torch.int32, device=device)

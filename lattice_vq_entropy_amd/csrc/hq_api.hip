@@ -20,6 +20,9 @@ struct hq_plan_s {
   float alpha, c_enc, c_dec;
   uint32_t sgn[4];              // bit c: coordinate c of D is -1
   uint32_t sl16[4], sl32[4];    // the same in the kernels' lane layouts
+  int rot;                      // 0: the RHT; 1: the Haar matrix
+  float* q;                     // Haar: Q (128 x 128 fp32, row-major, host), owned by the plan
+  float* dq;                    // Haar: device copy (caller's memory): Q^T, then Q
 };
 
 namespace {
@@ -49,6 +52,59 @@ bool lattice_ok(int lat) { return lat >= HQ_Z && lat <= HQ_E8; }
 
 hq_status dev_err(hipError_t e) { return e == hipSuccess ? HQ_OK : HQ_ERR_DEVICE; }
 
+// The fp32 scale constants for alpha: the RHT folds 1/sqrt(128) in, the
+// (orthonormal) Haar matrix does not.
+void plan_scales(hq_plan_s* p, float alpha) {
+  if (p->rot == 1) {
+    p->c_enc = (float)(1.0 / (double)alpha);
+    p->c_dec = alpha;
+  } else {
+    p->c_enc = (float)(1.0 / ((double)alpha * std::sqrt(128.0)));
+    p->c_dec = (float)((double)alpha / std::sqrt(128.0));
+  }
+}
+
+// The Haar rotation of a seed [reading of the QJL rotation the explainer
+// compares with the RHT; Mezzadri, Notices AMS 54 (2007)]: G = 128 x 128
+// standard normals, pair p from Philox4x32-10 (counter (p, 0, 0, "HAAR"),
+// key = seed) by Box-Muller in double; Q = modified Gram-Schmidt of G's
+// columns (dot products and updates in index order, double), so R has a
+// positive diagonal and Q is Haar distributed; rounded to fp32, row-major.
+constexpr uint32_t kTagHaar = 0x48414152u;  // "HAAR"
+void haar_host(uint64_t seed, float* q32) {
+  const int n = 128;
+  double* g = new double[n * n];
+  double* q = new double[n * n];
+  for (uint32_t p = 0; p < (uint32_t)(n * n / 2); ++p) {
+    uint32_t c[4] = {p, 0u, 0u, kTagHaar};
+    philox_host(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    const double u1 = ((double)c[0] + 1.0) / 4294967296.0;
+    const double u2 = (double)c[1] / 4294967296.0;
+    const double rad = std::sqrt(-2.0 * std::log(u1)), ang = 6.283185307179586 * u2;
+    g[2 * p] = rad * std::cos(ang);
+    g[2 * p + 1] = rad * std::sin(ang);
+  }
+  double v[128];
+  for (int j = 0; j < n; ++j) {
+    for (int i = 0; i < n; ++i) v[i] = g[i * n + j];
+    for (int c = 0; c < j; ++c) {
+      double r = 0.0;
+      for (int i = 0; i < n; ++i) r = r + q[i * n + c] * v[i];
+      for (int i = 0; i < n; ++i) v[i] = v[i] - r * q[i * n + c];
+    }
+    double nrm = 0.0;
+    for (int i = 0; i < n; ++i) nrm = nrm + v[i] * v[i];
+    nrm = std::sqrt(nrm);
+    for (int i = 0; i < n; ++i) q[i * n + j] = v[i] / nrm;
+  }
+  for (int i = 0; i < n * n; ++i) q32[i] = (float)q[i];
+  delete[] g;
+  delete[] q;
+}
+
+// Workspace: the rotated tiles (fp32) of a Haar plan follow the codec regions.
+uint64_t rot_buffer_offset(uint64_t n_tiles) { return hq::ws_align(hq::ws_bytes(n_tiles)); }
+
 // The signs of D (bit c of the 128: coordinate c is -1) in the two layouts the
 // kernels read.  The lane holding vector v (coordinates 8v..8v+7) takes word
 // v >> 2, in slot j = v & 3: for bf16 pairs, bit 15 - 4j - i is coordinate
@@ -76,7 +132,7 @@ void fill_common(const hq_plan_s* p, uint32_t sl16[4], uint32_t sl32[4], uint32_
 
 hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, bool dither,
                       uint64_t tile_base, uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k,
-                      void* ws, void* stream, bool len_only, bool append = false) {
+                      void* ws, void* stream, bool len_only, bool append = false, bool rotated = false) {
   if (!plan) return HQ_ERR_ARG;
   if (!plan->has_alpha) return HQ_ERR_NOALPHA;
   if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_ARG;
@@ -113,7 +169,26 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   a.stage = (uint32_t*)((char*)ws + lay.stage);
   a.partials = (unsigned long long*)a.E;
   a.base = append ? offsets : nullptr;
-  return dev_err(hq::launch_encode(plan->lattice, dither, dtype == HQ_BF16, len_only, a, st));
+  int in = dtype == HQ_BF16 ? 1 : 0;
+  if (plan->rot == 1) {  // the dense rotation first (skipped when the caller has it in the workspace)
+    float* rbuf = (float*)((char*)ws + rot_buffer_offset(n_tiles));
+    if (!rotated) {
+      hq::RotArgs r{};
+      r.x = x;
+      r.in_bf16 = dtype == HQ_BF16;
+      r.y = rbuf;
+      r.out_bf16 = 0;
+      r.mt = plan->dq;  // Q^T: Mt[j][i] = Q[i][j]
+      r.scale = 1.0f;
+      r.n_tiles = n_tiles;
+      if (hq::launch_rot(r, st) != hipSuccess) return HQ_ERR_DEVICE;
+    }
+    a.x = rbuf;
+    a.x0 = x;
+    a.x0_bf16 = dtype == HQ_BF16;
+    in = 2;
+  }
+  return dev_err(hq::launch_encode(plan->lattice, dither, in, len_only, a, st));
 }
 
 hq_status decode_impl(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets,
@@ -137,6 +212,22 @@ hq_status decode_impl(hq_plan_t plan, const uint32_t* words, uint64_t n_words, c
   a.tile_base = tile_base;
   a.ws = (hq::WsHeader*)ws;
   const dim3 grid((uint32_t)hq::ws_chunks(n_tiles));
+  if (plan->rot == 1) {  // the codes in the rotated domain, then the dense inverse rotation
+    if (((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+    float* rbuf = (float*)((char*)ws + rot_buffer_offset(n_tiles));
+    a.y = rbuf;
+    if (hq::launch_decode(plan->lattice, dither, hq::kOutRot, a, grid, (hipStream_t)stream) != hipSuccess)
+      return HQ_ERR_DEVICE;
+    hq::RotArgs r{};
+    r.x = rbuf;
+    r.in_bf16 = 0;
+    r.y = y;
+    r.out_bf16 = out_dtype == HQ_BF16;
+    r.mt = plan->dq + 128 * 128;  // Q: Mt[j][i] = Q[j][i] gives Q^T u
+    r.scale = plan->c_dec;
+    r.n_tiles = n_tiles;
+    return dev_err(hq::launch_rot(r, (hipStream_t)stream));
+  }
   return dev_err(hq::launch_decode(plan->lattice, dither, out_dtype == HQ_BF16 ? hq::kOutBf16 : hq::kOutF32, a,
                                    grid, (hipStream_t)stream));
 }
@@ -145,13 +236,14 @@ hq_status decode_impl(hq_plan_t plan, const uint32_t* words, uint64_t n_words, c
 // step is too fine for the 2^20 code range.
 hq_status rate_at(hq_plan_s* p, float a, const void* x, hq_dtype dtype, uint64_t n_tiles, bool dither,
                   uint64_t tile_base, void* ws, hipStream_t st, double* rate) {
-  hq_plan_s q = *p;
+  hq_plan_s q = *p;  // (shares the plan's rotation buffers; nothing is freed)
   q.has_alpha = true;
   q.alpha = a;
-  q.c_enc = (float)(1.0 / ((double)a * std::sqrt(128.0)));
-  q.c_dec = (float)((double)a / std::sqrt(128.0));
+  plan_scales(&q, a);
   hq::WsHeader* h = (hq::WsHeader*)ws;
-  hq_status s = encode_impl(&q, x, dtype, n_tiles, dither, tile_base, nullptr, 0, nullptr, nullptr, ws, st, true);
+  // a Haar plan's rotated tiles are in the workspace already (hq_calibrate)
+  hq_status s = encode_impl(&q, x, dtype, n_tiles, dither, tile_base, nullptr, 0, nullptr, nullptr, ws, st, true,
+                            false, q.rot == 1);
   if (s != HQ_OK) return s;
   unsigned long long bits = 0;
   if (hipMemcpyAsync(&bits, &h->bits, sizeof(bits), hipMemcpyDeviceToHost, st) != hipSuccess) return HQ_ERR_DEVICE;
@@ -224,8 +316,7 @@ hq_status hq_plan(hq_lattice lattice, int tile, float bps, uint64_t seed, hq_pla
 hq_status hq_plan_set_alpha(hq_plan_t plan, float alpha) {
   if (!plan || !(alpha > 0.0f) || !std::isfinite(alpha)) return HQ_ERR_ARG;
   plan->alpha = alpha;
-  plan->c_enc = (float)(1.0 / ((double)alpha * std::sqrt(128.0)));
-  plan->c_dec = (float)((double)alpha / std::sqrt(128.0));
+  plan_scales(plan, alpha);
   plan->has_alpha = true;
   return HQ_OK;
 }
@@ -239,9 +330,61 @@ hq_status hq_plan_get(hq_plan_t plan, float* alpha, float* c_enc, float* c_dec) 
   return HQ_OK;
 }
 
-void hq_plan_destroy(hq_plan_t plan) { delete plan; }
+void hq_plan_destroy(hq_plan_t plan) {
+  if (plan) delete[] plan->q;
+  delete plan;
+}
 
-size_t hq_workspace_bytes(hq_plan_t, uint64_t n_tiles) { return (size_t)hq::ws_bytes(n_tiles); }
+size_t hq_workspace_bytes(hq_plan_t plan, uint64_t n_tiles) {
+  if (plan && plan->rot == 1) return (size_t)(rot_buffer_offset(n_tiles) + 512ull * n_tiles);
+  return (size_t)hq::ws_bytes(n_tiles);
+}
+
+size_t hq_rotation_bytes(void) { return 2 * 128 * 128 * sizeof(float); }
+
+hq_status hq_plan_set_rotation(hq_plan_t plan, int kind, void* dev_buf, void* stream) {
+  if (!plan || (kind != 0 && kind != 1)) return HQ_ERR_ARG;
+  if (kind == 0) {
+    plan->rot = 0;
+    plan->dq = nullptr;
+  } else {
+    if (!dev_buf || ((uintptr_t)dev_buf & 15u) != 0) return HQ_ERR_ARG;
+    if (!plan->q) {
+      plan->q = new (std::nothrow) float[128 * 128];
+      if (!plan->q) return HQ_ERR_ARG;
+      haar_host(plan->seed, plan->q);
+    }
+    float* both = new (std::nothrow) float[2 * 128 * 128];
+    if (!both) return HQ_ERR_ARG;
+    for (int i = 0; i < 128; ++i)
+      for (int j = 0; j < 128; ++j) {
+        both[j * 128 + i] = plan->q[i * 128 + j];    // Q^T (the forward rotation's Mt)
+        both[16384 + i * 128 + j] = plan->q[i * 128 + j];  // Q (the inverse's Mt)
+      }
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e1 = hipMemcpyAsync(dev_buf, both, hq_rotation_bytes(), hipMemcpyHostToDevice, st);
+    const hipError_t e2 = hipStreamSynchronize(st);
+    delete[] both;
+    if (e1 != hipSuccess || e2 != hipSuccess) return HQ_ERR_DEVICE;
+    plan->rot = 1;
+    plan->dq = (float*)dev_buf;
+  }
+  if (plan->has_alpha) plan_scales(plan, plan->alpha);
+  return HQ_OK;
+}
+
+hq_status hq_plan_get_rotation(hq_plan_t plan, int* kind, float* q) {
+  if (!plan) return HQ_ERR_ARG;
+  if (kind) *kind = plan->rot;
+  if (q) {
+    if (plan->q) {
+      for (int i = 0; i < 128 * 128; ++i) q[i] = plan->q[i];
+    } else {
+      haar_host(plan->seed, q);  // (host only: the matrix the seed would give)
+    }
+  }
+  return HQ_OK;
+}
 
 uint64_t hq_encode_bound_words(hq_plan_t plan, uint64_t n_tiles) {
   const int lat = plan ? plan->lattice : HQ_E8;
@@ -289,6 +432,7 @@ hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words, 
                        const float* q, uint32_t qph, float* scores, void* ws, void* stream) {
   if (!plan) return HQ_ERR_ARG;
   if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (plan->rot != 0) return HQ_ERR_ARG;  // fused paths use the RHT
   if (qph == 0 || qph > 16) return HQ_ERR_ARG;
   if (n_heads == 0 || tiles_per_head == 0) return HQ_OK;
   if (!words || !offsets || !k || !q || !scores || !ws) return HQ_ERR_ARG;
@@ -322,6 +466,7 @@ hq_status hq_gemv(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const
                   void* ws, void* stream) {
   if (!plan) return HQ_ERR_ARG;
   if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (plan->rot != 0) return HQ_ERR_ARG;  // fused paths use the RHT
   if (cols == 0 || cols % 128 || nb == 0 || nb > 16) return HQ_ERR_ARG;
   if (rows == 0) return HQ_OK;
   if (!words || !offsets || !k || !x || !y || !ws) return HQ_ERR_ARG;
@@ -387,6 +532,7 @@ hq_status hq_gemm(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const
                   uint64_t rows, uint64_t cols, const float* x, uint32_t nb, float* y, void* ws, void* stream) {
   if (!plan) return HQ_ERR_ARG;
   if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (plan->rot != 0) return HQ_ERR_ARG;  // fused paths use the RHT
   if (plan->lattice == HQ_A2) return HQ_ERR_ARG;  // its codes are not integers
   if (cols == 0 || cols % 128 || nb == 0 || nb > hq::kGemmMaxVec) return HQ_ERR_ARG;
   if (rows == 0) return HQ_OK;
@@ -431,6 +577,7 @@ hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_
                           void* ws, void* stream) {
   if (!plan_k || !plan_v) return HQ_ERR_ARG;
   if (!plan_k->has_alpha || !plan_v->has_alpha) return HQ_ERR_NOALPHA;
+  if (plan_k->rot != 0 || plan_v->rot != 0) return HQ_ERR_ARG;  // fused paths use the RHT
   if (plan_k->lattice != plan_v->lattice || plan_k->seed != plan_v->seed) return HQ_ERR_ARG;
   if (qph == 0 || qph > 16 || !(scale == scale) || scale - scale != 0.0f) return HQ_ERR_ARG;
   if (n_heads == 0) return HQ_OK;
@@ -495,7 +642,7 @@ hq_status hq_header_write(hq_plan_t plan, int dithered, uint64_t tile_base, uint
   put_le(h + 0, 4, kHeaderMagic);
   put_le(h + 4, 2, kHeaderVersion);
   h[6] = (uint8_t)plan->lattice;
-  h[7] = (uint8_t)((dithered ? 1u : 0u) | (compact_side ? 2u : 0u));
+  h[7] = (uint8_t)((dithered ? 1u : 0u) | (compact_side ? 2u : 0u) | (plan->rot == 1 ? 4u : 0u));
   put_le(h + 8, 4, 128u);
   uint32_t ab, bb;
   std::memcpy(&ab, &plan->alpha, 4);
@@ -516,7 +663,7 @@ hq_status hq_header_read(const void* in, hq_header_info* info) {
   const uint8_t* h = (const uint8_t*)in;
   if (get_le(h + 0, 4) != kHeaderMagic || get_le(h + 4, 2) != kHeaderVersion) return HQ_ERR_CORRUPT;
   if (get_le(h + 60, 4) != crc32_ieee(h, 60)) return HQ_ERR_CORRUPT;
-  if (!lattice_ok(h[6]) || (h[7] & ~3u) != 0 || get_le(h + 8, 4) != 128u) return HQ_ERR_CORRUPT;
+  if (!lattice_ok(h[6]) || (h[7] & ~7u) != 0 || get_le(h + 8, 4) != 128u) return HQ_ERR_CORRUPT;
   const uint32_t ab = (uint32_t)get_le(h + 12, 4), bb = (uint32_t)get_le(h + 16, 4);
   std::memcpy(&info->alpha, &ab, 4);
   std::memcpy(&info->bps, &bb, 4);
@@ -525,6 +672,7 @@ hq_status hq_header_read(const void* in, hq_header_info* info) {
   info->lattice = (hq_lattice)h[6];
   info->dithered = h[7] & 1u;
   info->compact_side = (h[7] >> 1) & 1u;
+  info->rotation = (h[7] >> 2) & 1u;
   info->tile = 128;
   info->seed = get_le(h + 24, 8);
   info->tile_base = get_le(h + 32, 8);
@@ -598,6 +746,17 @@ hq_status hq_calibrate(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n
   if (!std::isfinite(ss)) return HQ_ERR_NONFINITE;
   const double sigma = std::sqrt(ss / (double)n);
   if (!(sigma > 0.0)) return HQ_ERR_ARG;
+  if (plan->rot == 1) {  // the dense rotation once; every trial then scales it
+    hq::RotArgs r{};
+    r.x = x;
+    r.in_bf16 = dtype == HQ_BF16;
+    r.y = (float*)((char*)ws + rot_buffer_offset(n_tiles));
+    r.out_bf16 = 0;
+    r.mt = plan->dq;
+    r.scale = 1.0f;
+    r.n_tiles = n_tiles;
+    if (hq::launch_rot(r, st) != hipSuccess) return HQ_ERR_DEVICE;
+  }
   static const double nu[4] = {1.0, 1.8612097182041991, 1.1892071150027210, 2.0};
   const double a0 = std::sqrt(2.0 * M_PI * M_E) * sigma / (nu[plan->lattice] * std::pow(2.0, (double)plan->bps));
   const double target = (double)plan->bps;

@@ -7,7 +7,7 @@
 
 namespace hq {
 
-constexpr int kOutF32 = 0, kOutBf16 = 1, kOutScores = 2, kOutGemv = 3;
+constexpr int kOutF32 = 0, kOutBf16 = 1, kOutScores = 2, kOutGemv = 3, kOutRot = 4;
 
 struct EncArgs {
   const void* x;
@@ -31,6 +31,8 @@ struct EncArgs {
   uint32_t* stage;   // kSlotWords staging words per chunk
   unsigned long long* partials;  // length-only pass: bits per chunk
   const uint64_t* base;  // append: the existing stream's end bit (device), else null
+  const void* x0;        // pre-rotated input (x is the rotated tiles): the original, for error kinds
+  int x0_bf16;
 };
 
 struct PlaceArgs {
@@ -84,7 +86,8 @@ struct GemvArgs {
   float c_dec;
 };
 
-hipError_t launch_encode(int lat, bool dither, bool bf16, bool len_only, const EncArgs& a, hipStream_t st);
+// in: 0 fp32 tiles, 1 bf16 tiles, 2 fp32 tiles already rotated (scaled by c_enc here)
+hipError_t launch_encode(int lat, bool dither, int in, bool len_only, const EncArgs& a, hipStream_t st);
 hipError_t launch_decode(int lat, bool dither, int out, const DecArgs& a, dim3 grid, hipStream_t st);
 // Attention over compressed keys and values (both dithered, one lattice and
 // seed): per work-group one KV head, kAttnQ of its queries and kAttnChunks
@@ -126,6 +129,16 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int lat, const GemmArgs& g, hipStream_t st);
 hipError_t launch_attention(int lat, const AttnArgs& a, uint32_t n_heads, hipStream_t st);
+// Dense rotation of tiles: y = fl32(fma-chain(M x) * scale) per tile, M given
+// as Mt[j][i] (128 x 128 fp32, device).
+struct RotArgs {
+  const void* x; int in_bf16;
+  void* y; int out_bf16;
+  const float* mt;
+  float scale;
+  uint64_t n_tiles;
+};
+hipError_t launch_rot(const RotArgs& a, hipStream_t st);
 hipError_t launch_side(bool pack, const uint64_t* offsets_in, const uint8_t* k_in, const uint8_t* side_in,
                        uint64_t n, uint8_t* side_out, uint64_t* offsets_out, uint8_t* k_out, WsHeader* ws,
                        hipStream_t st);

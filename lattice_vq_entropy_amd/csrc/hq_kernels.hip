@@ -115,17 +115,23 @@ struct TileSyms {
 // RHT -> (dither) -> nearest point -> strip -> zigzag -> Rice k for tile t,
 // held by the 16-lane row of the calling lane.  Every lane of the wave calls
 // it (ballots).  A tile past the end has zero input and L = 0.
-template <int L, bool DITHER, bool BF16>
+template <int L, bool DITHER, bool BF16, bool PRE>
 __device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF16>& lc, const InVec<BF16>& in,
                                            uint64_t t, bool valid, int v, int r, int grp, TileSyms& ts) {
   constexpr uint32_t RAW = Lat<L>::raw;
   float d[8];  // the dither first: its own nearest-point search then runs with only the input in flight
   if constexpr (DITHER) dither_lane<L>(a.key0, a.key1, a.tile_base + t, v, d);
   float u[8];
-  lc.apply(in, u);
-  fwht_tile(u, lc.fs);
+  if constexpr (PRE) {  // already rotated (the Haar matrix): only the scale
+    const uint32_t ww[8] = {in.w0.x, in.w0.y, in.w0.z, in.w0.w, in.w1.x, in.w1.y, in.w1.z, in.w1.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) u[i] = u[i] * lc.scale;
+    for (int i = 0; i < 8; ++i) u[i] = __builtin_bit_cast(float, ww[i]) * a.c_enc;
+  } else {
+    lc.apply(in, u);
+    fwht_tile(u, lc.fs);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = u[i] * lc.scale;
+  }
   if constexpr (DITHER) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[i] = u[i] + d[i];
@@ -140,7 +146,10 @@ __device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF1
     // the error and code it as zeros (the output is unspecified then)
     const bool tile_bad = ((bad_mask >> (grp * 16)) & 0xFFFFull) != 0;
     bool nf = false;
-    if (tile_bad && valid) nf = lane_nonfinite<BF16>(a.x, t, v);
+    if (tile_bad && valid) {
+      if constexpr (PRE) nf = a.x0_bf16 ? lane_nonfinite<true>(a.x0, t, v) : lane_nonfinite<false>(a.x0, t, v);
+      else nf = lane_nonfinite<BF16>(a.x, t, v);
+    }
     const bool tile_nf = ((__ballot(nf) >> (grp * 16)) & 0xFFFFull) != 0;
     if (tile_bad) {
       if (r == 0 && valid) set_status(a.ws, tile_nf ? 2 : 3);
@@ -258,8 +267,9 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
 // chunk, packing into LDS.  Then the chunk's bits go to its staging slot, its
 // bit count to agg, and per tile the chunk-local bit offset and k.  No
 // work-group waits on another.  LEN_ONLY: the chunk's bit count only.
-template <int L, bool DITHER, bool BF16, bool LEN_ONLY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 8 : 1))) void encode_k(EncArgs a) {
+template <int L, bool DITHER, int IN, bool LEN_ONLY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IN == 1 ? 8 : 1))) void encode_k(EncArgs a) {
+  constexpr bool BF16 = IN == 1, PRE = IN == 2;  // input: fp32, bf16, or fp32 already rotated
   __shared__ __align__(16) uint32_t s_stage[kSlotWords];
   __shared__ uint32_t s_len[kChunkTiles], s_lo[kChunkTiles], s_k[kChunkTiles];
 
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 8 : 
       const int slot = p * 16 + pslot;
       const uint64_t t = t_first + slot;
       TileSyms ts;
-      tile_front<L, DITHER, BF16>(a, lc, in[p], t, t < a.n_tiles, v, r, grp, ts);
+      tile_front<L, DITHER, BF16, PRE>(a, lc, in[p], t, t < a.n_tiles, v, r, grp, ts);
       if (r == 0) s_len[slot] = ts.L;
     }
     __syncthreads();
@@ -302,7 +312,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 8 : 
       const uint64_t t = t_first + slot;
       const bool valid = t < a.n_tiles;
       TileSyms ts;
-      tile_front<L, DITHER, BF16>(a, lc, in[p], t, valid, v, r, grp, ts);
+      tile_front<L, DITHER, BF16, PRE>(a, lc, in[p], t, valid, v, r, grp, ts);
       if (r == 0) {
         s_len[slot] = ts.L;
         s_k[slot] = ts.k;
@@ -890,6 +900,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
           if (r == 0) a.scores[(head * a.qph + g) * a.tiles_per_head + sidx] = acc * a.c_dec;
         }
       }
+    } else if constexpr (OUT == kOutRot) {
+      // the dequantised tile in the rotated domain (a dense inverse rotation follows)
+      if (valid) {
+        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + t * kTile + 8 * v);
+        dst[0] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        dst[1] = make_float4(pv[4], pv[5], pv[6], pv[7]);
+      }
     } else {
       fwht_tile(pv, fs);
       if (valid) {
@@ -984,16 +1001,16 @@ __global__ __launch_bounds__(1024) void reduce_k(const T* p, uint32_t n, T* out)
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int L, bool DITHER, bool BF16>
+template <int L, bool DITHER, int IN>
 static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   const dim3 grid(a.n_chunks);
   if (len_only) {
-    hipLaunchKernelGGL((encode_k<L, DITHER, BF16, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((encode_k<L, DITHER, IN, true>), grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL(reduce_k<unsigned long long>, dim3(1), dim3(1024), 0, st,
                        (const unsigned long long*)a.partials, a.n_chunks, &a.ws->bits);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((encode_k<L, DITHER, BF16, false>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((encode_k<L, DITHER, IN, false>), grid, dim3(256), 0, st, a);
   const bool self_scan = a.n_chunks <= kSelfScanChunks;
   // step 2 (two-level): Eloc (u32 per chunk, padded to a multiple of 4) at
   // the start of the E region, the block prefixes (u64) after it
@@ -1026,13 +1043,15 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_encode(int lat, bool dither, bool bf16, bool len_only, const EncArgs& a, hipStream_t st) {
+hipError_t launch_encode(int lat, bool dither, int in, bool len_only, const EncArgs& a, hipStream_t st) {
 #define HQ_ENC(LL)                                                                        \
   if (lat == LL) {                                                                        \
-    if (dither) return bf16 ? launch_encode_t<LL, true, true>(a, len_only, st)            \
-                            : launch_encode_t<LL, true, false>(a, len_only, st);          \
-    return bf16 ? launch_encode_t<LL, false, true>(a, len_only, st)                       \
-                : launch_encode_t<LL, false, false>(a, len_only, st);                     \
+    if (dither) return in == 1   ? launch_encode_t<LL, true, 1>(a, len_only, st)          \
+                       : in == 2 ? launch_encode_t<LL, true, 2>(a, len_only, st)          \
+                                 : launch_encode_t<LL, true, 0>(a, len_only, st);         \
+    return in == 1   ? launch_encode_t<LL, false, 1>(a, len_only, st)                     \
+           : in == 2 ? launch_encode_t<LL, false, 2>(a, len_only, st)                     \
+                     : launch_encode_t<LL, false, 0>(a, len_only, st);                    \
   }
   HQ_ENC(0) HQ_ENC(1) HQ_ENC(2) HQ_ENC(3)
 #undef HQ_ENC
@@ -1043,6 +1062,7 @@ template <int L, bool DITHER>
 static hipError_t launch_decode_t(const DecArgs& a, int out, dim3 grid, hipStream_t st) {
   if (out == kOutBf16) hipLaunchKernelGGL((decode_k<L, DITHER, kOutBf16>), grid, dim3(256), 0, st, a);
   else if (out == kOutF32) hipLaunchKernelGGL((decode_k<L, DITHER, kOutF32>), grid, dim3(256), 0, st, a);
+  else if (out == kOutRot) hipLaunchKernelGGL((decode_k<L, DITHER, kOutRot>), grid, dim3(256), 0, st, a);
   else if constexpr (DITHER) hipLaunchKernelGGL((decode_k<L, true, kOutScores>), grid, dim3(256), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
@@ -1651,6 +1671,96 @@ hipError_t launch_gemm(int lat, const GemmArgs& g, hipStream_t st) {
     const uint64_t n = (uint64_t)g.nb * g.rows;
     hipLaunchKernelGGL(gemm_sum_k, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, g);
   }
+  return hipGetLastError();
+}
+
+// ===========================================================================
+// Dense rotation (the Haar matrix): y_i = fl32(t_i * scale) with t_i the fp32
+// fma chain over j = 0..127 of M[i][j] x_j, in index order, for every tile.
+// Persistent work-groups: the matrix (as Mt[j][i], 64 KB) is loaded into LDS
+// once; per chunk of 32 tiles the inputs go to LDS transposed (Xt[j][t]) and
+// thread (coordinates 4c..4c+3, tiles 4g..4g+3) keeps 16 chains, reading one
+// float4 of each per step.
+// ===========================================================================
+__global__ __launch_bounds__(256) void rot_k(RotArgs a) {
+  __shared__ __align__(16) float s_m[kTile * kTile];  // Mt[128][128] (64 KB: gfx950 has 160 KB per CU)
+  __shared__ __align__(16) float s_x[kTile * 32];     // Xt[128][32]
+  const uint32_t tid = threadIdx.x;
+  for (uint32_t i = tid; i < kTile * kTile / 4; i += 256u)
+    reinterpret_cast<float4*>(s_m)[i] = reinterpret_cast<const float4*>(a.mt)[i];
+  const uint64_t n_chunks = (a.n_tiles + 31) / 32;
+  const uint32_t c4 = 4u * (tid & 31u), g4 = 4u * (tid >> 5);
+  for (uint64_t ch = blockIdx.x; ch < n_chunks; ch += gridDim.x) {
+    // inputs: thread -> tile tid / 8, coordinates 16 (tid % 8) .. + 15
+    {
+      const uint32_t tt = tid >> 3, j0 = 16u * (tid & 7u);
+      const uint64_t t = ch * 32u + tt;
+      float xv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xv[e] = 0.0f;
+      if (t < a.n_tiles) {
+        if (a.in_bf16) {
+          const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + t * kTile + j0);
+          const uint4 w0 = p[0], w1 = p[1];
+          const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xv[2 * e] = __builtin_bit_cast(float, ww[e] << 16);
+            xv[2 * e + 1] = __builtin_bit_cast(float, ww[e] & 0xFFFF0000u);
+          }
+        } else {
+          const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + t * kTile + j0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float4 f = p[e];
+            xv[4 * e] = f.x; xv[4 * e + 1] = f.y; xv[4 * e + 2] = f.z; xv[4 * e + 3] = f.w;
+          }
+        }
+      }
+      __syncthreads();  // (the matrix is in; the previous chunk's inputs are consumed)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s_x[(j0 + e) * 32u + tt] = xv[e];
+    }
+    __syncthreads();
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[i][k] = 0.0f;
+#pragma unroll 4
+    for (uint32_t j = 0; j < kTile; ++j) {
+      const float4 m = *reinterpret_cast<const float4*>(s_m + j * kTile + c4);
+      const float4 x = *reinterpret_cast<const float4*>(s_x + j * 32u + g4);
+      const float mv[4] = {m.x, m.y, m.z, m.w}, xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[i][k] = __builtin_fmaf(mv[i], xw[k], acc[i][k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint64_t t = ch * 32u + g4 + (uint32_t)k;
+      if (t >= a.n_tiles) continue;
+      const float o0 = acc[0][k] * a.scale, o1 = acc[1][k] * a.scale, o2 = acc[2][k] * a.scale,
+                  o3 = acc[3][k] * a.scale;
+      if (a.out_bf16) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        typedef float f32x2_t __attribute__((ext_vector_type(2)));
+        const f32x2_t f01 = {o0, o1}, f23 = {o2, o3};
+        const uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(f01, bf16x2_t)),
+                                    __builtin_bit_cast(uint32_t, __builtin_convertvector(f23, bf16x2_t)));
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + t * kTile + c4) = pk;
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + t * kTile + c4) = make_float4(o0, o1, o2, o3);
+      }
+    }
+  }
+}
+
+hipError_t launch_rot(const RotArgs& a, hipStream_t st) {
+  const uint64_t n_chunks = (a.n_tiles + 31) / 32;
+  const uint32_t grid = (uint32_t)(n_chunks < 512 ? n_chunks : 512);  // two work-groups per CU (LDS)
+  hipLaunchKernelGGL(rot_k, dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

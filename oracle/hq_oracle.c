@@ -1023,8 +1023,17 @@ static void le_store(uint8_t *p, uint64_t v, int n) {
 /* magic "HQS1", version 1, lattice, flags (1 dithered, 2 compact side),
  * tile 128, alpha and bps as fp32 bits, seed, tile base, tile count, total
  * bits, CRC-32 of bytes 0..59 at 60; reserved fields zero. */
+void orc_header_write_r(int lat, uint64_t seed, float alpha, float bps, int dithered, int compact, int rot,
+                        uint64_t tile_base, uint64_t n_tiles, uint64_t total_bits, uint8_t out[64]);
+
 void orc_header_write(int lat, uint64_t seed, float alpha, float bps, int dithered, int compact, uint64_t tile_base,
                       uint64_t n_tiles, uint64_t total_bits, uint8_t out[64]) {
+  orc_header_write_r(lat, seed, alpha, bps, dithered, compact, 0, tile_base, n_tiles, total_bits, out);
+}
+
+/* flags bit 2: the Haar rotation */
+void orc_header_write_r(int lat, uint64_t seed, float alpha, float bps, int dithered, int compact, int rot,
+                        uint64_t tile_base, uint64_t n_tiles, uint64_t total_bits, uint8_t out[64]) {
   uint32_t ab, bb;
   memset(out, 0, 64);
   memcpy(&ab, &alpha, 4);
@@ -1032,7 +1041,7 @@ void orc_header_write(int lat, uint64_t seed, float alpha, float bps, int dither
   out[0] = 'H'; out[1] = 'Q'; out[2] = 'S'; out[3] = '1';
   le_store(out + 4, 1, 2);
   out[6] = (uint8_t)lat;
-  out[7] = (uint8_t)((dithered ? 1 : 0) + (compact ? 2 : 0));
+  out[7] = (uint8_t)((dithered ? 1 : 0) + (compact ? 2 : 0) + (rot ? 4 : 0));
   le_store(out + 8, 128, 4);
   le_store(out + 12, ab, 4);
   le_store(out + 16, bb, 4);

@@ -159,6 +159,8 @@ int orc_calibrate_r(int lat, uint64_t seed, float bps, int rot, const void *x, i
 uint32_t orc_crc32(const uint8_t *p, size_t n);
 void orc_header_write(int lat, uint64_t seed, float alpha, float bps, int dithered, int compact, uint64_t tile_base,
                       uint64_t n_tiles, uint64_t total_bits, uint8_t out[64]);
+void orc_header_write_r(int lat, uint64_t seed, float alpha, float bps, int dithered, int compact, int rot,
+                        uint64_t tile_base, uint64_t n_tiles, uint64_t total_bits, uint8_t out[64]);
 int orc_side_pack(const uint64_t *offsets, const uint8_t *k, uint64_t n, uint8_t *out);
 int orc_calibrate(int lat, uint64_t seed, float bps, const void *x, int dtype,
                   uint64_t n_tiles, int dithered, uint64_t tile_base,

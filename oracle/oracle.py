@@ -90,6 +90,7 @@ def lib():
             "orc_calibrate_r": (_i, [_i, _u64, _f, _i, _p, _i, _u64, _i, _u64, _p, _p, _p]),
             "orc_crc32": (C.c_uint32, [_p, C.c_size_t]),
             "orc_header_write": (None, [_i, _u64, _f, _f, _i, _i, _u64, _u64, _u64, _p]),
+            "orc_header_write_r": (None, [_i, _u64, _f, _f, _i, _i, _i, _u64, _u64, _u64, _p]),
             "orc_side_pack": (_i, [_p, _p, _u64, _p]),
             "orc_gemv": (_i, [_i, _u64, _f, _p, _p, _p, _u64, _u64, _p, _u32, _p]),
             "orc_kv_attention": (_i, [_i, _u64, _f, _p, _p, _p, _u64, _f, _p, _p, _p, _u64, _u32, _u64, _p,
@@ -373,10 +374,10 @@ def crc32(data: bytes) -> int:
 
 
 def header(lat: int, seed: int, alpha: float, bps: float, dithered: bool, compact: bool, tile_base: int,
-           n_tiles: int, total_bits: int) -> bytes:
+           n_tiles: int, total_bits: int, rot: int = 0) -> bytes:
     out = np.zeros(64, np.uint8)
-    lib().orc_header_write(lat, seed, alpha, bps, int(dithered), int(compact), tile_base, n_tiles, total_bits,
-                           _ptr(out))
+    lib().orc_header_write_r(lat, seed, alpha, bps, int(dithered), int(compact), rot, tile_base, n_tiles, total_bits,
+                             _ptr(out))
     return out.tobytes()
 
 

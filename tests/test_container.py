@@ -128,3 +128,20 @@ def test_side_abi(hq):
     assert L.hq_side_pack(D, D, 4, C.c_void_p(4104), D, None) == hq.ERR_ARG  # misaligned side
     assert L.hq_side_unpack(D, 4, None, D, None) == hq.ERR_ARG
     assert L.hq_side_pack(D, D, 0, D, D, None) == hq.OK
+
+
+def test_header_rotation_flag(hq, orc):
+    h = orc.header(2, 7, 0.25, 2.0, True, True, 0, 10, 5000, rot=1)
+    assert h[7] == 1 | 2 | 4
+    info = hq.header_read(h)
+    assert info.rotation == 1 and info.dithered == 1 and info.compact_side == 1
+    assert hq.header_read(orc.header(2, 7, 0.25, 2.0, True, True, 0, 10, 5000)).rotation == 0
+
+
+@pytest.mark.parametrize("seed", [0x5EED0001, 1, 2 ** 63 + 5])
+def test_library_haar_matrix_equals_oracle(hq, orc, seed):
+    """Two implementations of the Haar recipe (Philox normals, Gram-Schmidt in
+    double, fp32 rounding) give the same matrix bit for bit."""
+    kind, q = hq.Plan("D4", 2.0, seed).rotation()
+    assert kind == 0
+    assert np.array_equal(q.view(np.uint32), orc.haar(seed).view(np.uint32))
