@@ -94,10 +94,12 @@ def workload_rows(hq, W, torch, np, iters):
     rows = []
     seed = W.PLAN_SEED
 
-    def codec(name, x, lat, bps, dithered=False, tile_base=0, alpha=None, out_dtype=torch.bfloat16):
+    def codec(name, x, lat, bps, dithered=False, tile_base=0, alpha=None, out_dtype=torch.bfloat16, rot=0):
         n_el = x.numel()
         n_tiles = n_el // 128
         plan = hq.Plan(lat, bps, seed)
+        if rot:
+            plan.set_rotation(rot, device=dev)
         ws = plan.workspace(n_tiles)
         if alpha is None:
             plan.calibrate(x, ws, dithered=dithered, tile_base=tile_base)
@@ -113,6 +115,8 @@ def workload_rows(hq, W, torch, np, iters):
         inb = x.element_size()
         extra = {"lattice": "ZA2D4E8"[[0, 1, 3, 5][lat]:[1, 3, 5, 7][lat]], "bps": round(bits / n_el, 4),
                  "dithered": dithered}
+        if rot:
+            extra["rotation"] = "Haar"
         rows.append(_row(name, "kv_encode" if dithered else "encode", te, n_el, inb, bits, n_tiles, extra))
         rows.append(_row(name, "kv_decode" if dithered else "decode", td, n_el, y.element_size(), bits, n_tiles,
                          extra))
@@ -174,6 +178,7 @@ def workload_rows(hq, W, torch, np, iters):
     k, v, q = W.c3(dev)
     codec("KV bf16 [8,8,32768,128] K", k, 2, 2.0, dithered=True)
     codec("KV bf16 [8,8,32768,128] V", v, 2, 2.0, dithered=True, tile_base=k.numel() // 128)
+    codec("KV bf16 [8,8,32768,128] K, Haar rotation", k, 2, 2.0, dithered=True, rot=1)
     del k, v, q
     torch.cuda.empty_cache()
     x = W.c4(dev)
