@@ -743,16 +743,38 @@ int orc_kv_scores(int lat, uint64_t seed, float alpha, const uint32_t *words,
                   const uint64_t *offsets, const uint8_t *k, uint32_t n_heads,
                   uint64_t tiles_per_head, uint64_t tile_base, const float *q,
                   uint32_t qph, double *scores) {
+  return orc_kv_scores_r(lat, seed, alpha, 0, words, offsets, k, n_heads, tiles_per_head, tile_base, q, qph,
+                         scores);
+}
+
+/* With the Haar rotation (rot = 1): q . k_hat = q . (alpha Q^T u_hat) =
+ * alpha <Q q, u_hat>, in fp64. */
+int orc_kv_scores_r(int lat, uint64_t seed, float alpha, int rot, const uint32_t *words,
+                    const uint64_t *offsets, const uint8_t *k, uint32_t n_heads,
+                    uint64_t tiles_per_head, uint64_t tile_base, const float *q,
+                    uint32_t qph, double *scores) {
   if (lat_dim(lat) == 0 || !(alpha > 0.0f) || qph == 0) return ORC_ERR_ARG;
-  float s[N], c_enc, c_dec;
-  orc_signs(seed, s);
-  orc_scales(alpha, &c_enc, &c_dec);
+  rot_ctx rc;
+  if (ctx_init(&rc, rot, seed, alpha) != ORC_OK) return ORC_ERR_ARG;
+  const float c_dec = rc.c_dec;
   uint32_t nq = n_heads * qph;
   double *qt = (double *)malloc(sizeof(double) * (size_t)nq * N);
-  if (!qt) return ORC_ERR_ARG;
+  if (!qt) {
+    ctx_free(&rc);
+    return ORC_ERR_ARG;
+  }
   for (uint32_t r = 0; r < nq; ++r) {
-    for (int i = 0; i < N; ++i) qt[(size_t)r * N + i] = (double)s[i] * (double)q[(size_t)r * N + i];
-    fwht128_f64(&qt[(size_t)r * N]);
+    const float *qr = &q[(size_t)r * N];
+    if (rot == 0) {
+      for (int i = 0; i < N; ++i) qt[(size_t)r * N + i] = (double)rc.s[i] * (double)qr[i];
+      fwht128_f64(&qt[(size_t)r * N]);
+    } else {
+      for (int i = 0; i < N; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < N; ++j) acc += (double)rc.q[i * N + j] * (double)qr[j];
+        qt[(size_t)r * N + i] = acc;
+      }
+    }
   }
   int status = ORC_OK;
   for (uint32_t h = 0; h < n_heads; ++h) {
@@ -779,6 +801,7 @@ int orc_kv_scores(int lat, uint64_t seed, float alpha, const uint32_t *words,
       }
     }
   }
+  ctx_free(&rc);
   free(qt);
   return status;
 }
@@ -796,7 +819,7 @@ int orc_kv_scores(int lat, uint64_t seed, float alpha, const uint32_t *words,
 /* have their own alpha.  The softmax subtracts the maximum score.  Corrupt  */
 /* records count as zero vectors and set the status.                         */
 /* ------------------------------------------------------------------------ */
-static void recon_f64(int lat, uint64_t seed, const float s[128], float c_dec, const uint32_t *words,
+static void recon_f64(int lat, uint64_t seed, const rot_ctx *rc, float c_dec, const uint32_t *words,
                       const uint64_t *offsets, const uint8_t *k, uint64_t t, uint64_t tile_id, double w[128],
                       int *status) {
   int32_t codes[N];
@@ -808,28 +831,51 @@ static void recon_f64(int lat, uint64_t seed, const float s[128], float c_dec, c
   }
   float uh[N];
   dequant_codes(lat, seed, codes, 1, tile_id, uh);
-  for (int i = 0; i < N; ++i) w[i] = (double)uh[i];
-  fwht128_f64(w);
-  for (int i = 0; i < N; ++i) w[i] = (double)s[i] * ((double)c_dec * w[i]);
+  if (!rc->haar) {
+    for (int i = 0; i < N; ++i) w[i] = (double)uh[i];
+    fwht128_f64(w);
+    for (int i = 0; i < N; ++i) w[i] = (double)rc->s[i] * ((double)c_dec * w[i]);
+  } else { /* alpha Q^T u_hat */
+    for (int i = 0; i < N; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < N; ++j) acc += (double)rc->q[j * N + i] * (double)uh[j];
+      w[i] = (double)c_dec * acc;
+    }
+  }
 }
 
 int orc_kv_attention(int lat, uint64_t seed, float alpha_k, const uint32_t *kw, const uint64_t *ko,
                      const uint8_t *kk, uint64_t k_tile_base, float alpha_v, const uint32_t *vw,
                      const uint64_t *vo, const uint8_t *vk, uint64_t v_tile_base, uint32_t n_heads,
                      uint64_t seq, const float *q, uint32_t qph, float scale, double *out) {
+  return orc_kv_attention_r(lat, seed, 0, alpha_k, kw, ko, kk, k_tile_base, alpha_v, vw, vo, vk, v_tile_base,
+                            n_heads, seq, q, qph, scale, out);
+}
+
+int orc_kv_attention_r(int lat, uint64_t seed, int rot, float alpha_k, const uint32_t *kw, const uint64_t *ko,
+                       const uint8_t *kk, uint64_t k_tile_base, float alpha_v, const uint32_t *vw,
+                       const uint64_t *vo, const uint8_t *vk, uint64_t v_tile_base, uint32_t n_heads,
+                       uint64_t seq, const float *q, uint32_t qph, float scale, double *out) {
   if (lat_dim(lat) == 0 || !(alpha_k > 0.0f) || !(alpha_v > 0.0f) || qph == 0 || seq == 0) return ORC_ERR_ARG;
-  float s[N], c_enc, ck, cv;
-  orc_signs(seed, s);
-  orc_scales(alpha_k, &c_enc, &ck);
-  orc_scales(alpha_v, &c_enc, &cv);
+  rot_ctx rk, rv;
+  if (ctx_init(&rk, rot, seed, alpha_k) != ORC_OK) return ORC_ERR_ARG;
+  if (ctx_init(&rv, rot, seed, alpha_v) != ORC_OK) {
+    ctx_free(&rk);
+    return ORC_ERR_ARG;
+  }
+  const float ck = rk.c_dec, cv = rv.c_dec;
   double *sc = (double *)malloc(sizeof(double) * (size_t)seq * qph);
-  if (!sc) return ORC_ERR_ARG;
+  if (!sc) {
+    ctx_free(&rk);
+    ctx_free(&rv);
+    return ORC_ERR_ARG;
+  }
   int status = ORC_OK;
   for (uint32_t h = 0; h < n_heads; ++h) {
     for (uint64_t j = 0; j < seq; ++j) {
       const uint64_t t = (uint64_t)h * seq + j;
       double kh[N];
-      recon_f64(lat, seed, s, ck, kw, ko, kk, t, k_tile_base + t, kh, &status);
+      recon_f64(lat, seed, &rk, ck, kw, ko, kk, t, k_tile_base + t, kh, &status);
       for (uint32_t g = 0; g < qph; ++g) {
         const float *qr = &q[((size_t)h * qph + g) * N];
         double acc = 0.0;
@@ -848,13 +894,15 @@ int orc_kv_attention(int lat, uint64_t seed, float alpha_k, const uint32_t *kw, 
         const double pj = exp(sg[j] - m);
         l += pj;
         double vh[N];
-        recon_f64(lat, seed, s, cv, vw, vo, vk, (uint64_t)h * seq + j, v_tile_base + (uint64_t)h * seq + j, vh,
+        recon_f64(lat, seed, &rv, cv, vw, vo, vk, (uint64_t)h * seq + j, v_tile_base + (uint64_t)h * seq + j, vh,
                   &status);
         for (int i = 0; i < N; ++i) o[i] += pj * vh[i];
       }
       for (int i = 0; i < N; ++i) o[i] /= l;
     }
   }
+  ctx_free(&rk);
+  ctx_free(&rv);
   free(sc);
   return status;
 }

@@ -156,6 +156,14 @@ int orc_decode_r(int lat, uint64_t seed, float alpha, int rot, const uint32_t *w
 int orc_calibrate_r(int lat, uint64_t seed, float bps, int rot, const void *x, int dtype,
                     uint64_t n_tiles, int dithered, uint64_t tile_base,
                     float *alpha_out, double *bps_out, int *iters_out);
+int orc_kv_scores_r(int lat, uint64_t seed, float alpha, int rot, const uint32_t *words,
+                    const uint64_t *offsets, const uint8_t *k, uint32_t n_heads,
+                    uint64_t tiles_per_head, uint64_t tile_base, const float *q,
+                    uint32_t qph, double *scores);
+int orc_kv_attention_r(int lat, uint64_t seed, int rot, float alpha_k, const uint32_t *kw, const uint64_t *ko,
+                       const uint8_t *kk, uint64_t k_tile_base, float alpha_v, const uint32_t *vw,
+                       const uint64_t *vo, const uint8_t *vk, uint64_t v_tile_base, uint32_t n_heads,
+                       uint64_t seq, const float *q, uint32_t qph, float scale, double *out);
 uint32_t orc_crc32(const uint8_t *p, size_t n);
 void orc_header_write(int lat, uint64_t seed, float alpha, float bps, int dithered, int compact, uint64_t tile_base,
                       uint64_t n_tiles, uint64_t total_bits, uint8_t out[64]);

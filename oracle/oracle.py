@@ -84,6 +84,9 @@ def lib():
             "orc_kv_scores": (_i, [_i, _u64, _f, _p, _p, _p, _u32, _u64, _u64, _p, _u32, _p]),
             "orc_calibrate": (_i, [_i, _u64, _f, _p, _i, _u64, _i, _u64, _p, _p, _p]),
             "orc_haar": (None, [_u64, _p]),
+            "orc_kv_scores_r": (_i, [_i, _u64, _f, _i, _p, _p, _p, _u32, _u64, _u64, _p, _u32, _p]),
+            "orc_kv_attention_r": (_i, [_i, _u64, _i, _f, _p, _p, _p, _u64, _f, _p, _p, _p, _u64, _u32, _u64, _p,
+                                        _u32, _f, _p]),
             "orc_encode_r": (_i, [_i, _u64, _f, _i, _p, _i, _u64, _i, _u64, _p, _u64, _p, _p]),
             "orc_total_bits_r": (_i, [_i, _u64, _f, _i, _p, _i, _u64, _i, _u64, _p]),
             "orc_decode_r": (_i, [_i, _u64, _f, _i, _p, _p, _p, _u64, _i, _u64, _p, _i]),
@@ -314,15 +317,15 @@ def dequant_rotated_many(lat: int, seed: int, words, offsets, k, n: int, dithere
 
 
 def kv_scores(lat: int, seed: int, alpha: float, words, offsets, k, n_heads: int,
-              tiles_per_head: int, tile_base: int, q: np.ndarray, qph: int):
+              tiles_per_head: int, tile_base: int, q: np.ndarray, qph: int, rot: int = 0):
     words = np.ascontiguousarray(words, dtype=np.uint32)
     offsets = np.ascontiguousarray(offsets, dtype=np.uint64)
     k = np.ascontiguousarray(k, dtype=np.uint8)
     q = np.ascontiguousarray(q, dtype=np.float32)
     assert q.size == n_heads * qph * TILE
     scores = np.zeros(n_heads * qph * tiles_per_head, np.float64)
-    st = lib().orc_kv_scores(lat, seed, alpha, _ptr(words), _ptr(offsets), _ptr(k), n_heads,
-                             tiles_per_head, tile_base, _ptr(q), qph, _ptr(scores))
+    st = lib().orc_kv_scores_r(lat, seed, alpha, rot, _ptr(words), _ptr(offsets), _ptr(k), n_heads,
+                               tiles_per_head, tile_base, _ptr(q), qph, _ptr(scores))
     return st, scores.reshape(n_heads * qph, tiles_per_head)
 
 
@@ -339,7 +342,7 @@ def gemv(lat: int, seed: int, alpha: float, words, offsets, k, rows: int, cols: 
 
 
 def kv_attention(lat: int, seed: int, alpha_k: float, kstream, k_tile_base: int, alpha_v: float, vstream,
-                 v_tile_base: int, n_heads: int, seq: int, q: np.ndarray, qph: int, scale: float):
+                 v_tile_base: int, n_heads: int, seq: int, q: np.ndarray, qph: int, scale: float, rot: int = 0):
     """softmax(scale q . k_hat) v_hat per query in fp64; streams are (words, offsets, k).
     Returns (status, out [n_heads*qph, 128])."""
     kw, ko, kk = (np.ascontiguousarray(a, dtype=d) for a, d in zip(kstream, (np.uint32, np.uint64, np.uint8)))
@@ -347,8 +350,9 @@ def kv_attention(lat: int, seed: int, alpha_k: float, kstream, k_tile_base: int,
     q = np.ascontiguousarray(q, dtype=np.float32)
     assert q.size == n_heads * qph * TILE
     out = np.zeros(n_heads * qph * TILE, np.float64)
-    st = lib().orc_kv_attention(lat, seed, alpha_k, _ptr(kw), _ptr(ko), _ptr(kk), k_tile_base, alpha_v, _ptr(vw),
-                                _ptr(vo), _ptr(vk), v_tile_base, n_heads, seq, _ptr(q), qph, scale, _ptr(out))
+    st = lib().orc_kv_attention_r(lat, seed, rot, alpha_k, _ptr(kw), _ptr(ko), _ptr(kk), k_tile_base, alpha_v,
+                                  _ptr(vw), _ptr(vo), _ptr(vk), v_tile_base, n_heads, seq, _ptr(q), qph, scale,
+                                  _ptr(out))
     return st, out.reshape(n_heads * qph, TILE)
 
 

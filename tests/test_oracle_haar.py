@@ -109,3 +109,55 @@ def test_haar_calibration_hits_the_rate(orc):
     assert st == 0 and abs(rate - 2.0) <= 0.002
     st, bits = orc.total_bits(2, SEED, alpha, x, dithered=True, rot=1)
     assert st == 0 and abs(bits / x.size - rate) < 1e-12
+
+
+@pytest.mark.parametrize("lat", [2, 3])
+def test_haar_scores_equal_query_dot_decoded_key(orc, lat):
+    """alpha <Q q, u_hat> (the rotated-domain score) equals q . k_hat with
+    k_hat the Haar decoder's fp32 reconstruction, to its rounding."""
+    rng = np.random.default_rng(3400 + lat)
+    H, S, qph = 2, 30, 3
+    kx = rng.standard_normal((H * S, 128)).astype(np.float32)
+    q = rng.standard_normal((H * qph, 128)).astype(np.float32)
+    alpha = 0.4
+    st, w, off, k = orc.encode(lat, SEED, alpha, kx, dithered=True, tile_base=70, rot=1)
+    assert st == 0
+    st, sc = orc.kv_scores(lat, SEED, alpha, w, off, k, H, S, 70, q, qph, rot=1)
+    assert st == 0
+    st, y = orc.decode(lat, SEED, alpha, w, off, k, dithered=True, tile_base=70, rot=1)
+    khat = y.reshape(H, S, 128).astype(np.float64)
+    want = np.einsum("hgi,hsi->hgs", q.reshape(H, qph, 128).astype(np.float64), khat).reshape(H * qph, S)
+    scale = np.linalg.norm(q, axis=1)[:, None] * np.linalg.norm(khat.reshape(H * S, 128), axis=1).reshape(H, S).repeat(qph, 0)
+    assert np.all(np.abs(sc - want) <= 1e-5 * scale)
+    # and not the RHT's scores
+    st, sr = orc.kv_scores(lat, SEED, alpha, w, off, k, H, S, 70, q, qph, rot=0)
+    assert np.abs(sr - want).max() > 1e-2 * scale.max()
+
+
+def test_haar_attention_one_key_and_uniform(orc):
+    """With the Haar rotation: one key gives its value's reconstruction; scale 0
+    gives the mean of the values' reconstructions."""
+    rng = np.random.default_rng(3500)
+    H, S, qph, lat, ak, av = 2, 20, 2, 3, 0.5, 0.4
+    kx = rng.standard_normal((H * S, 128)).astype(np.float32)
+    vx = rng.standard_normal((H * S, 128)).astype(np.float32)
+    q = rng.standard_normal((H * qph, 128)).astype(np.float32)
+    st, kw, ko, kk = orc.encode(lat, SEED, ak, kx, dithered=True, tile_base=0, rot=1)
+    st2, vw, vo, vk = orc.encode(lat, SEED, av, vx, dithered=True, tile_base=H * S, rot=1)
+    assert st == 0 and st2 == 0
+    st, vd = orc.decode(lat, SEED, av, vw, vo, vk, dithered=True, tile_base=H * S, rot=1)
+    vd = vd.reshape(H, S, 128).astype(np.float64)
+    tol = 256 * 2.0 ** -24 * np.abs(vd).max()
+    st, o = orc.kv_attention(lat, SEED, ak, (kw, ko, kk), 0, av, (vw, vo, vk), H * S, H, S, q, qph, 0.0, rot=1)
+    assert st == 0
+    np.testing.assert_allclose(o.reshape(H, qph, 128), np.repeat(vd.mean(axis=1)[:, None, :], qph, axis=1),
+                               rtol=0, atol=tol)
+    # one key per head: the streams of keys 0 and S (first of each head), as 1-tile heads
+    for h in range(H):
+        t = h * S
+        ks = (kw, ko[t:t + 2], kk[t:t + 1])
+        vs = (vw, vo[t:t + 2], vk[t:t + 1])
+        st, o1 = orc.kv_attention(lat, SEED, ak, ks, t, av, vs, H * S + t, 1, 1, q[h * qph:(h + 1) * qph], qph, 0.3,
+                                  rot=1)
+        assert st == 0
+        np.testing.assert_allclose(o1, np.repeat(vd[h, 0][None, :], qph, axis=0), rtol=0, atol=tol)
