@@ -88,10 +88,12 @@ hq_status hq_plan(hq_lattice lattice, int tile, float bps, uint64_t seed, hq_pla
  * alpha), t' the chain of Q[j][i] u_j.  Kind 1 needs dev_buf: hq_rotation_bytes()
  * bytes of caller-owned device memory, 16-byte aligned, kept for the plan's
  * life (the call uploads Q^T and Q and synchronises stream).  Encode, decode,
- * their KV and append variants and calibration follow the plan; hq_kv_scores,
- * hq_gemv, hq_gemm and hq_kv_attention (which fold the RHT into the other
- * operand) return HQ_ERR_ARG for a Haar plan.  The workspace of a Haar plan is
- * larger (hq_workspace_bytes counts 512 bytes per tile more).
+ * their KV and append variants, calibration, hq_kv_scores and hq_kv_attention
+ * follow the plan (the two fused KV paths rotate the queries with Q, and the
+ * attention rotates its result back with Q^T, by the same fp32 chains);
+ * hq_gemv and hq_gemm (which fold the RHT into the vectors) return
+ * HQ_ERR_ARG for a Haar plan.  The workspace of a Haar plan is larger
+ * (hq_workspace_bytes counts 512 bytes per tile more).
  * hq_plan_get_rotation: the kind, and if q is not NULL the Haar matrix of the
  * plan's seed (128 x 128 fp32, row-major, host memory; computed on the host,
  * whatever the current kind). */
@@ -166,7 +168,15 @@ hq_status hq_kv_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
  * them: scores[(h*qph + g)*tiles_per_head + s] = q_{h,g} . k_hat_{h,s}
  * = c_dec <H D q_{h,g}, u_hat_{h,s}> for the keys of n_heads heads stored as
  * tiles h*tiles_per_head + s of one encode (tile ids tile_base + that).
- * q: fp32 [n_heads*qph][128]; scores: fp32.  qph <= 16. */
+ * With a Haar plan, = alpha <Q q_{h,g}, u_hat_{h,s}> (Q orthogonal): the
+ * queries are rotated first, by a launch of their own, into the workspace.
+ * q: fp32 [n_heads*qph][128] (16-byte aligned for a Haar plan); scores: fp32
+ * [n_heads*qph][tiles_per_head].  1 <= qph <= 16.  ws: at least
+ * hq_kv_scores_workspace_bytes(plan, n_heads, tiles_per_head, qph) bytes
+ * (the codec workspace of the n_heads * tiles_per_head tiles suffices unless a
+ * Haar plan has qph > tiles_per_head), zero-filled once, 16-byte aligned for a
+ * Haar plan.  Corrupt records score 0 and set HQ_ERR_CORRUPT. */
+size_t hq_kv_scores_workspace_bytes(hq_plan_t plan, uint32_t n_heads, uint64_t tiles_per_head, uint32_t qph);
 hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
                        const uint64_t* offsets, const uint8_t* k, uint32_t n_heads,
                        uint64_t tiles_per_head, uint64_t tile_base, const float* q,
@@ -217,14 +227,18 @@ hq_status hq_gemm(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
  *   out[h*qph + g] = sum_s softmax_s(scale * q_{h,g} . k_hat_{h,s}) v_hat_{h,s}
  * for the keys and values of head h stored as tiles h*seq + s of one
  * hq_kv_encode each (tile ids k_tile_base + that and v_tile_base + that).
- * plan_k and plan_v hold each stream's alpha and must share lattice and seed.
- * q: fp32 [n_heads*qph][128] (finite); out: fp32 [n_heads*qph][128];
+ * plan_k and plan_v hold each stream's alpha and must share lattice, seed and
+ * rotation kind.  With Haar plans the scores are alpha_K <Q q, u_hat_K> and
+ * the output Q^T (alpha_V sum_j p_j u_hat_V,j / L): two more launches rotate
+ * the queries (into the workspace) and the result.
+ * q: fp32 [n_heads*qph][128] (finite); out: fp32 [n_heads*qph][128] (both
+ * 16-byte aligned for Haar plans);
  * 1 <= qph <= 16; scale finite.  The weighted sums are formed in the rotated
  * domain by work-groups of 256 keys (maximum, weights e^(s - m) and their sum
  * per group) and combined per query in a fixed order, so results are
  * deterministic.  ws: at least hq_kv_attention_workspace_bytes(n_heads, seq,
  * qph) bytes, 16-byte aligned, zero-filled once.  Two stream-ordered
- * launches.  Records that do not parse count as zero vectors (score
+ * launches (four with Haar plans).  Records that do not parse count as zero vectors (score
  * scale * 0) and set HQ_ERR_CORRUPT. */
 size_t hq_kv_attention_workspace_bytes(uint32_t n_heads, uint64_t seq, uint32_t qph);
 hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_n_words,

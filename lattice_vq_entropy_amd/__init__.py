@@ -45,6 +45,7 @@ _SIGNATURES = {
     "hq_decode": (_i, [_p, _p, _u64, _p, _p, _u64, _p, _i, _p, _p]),
     "hq_kv_encode": (_i, [_p, _p, _i, _u64, _u64, _p, _u64, _p, _p, _p, _p]),
     "hq_kv_decode": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _i, _p, _p]),
+    "hq_kv_scores_workspace_bytes": (C.c_size_t, [_p, _u32, _u64, _u32]),
     "hq_kv_scores": (_i, [_p, _p, _u64, _p, _p, _u32, _u64, _u64, _p, _u32, _p, _p, _p]),
     "hq_gemv_workspace_bytes": (C.c_size_t, [_u64, _u64, _u32]),
     "hq_gemv": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _u32, _p, _p, _p]),
@@ -301,6 +302,9 @@ def kv_scores(plan: Plan, enc: Encoded, n_heads: int, tiles_per_head: int, q: to
     """hq_kv_scores: fp32 [n_heads*qph, tiles_per_head] = q . k_hat without materialising k_hat."""
     if q.dtype != torch.float32 or q.numel() != n_heads * qph * TILE:
         raise ValueError("q must be fp32 [n_heads*qph, 128]")
+    need = int(lib().hq_kv_scores_workspace_bytes(plan.handle, n_heads, tiles_per_head, qph))
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes, {need} needed")
     s = out if out is not None else torch.empty(n_heads * qph, tiles_per_head, dtype=torch.float32,
                                                 device=q.device)
     rc = lib().hq_kv_scores(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),

@@ -427,17 +427,27 @@ hq_status hq_kv_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words, 
   return decode_impl(plan, words, n_words, offsets, k, n_tiles, true, tile_base, y, out_dtype, ws, stream);
 }
 
+size_t hq_kv_scores_workspace_bytes(hq_plan_t plan, uint32_t n_heads, uint64_t tiles_per_head, uint32_t qph) {
+  const uint64_t n = (uint64_t)n_heads * tiles_per_head;
+  if (plan && plan->rot == 1) {  // the rotated queries follow the codec's regions
+    const uint64_t a = hq_workspace_bytes(plan, n), b = rot_buffer_offset(n) + 512ull * n_heads * qph;
+    return (size_t)(a > b ? a : b);
+  }
+  return (size_t)hq::ws_bytes(n);
+}
+
 hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets,
                        const uint8_t* k, uint32_t n_heads, uint64_t tiles_per_head, uint64_t tile_base,
                        const float* q, uint32_t qph, float* scores, void* ws, void* stream) {
   if (!plan) return HQ_ERR_ARG;
   if (!plan->has_alpha) return HQ_ERR_NOALPHA;
-  if (plan->rot != 0) return HQ_ERR_ARG;  // fused paths use the RHT
+  if (plan->rot != 0 && plan->rot != 1) return HQ_ERR_ARG;
   if (qph == 0 || qph > 16) return HQ_ERR_ARG;
   if (n_heads == 0 || tiles_per_head == 0) return HQ_OK;
   if (!words || !offsets || !k || !q || !scores || !ws) return HQ_ERR_ARG;
   const uint64_t cph = (tiles_per_head + hq::kChunkTiles - 1) / hq::kChunkTiles;
   if (cph > 0x7FFFFFFFull || n_heads > 65535u) return HQ_ERR_ARG;
+  if (plan->rot == 1 && ((((uintptr_t)q | (uintptr_t)ws) & 15u) != 0)) return HQ_ERR_ARG;
   hq::DecArgs a{};
   a.words = words;
   a.n_words = n_words;
@@ -452,6 +462,20 @@ hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words, 
   a.scores = scores;
   a.qph = qph;
   a.tiles_per_head = tiles_per_head;
+  if (plan->rot == 1) {  // q~ = Q q (fp32 chains, as the encoder rotates the keys) into the workspace
+    float* qr = (float*)((char*)ws + rot_buffer_offset(a.n_tiles));
+    hq::RotArgs r{};
+    r.x = q;
+    r.in_bf16 = 0;
+    r.y = qr;
+    r.out_bf16 = 0;
+    r.mt = plan->dq;  // Q^T: Mt[j][i] = Q[i][j]
+    r.scale = 1.0f;
+    r.n_tiles = (uint64_t)n_heads * qph;
+    if (hq::launch_rot(r, (hipStream_t)stream) != hipSuccess) return HQ_ERR_DEVICE;
+    a.q = qr;
+    a.q_rot = 1;
+  }
   return dev_err(hq::launch_decode(plan->lattice, true, hq::kOutScores, a, dim3((uint32_t)cph, n_heads),
                                    (hipStream_t)stream));
 }
@@ -565,9 +589,17 @@ hq_status hq_gemm(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const
   return dev_err(hq::launch_gemm(plan->lattice, g, (hipStream_t)stream));
 }
 
-size_t hq_kv_attention_workspace_bytes(uint32_t n_heads, uint64_t seq, uint32_t qph) {
+namespace {
+// The attention workspace: [header][partials][per query 128 floats: the
+// rotated queries, then the pre-image of the output (dense rotation only)].
+uint64_t attn_qbuf_offset(uint32_t n_heads, uint64_t seq, uint32_t qph) {
   const uint64_t groups = (seq + hq::kAttnChunks * hq::kChunkTiles - 1) / (hq::kAttnChunks * hq::kChunkTiles);
-  return (size_t)(sizeof(hq::WsHeader) + 4ull * n_heads * groups * qph * hq::kAttnPart);
+  return hq::ws_align(sizeof(hq::WsHeader) + 4ull * n_heads * groups * qph * hq::kAttnPart);
+}
+}  // namespace
+
+size_t hq_kv_attention_workspace_bytes(uint32_t n_heads, uint64_t seq, uint32_t qph) {
+  return (size_t)(attn_qbuf_offset(n_heads, seq, qph) + 512ull * n_heads * qph);
 }
 
 hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_n_words, const uint64_t* k_offsets,
@@ -577,13 +609,14 @@ hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_
                           void* ws, void* stream) {
   if (!plan_k || !plan_v) return HQ_ERR_ARG;
   if (!plan_k->has_alpha || !plan_v->has_alpha) return HQ_ERR_NOALPHA;
-  if (plan_k->rot != 0 || plan_v->rot != 0) return HQ_ERR_ARG;  // fused paths use the RHT
+  if (plan_k->rot != plan_v->rot || (plan_k->rot != 0 && plan_k->rot != 1)) return HQ_ERR_ARG;
   if (plan_k->lattice != plan_v->lattice || plan_k->seed != plan_v->seed) return HQ_ERR_ARG;
   if (qph == 0 || qph > 16 || !(scale == scale) || scale - scale != 0.0f) return HQ_ERR_ARG;
   if (n_heads == 0) return HQ_OK;
   if (seq == 0 || !k_words || !k_offsets || !k_k || !v_words || !v_offsets || !v_k || !q || !out || !ws)
     return HQ_ERR_ARG;
   if (((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+  if (plan_k->rot == 1 && ((((uintptr_t)q | (uintptr_t)out) & 15u) != 0)) return HQ_ERR_ARG;
   const uint64_t groups = (seq + hq::kAttnChunks * hq::kChunkTiles - 1) / (hq::kAttnChunks * hq::kChunkTiles);
   if (n_heads > 65535u || groups > 0x7FFFFFFFull || seq > (1ull << 40)) return HQ_ERR_ARG;
   hq::AttnArgs a{};
@@ -609,7 +642,26 @@ hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_
   a.ws = (hq::WsHeader*)ws;
   a.part = (float*)((char*)ws + sizeof(hq::WsHeader));
   a.out = out;
-  return dev_err(hq::launch_attention(plan_k->lattice, a, n_heads, (hipStream_t)stream));
+  if (plan_k->rot == 0) return dev_err(hq::launch_attention(plan_k->lattice, a, n_heads, (hipStream_t)stream));
+  // dense rotation: q~ = Q q into the workspace; the combine leaves c_dec_V A / L
+  // there (the rotated queries are consumed by then) and rot_k applies Q^T
+  const hipStream_t st = (hipStream_t)stream;
+  float* qb = (float*)((char*)ws + attn_qbuf_offset(n_heads, seq, qph));
+  hq::RotArgs r{};
+  r.x = q;
+  r.y = qb;
+  r.mt = plan_k->dq;  // Q^T: Mt[j][i] = Q[i][j]
+  r.scale = 1.0f;
+  r.n_tiles = (uint64_t)n_heads * qph;
+  if (hq::launch_rot(r, st) != hipSuccess) return HQ_ERR_DEVICE;
+  a.q = qb;
+  a.q_rot = 1;
+  a.rot_out = qb;
+  if (hq::launch_attention(plan_k->lattice, a, n_heads, st) != hipSuccess) return HQ_ERR_DEVICE;
+  r.x = qb;
+  r.y = out;
+  r.mt = plan_v->dq + 128 * 128;  // Q: Mt[j][i] = Q[j][i] gives Q^T y
+  return dev_err(hq::launch_rot(r, st));
 }
 
 size_t hq_side_bytes(uint64_t n_tiles) { return (size_t)(96ull * ((n_tiles + 31) / 32)); }

@@ -68,6 +68,7 @@ struct DecArgs {
   float* scores;
   uint32_t qph;
   uint64_t tiles_per_head;
+  int q_rot;  // the queries are already rotated (dense rotation: Q q), else H D q is formed here
   // matrix-vector mode: rotated vector blocks H D x (nb x cols fp32), per-tile
   // dot products (n_tiles x nb fp32), vectors per call, 128-column blocks per row
   const float* xr;
@@ -101,6 +102,8 @@ struct AttnArgs {
   uint32_t sl32[4];
   uint32_t key0, key1;
   const float* q;
+  int q_rot;          // the queries are already rotated (dense rotation: Q q)
+  float* rot_out;     // dense rotation: c_dec_V A / L per query, for rot_k with Q^T (else null)
   uint32_t qph;
   float scale;
   uint64_t seq;

@@ -800,17 +800,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
   if (tid <= (int)nt) s_off[tid] = a.offsets[t_first + tid];
   if (tid < (int)nt) s_k[tid] = a.kin[t_first + tid];
   if constexpr (OUT == kOutScores) {
-    // rotate the head's queries: q~ = H D q, one query per 16-lane row
+    // rotate the head's queries: q~ = H D q, one query per 16-lane row (with
+    // a dense rotation the queries arrive rotated: q~ = Q q)
     const int g = wv * 4 + grp;
     if (g < (int)a.qph) {
       const float* qp = a.q + ((head * a.qph + g) * kTile + 8 * v);
-      const uint32_t sm = lane_signs32(a.sl32, v);
-      float xq[8];
+      if (a.q_rot) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xq[i] = __builtin_bit_cast(float, fbits(qp[i]) ^ ((sm << i) & 0x80000000u));
-      fwht_tile(xq, fs);
+        for (int i = 0; i < 8; ++i) s_q[g][8 * v + i] = qp[i];
+      } else {
+        const uint32_t sm = lane_signs32(a.sl32, v);
+        float xq[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s_q[g][8 * v + i] = xq[i] * fs.lane_sign;
+        for (int i = 0; i < 8; ++i) xq[i] = __builtin_bit_cast(float, fbits(qp[i]) ^ ((sm << i) & 0x80000000u));
+        fwht_tile(xq, fs);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_q[g][8 * v + i] = xq[i] * fs.lane_sign;
+      }
     }
   }
   __syncthreads();
@@ -1158,13 +1164,18 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 
   if (wv == 0 && grp < (int)nq) {  // rotate the queries: q~ = H D q (row-uniform branch)
     const float* qp = a.q + ((head * a.qph + q0 + grp) * kTile + 8 * v);
-    const uint32_t sm = lane_signs32(a.sl32, v);
-    float xq[8];
+    if (a.q_rot) {  // a dense rotation: the queries arrive rotated, q~ = Q q
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xq[i] = __builtin_bit_cast(float, fbits(qp[i]) ^ ((sm << i) & 0x80000000u));
-    fwht_tile(xq, fs);
+      for (int i = 0; i < 8; ++i) s_q[grp][8 * v + i] = qp[i];
+    } else {
+      const uint32_t sm = lane_signs32(a.sl32, v);
+      float xq[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s_q[grp][8 * v + i] = xq[i] * fs.lane_sign;
+      for (int i = 0; i < 8; ++i) xq[i] = __builtin_bit_cast(float, fbits(qp[i]) ^ ((sm << i) & 0x80000000u));
+      fwht_tile(xq, fs);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s_q[grp][8 * v + i] = xq[i] * fs.lane_sign;
+    }
   } else if (wv == 0) {  // unused query rows score zero
 #pragma unroll
     for (int i = 0; i < 8; ++i) s_q[grp][8 * v + i] = 0.0f;
@@ -1299,7 +1310,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 // groups of its head: M = max m_c, L = sum l_c e^(m_c - M), A = sum acc_c
 // e^(m_c - M).  Thread (slice, i) sums coordinate i over the groups c = slice
 // mod 8 in order; the 8 slices are then added as a fixed pairwise tree.  The
-// output out = D H (c_dec_V A / L) is formed by one 16-lane row.
+// output out = D H (c_dec_V A / L) is formed by one 16-lane row (with a dense
+// rotation, c_dec_V A / L is written to rot_out and rotated back by rot_k).
 __global__ __launch_bounds__(1024) void attn_combine_k(AttnArgs a) {
   __shared__ float s_red[16];
   __shared__ float s_a[8][kTile];
@@ -1354,6 +1366,14 @@ __global__ __launch_bounds__(1024) void attn_combine_k(AttnArgs a) {
       const int c = 8 * v + j;
       x[j] = (((s_a[0][c] + s_a[1][c]) + (s_a[2][c] + s_a[3][c])) + ((s_a[4][c] + s_a[5][c]) + (s_a[6][c] + s_a[7][c]))) *
              f;
+    }
+    if (a.rot_out) {  // a dense rotation: c_dec_V A / L goes to its inverse rotation (Q^T) instead
+      if (lane < 16) {
+        float4* o = reinterpret_cast<float4*>(a.rot_out + (uint64_t)hg * kTile + 8 * v);
+        o[0] = make_float4(x[0], x[1], x[2], x[3]);
+        o[1] = make_float4(x[4], x[5], x[6], x[7]);
+      }
+      return;
     }
     fwht_tile(x, fs);
     const uint32_t sm = lane_signs32(a.sl32, v);

@@ -97,6 +97,10 @@ def test_argument_errors_are_synchronous(hq):
     assert A(*args(pk, pv, seq=0)) == hq.ERR_ARG
     assert A(*args(pk, pv, ws=C.c_void_p(4104))) == hq.ERR_ARG                      # misaligned workspace
     assert A(*args(pk, pv, n_heads=0)) == hq.OK                                      # no heads: nothing to do
-    # workspace: header, then per head, group of 256 keys and query the maximum, the sum and 128 values
-    assert L.hq_kv_attention_workspace_bytes(2, 300, 4) == 256 + 4 * 2 * 2 * 4 * 130
-    assert L.hq_kv_attention_workspace_bytes(8, 131072, 4) == 256 + 4 * 8 * 512 * 4 * 130
+    # workspace: header, then per head, group of 256 keys and query the maximum, the sum and 128 values,
+    # then (256-byte aligned) 128 floats per query for the dense rotation's queries and result
+    al = lambda b: (b + 255) // 256 * 256
+    # scores with the RHT: the codec workspace of the keys' tiles
+    assert L.hq_kv_scores_workspace_bytes(pk.handle, 2, 300, 4) == pk.workspace_bytes(600)
+    assert L.hq_kv_attention_workspace_bytes(2, 300, 4) == al(256 + 4 * 2 * 2 * 4 * 130) + 512 * 8
+    assert L.hq_kv_attention_workspace_bytes(8, 131072, 4) == al(256 + 4 * 8 * 512 * 4 * 130) + 512 * 32
