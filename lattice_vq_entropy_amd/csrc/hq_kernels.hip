@@ -136,9 +136,12 @@ __device__ __forceinline__ void tile_front(const EncArgs& a, const LaneConst<BF1
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[i] = u[i] + d[i];
   }
-  bool bad = false;
+  // out of range or not finite: the largest |u| by IEEE maximum (NaN wins),
+  // one compare per lane instead of eight
+  float umax = __builtin_elementwise_maximum(__builtin_fabsf(u[0]), __builtin_fabsf(u[1]));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) bad |= !(__builtin_fabsf(u[i]) < kRangeLimit);
+  for (int i = 2; i < 8; ++i) umax = __builtin_elementwise_maximum(umax, __builtin_fabsf(u[i]));
+  const bool bad = !(umax < kRangeLimit);
   quantize_syms<L>(u, ts.w, ts.odd);
   const uint64_t bad_mask = __ballot(bad);
   if (bad_mask) {
@@ -407,27 +410,33 @@ __global__ __launch_bounds__(1024) void blockscan_k(uint64_t* T, uint32_t nb) {
   }
 }
 
-// Encode, step 3 of 3: one chunk per work-group.  The chunk's staged bits go
-// to stream bits [B + E[c], B + E[c+1]) with a funnel shift, four words per
-// thread (one uint4 staging load, issued with the offset loads before they
-// arrive); the word shared with the predecessor takes the predecessor's last
-// 32 bits, recorded by step 1, so every stream word is written exactly once.
-// B is 0, or when appending to an existing stream its end bit: then the first
-// chunk's first word keeps the existing bits below B.  Also the per-tile
-// offsets, and the capacity check.  Each work-group forms E[c] itself: up to
-// kSelfScanChunks chunks (SELF_SCAN) as the sum of the bit counts of the
-// chunks before its own (all reads of one small array that the L2 serves), so
-// step 2 is skipped; above that as the bits of the blocks of 1024 chunks
-// before its own (step 2) plus the counts in its block before it.
+// Encode, step 3 of 3: one chunk per wave, kPlaceChunks chunks per
+// work-group.  The chunk's staged bits go to stream bits [B + E[c], B + E[c+1])
+// with a funnel shift, four words per lane (the first kSpecIters uint4 of
+// staging loads issued with the offset loads, before they arrive); the word
+// shared with the predecessor takes the predecessor's last 32 bits, recorded
+// by step 1, so every stream word is written exactly once.  B is 0, or when
+// appending to an existing stream its end bit: then the first chunk's first
+// word keeps the existing bits below B.  Also the per-tile offsets, and the
+// capacity check.  E[c] is formed here: up to kSelfScanChunks chunks
+// (SELF_SCAN) the work-group sums the bit counts of the chunks before its
+// first (all reads of one small array that the L2 serves) and each wave adds
+// those of the work-group's chunks before its own, so step 2 is skipped; above
+// that as the bits of the blocks of 1024 chunks before its own (step 2) plus
+// the counts in its block before it.
 constexpr uint32_t kSelfScanChunks = 8192;
+constexpr uint32_t kPlaceChunks = 4;  // one per wave
 template <bool SELF_SCAN>
 __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
-  const uint32_t tid = threadIdx.x, chunk = blockIdx.x;
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+  const uint32_t cg = blockIdx.x * kPlaceChunks;  // the work-group's first chunk
+  const uint32_t chunk = cg + wv;
+  const bool live = chunk < a.n_chunks;  // (wave-uniform)
   const uint32_t* st = a.stage + (uint64_t)chunk * kSlotWords;
-  // SELF_SCAN: the counts [0, chunk) as uint4 (the count array is padded to 64
+  // SELF_SCAN: the counts [0, cg) as uint4 (the count array is padded to 64
   // entries), loaded first so that summing them waits for these loads only;
-  // only the rounds of 1024 that hold counts below chunk are loaded, and lanes
-  // past chunk in the last one read entry 0
+  // only the rounds of 1024 that hold counts below cg are loaded, and lanes
+  // past cg in the last one read entry 0
   constexpr uint32_t kR = SELF_SCAN ? kSelfScanChunks / 1024 : 1;
   uint4 g[kR];
   if constexpr (SELF_SCAN) {
@@ -435,56 +444,66 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
     for (uint32_t j = 0; j < kR; ++j) {  // (the round tests are work-group uniform)
       const uint32_t i = 4u * tid + 1024u * j;
       g[j] = make_uint4(0u, 0u, 0u, 0u);
-      if (1024u * (j + 1) <= chunk) g[j] = *reinterpret_cast<const uint4*>(a.agg + i);
-      else if (1024u * j < chunk) g[j] = *reinterpret_cast<const uint4*>(a.agg + (i < chunk ? i : 0u));
+      if (1024u * (j + 1) <= cg) g[j] = *reinterpret_cast<const uint4*>(a.agg + i);
+      else if (1024u * j < cg) g[j] = *reinterpret_cast<const uint4*>(a.agg + (i < cg ? i : 0u));
     }
   }
-  // the first kSpecWords staging words are read before the chunk's length is
-  // known (enough below about 6 bits per scalar); longer chunks read the rest
-  // after it
-  constexpr uint32_t kSpecWords = 768;
-  const bool spec = 4u * tid < kSpecWords;
-  const uint4 c0 = spec ? *reinterpret_cast<const uint4*>(st + 4u * tid) : make_uint4(0u, 0u, 0u, 0u);
-  uint32_t p0 = (spec && tid) ? st[4u * tid - 1u] : 0u;
+  // the first 256 * kSpecIters staging words are read before the chunk's length
+  // is known (enough below about 6 bits per scalar); longer chunks read the
+  // rest after it
+  constexpr uint32_t kSpecIters = 3;
+  uint4 c0[kSpecIters];
+  uint32_t p0[kSpecIters];
+#pragma unroll
+  for (uint32_t j = 0; j < kSpecIters; ++j) {
+    const uint32_t i = 4u * lane + 256u * j;
+    c0[j] = live ? *reinterpret_cast<const uint4*>(st + i) : make_uint4(0u, 0u, 0u, 0u);
+    p0[j] = (live && i) ? st[i - 1u] : 0u;
+  }
   const uint64_t B = a.base ? *a.base : 0ull;  // work-group uniform
-  uint32_t tw;                                 // work-group uniform
-  if (chunk > 0) tw = a.tailw[chunk - 1];
-  else if ((B & 31) && (B >> 5) < a.cap_words) tw = a.words[B >> 5] << (32u - (uint32_t)(B & 31));  // bits below B
-  else tw = 0u;  // (B past the capacity fails the capacity check below)
-  if (tid == 0) p0 = tw;
-  uint64_t E, E1;
+  uint32_t tw = 0u;                            // wave uniform
+  if (live) {
+    if (chunk > 0) tw = a.tailw[chunk - 1];
+    else if ((B & 31) && (B >> 5) < a.cap_words) tw = a.words[B >> 5] << (32u - (uint32_t)(B & 31));  // bits below B
+    // (B past the capacity fails the capacity check below)
+  }
+  if (lane == 0) p0[0] = tw;
+  const uint64_t t = (uint64_t)chunk * kChunkTiles + lane;
+  const bool tl = live && lane < kChunkTiles && t < a.n_tiles;
+  const uint32_t lc = tl ? a.loc[t] : 0u;
+  const uint32_t A = live ? a.agg[chunk] : 0u;
+  uint64_t E;
   if constexpr (SELF_SCAN) {
     __shared__ uint32_t s_part[4];
-    const uint32_t A = a.agg[chunk];
-    // rounds wholly below chunk add all four counts; only the round holding
-    // chunk masks (the tests are work-group uniform, so no VALU is spent on
-    // rounds that were not loaded)
+    // rounds wholly below cg add all four counts; only the round holding cg
+    // masks (the tests are work-group uniform, so no VALU is spent on rounds
+    // that were not loaded)
     uint32_t part = 0;
 #pragma unroll
     for (uint32_t j = 0; j < kR; ++j) {
-      if (1024u * (j + 1) <= chunk) {
+      if (1024u * (j + 1) <= cg) {
         part += g[j].x + g[j].y + g[j].z + g[j].w;
-      } else if (1024u * j < chunk) {
+      } else if (1024u * j < cg) {
         const uint32_t i = 4u * tid + 1024u * j;
-        part += (i < chunk ? g[j].x : 0u) + (i + 1 < chunk ? g[j].y : 0u) + (i + 2 < chunk ? g[j].z : 0u) +
-                (i + 3 < chunk ? g[j].w : 0u);
+        part += (i < cg ? g[j].x : 0u) + (i + 1 < cg ? g[j].y : 0u) + (i + 2 < cg ? g[j].z : 0u) +
+                (i + 3 < cg ? g[j].w : 0u);
       }
     }
     // (the wave total is formed by every lane: a lane-0-only branch would
     // leave the other rows' sums unfinished when read across lanes)
     const uint32_t wsum = wave_sum_u32(part);
-    if ((tid & 63) == 0) s_part[tid >> 6] = wsum;
+    if (lane == 0) s_part[wv] = wsum;
     __syncthreads();
-    E = B + s_part[0] + s_part[1] + s_part[2] + s_part[3];  // the sum: at most 8192 * 94720 bits
-    E1 = E + A;
+    uint32_t before = 0;  // the work-group's chunks before this wave's (all below n_chunks when live)
+    for (uint32_t w = 0; w < wv; ++w) before += live ? a.agg[cg + w] : 0u;
+    E = B + s_part[0] + s_part[1] + s_part[2] + s_part[3] + before;  // at most 8192 * 94720 bits
   } else {  // the block's prefix plus the offset within the block (uniform loads)
-    E = B + a.blockpre[chunk >> 10] + a.eloc[chunk];
-    E1 = E + a.agg[chunk];
+    E = live ? B + a.blockpre[chunk >> 10] + a.eloc[chunk] : 0ull;
   }
-  if (tid == 0 && chunk == a.n_chunks - 1 && (E1 + 31) / 32 > a.cap_words) atomicOr(&a.ws->status, 1u << 4);
-  const uint64_t t = (uint64_t)chunk * kChunkTiles + tid;
-  const uint32_t lc = (tid < kChunkTiles && t < a.n_tiles) ? a.loc[t] : 0u;
-  if (tid < kChunkTiles && t < a.n_tiles) {
+  if (!live) return;
+  const uint64_t E1 = E + A;
+  if (lane == 0 && chunk == a.n_chunks - 1 && (E1 + 31) / 32 > a.cap_words) atomicOr(&a.ws->status, 1u << 4);
+  if (tl) {
     a.offsets[t] = E + lc;
     if (t == a.n_tiles - 1) a.offsets[a.n_tiles] = E1;
   }
@@ -494,11 +513,15 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   const uint64_t endw = last ? (E1 + 31) >> 5 : E1 >> 5;
   const uint64_t stop = endw < a.cap_words ? endw : a.cap_words;
   const uint32_t nw = stop > first ? (uint32_t)(stop - first) : 0u;
-  uint4 c = c0;
-  uint32_t p = p0;
   // staging words i..i+3 with i < nw <= 2962 stay inside the slot
-  for (uint32_t i = 4u * tid; i < nw; i += 1024u) {
-    if (i >= kSpecWords) {
+  uint32_t j = 0;
+  for (uint32_t i = 4u * lane; i < nw; i += 256u, ++j) {
+    uint4 c;
+    uint32_t p;
+    if (j < kSpecIters) {  // (uniform)
+      c = j == 0 ? c0[0] : j == 1 ? c0[1] : c0[2];
+      p = j == 0 ? p0[0] : j == 1 ? p0[1] : p0[2];
+    } else {
       c = *reinterpret_cast<const uint4*>(st + i);
       p = st[i - 1];
     }
@@ -1042,10 +1065,11 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   pa.base = a.base;
   pa.eloc = eloc;
   pa.blockpre = blockpre;
+  const dim3 pgrid((a.n_chunks + kPlaceChunks - 1) / kPlaceChunks);
   if (self_scan)
-    hipLaunchKernelGGL(place_k<true>, grid, dim3(256), 0, st, pa);
+    hipLaunchKernelGGL(place_k<true>, pgrid, dim3(256), 0, st, pa);
   else
-    hipLaunchKernelGGL(place_k<false>, grid, dim3(256), 0, st, pa);
+    hipLaunchKernelGGL(place_k<false>, pgrid, dim3(256), 0, st, pa);
   return hipGetLastError();
 }
 

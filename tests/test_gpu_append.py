@@ -121,3 +121,18 @@ def test_append_capacity_error(hq):
     enc2 = hq.Encoded(small[0], offsets[:21], k[:20], 20, storage=small)
     hq.append(plan, enc2, x[20:].contiguous(), ws)
     assert hq.status_sync(ws) == hq.ERR_CAPACITY
+    # an encode of several chunks into too few words also fails, and the
+    # workspace stays usable: encodes on it equal encodes on a fresh one
+    x = (torch.randn(300, 128) * 0.03).to(torch.bfloat16).cuda()
+    w3, o3, k3 = hq.alloc_stream(plan, 300, x.device)
+    ws = plan.workspace(300)
+    hq.encode(plan, x, ws, out=(w3[:100], o3, k3))
+    assert hq.status_sync(ws) == hq.ERR_CAPACITY
+    for n in (300, 40, 7, 300):
+        e1 = hq.encode(plan, x[:n].contiguous(), ws)
+        assert hq.status_sync(ws) == hq.OK
+        wsf = plan.workspace(n)
+        e2 = hq.encode(plan, x[:n].contiguous(), wsf)
+        assert hq.status_sync(wsf) == hq.OK
+        assert torch.equal(e1.offsets, e2.offsets)
+        assert torch.equal(e1.words[: e1.used_words()], e2.words[: e2.used_words()])
