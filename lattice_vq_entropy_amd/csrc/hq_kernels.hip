@@ -58,6 +58,16 @@ __device__ __forceinline__ bool lane_nonfinite(const void* x, uint64_t t, int v)
   return nf;
 }
 
+// 16 bytes to global memory with non-temporal (streaming) stores: outputs
+// that the next launch reads, so the writing launch leaves them out of its L2
+// (measured: the launch that follows starts sooner).
+__device__ __forceinline__ void store_nt4(uint32_t* p, uint32_t x, uint32_t y, uint32_t z, uint32_t w) {
+  __builtin_nontemporal_store(x, p);
+  __builtin_nontemporal_store(y, p + 1);
+  __builtin_nontemporal_store(z, p + 2);
+  __builtin_nontemporal_store(w, p + 3);
+}
+
 // OR a value of up to 64 bits into the LDS bit stream s at bit P (stream bit
 // P is bit P % 32 of s[P / 32]).
 __device__ __forceinline__ void lds_or64(uint32_t* s, uint32_t P, uint64_t val) {
@@ -334,7 +344,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IN == 1 ? 8
     // the used words and at least one zero word after them, in whole uint4
     const uint32_t n4 = ((A >> 5) + 2u + 3u) >> 2;
     uint4* dst = reinterpret_cast<uint4*>(a.stage + (uint64_t)chunk * kSlotWords);
-    for (uint32_t i = tid; i < n4; i += 256) dst[i] = reinterpret_cast<const uint4*>(s_stage)[i];
+    for (uint32_t i = tid; i < n4; i += 256) {
+      const uint4 q = reinterpret_cast<const uint4*>(s_stage)[i];
+      store_nt4(&dst[i].x, q.x, q.y, q.z, q.w);
+    }
     if (tid < kChunkTiles) {
       const uint64_t t = t_first + tid;
       if (t < a.n_tiles) {
@@ -951,13 +964,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
             const f32x2_t f = {o[2 * i], o[2 * i + 1]};
             pk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t)) ^ ((sm << i) & 0x80008000u);
           }
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.y) + t * kTile + 8 * v) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          store_nt4(reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.y) + t * kTile + 8 * v), pk[0], pk[1],
+                    pk[2], pk[3]);
         } else {
-          uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<float*>(a.y) + t * kTile + 8 * v);
-          dst[0] = make_uint4(__builtin_bit_cast(uint32_t, o[0]), __builtin_bit_cast(uint32_t, o[1]),
-                              __builtin_bit_cast(uint32_t, o[2]), __builtin_bit_cast(uint32_t, o[3]));
-          dst[1] = make_uint4(__builtin_bit_cast(uint32_t, o[4]), __builtin_bit_cast(uint32_t, o[5]),
-                              __builtin_bit_cast(uint32_t, o[6]), __builtin_bit_cast(uint32_t, o[7]));
+          uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<float*>(a.y) + t * kTile + 8 * v);
+          store_nt4(dst, __builtin_bit_cast(uint32_t, o[0]), __builtin_bit_cast(uint32_t, o[1]),
+                    __builtin_bit_cast(uint32_t, o[2]), __builtin_bit_cast(uint32_t, o[3]));
+          store_nt4(dst + 4, __builtin_bit_cast(uint32_t, o[4]), __builtin_bit_cast(uint32_t, o[5]),
+                    __builtin_bit_cast(uint32_t, o[6]), __builtin_bit_cast(uint32_t, o[7]));
         }
       }
     }
