@@ -26,18 +26,31 @@ template <bool BF16> struct InVec;
 template <> struct InVec<true> { uint4 w; };
 template <> struct InVec<false> { uint4 w0, w1; };
 
-template <bool BF16>
+// 16 bytes from global memory; NT: a non-temporal (streaming) load, for data
+// read once per launch (measured: it leaves the L2 to what is reused).
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint32_t* p) {
+  if constexpr (NT)
+    return make_uint4(__builtin_nontemporal_load(p), __builtin_nontemporal_load(p + 1), __builtin_nontemporal_load(p + 2),
+                      __builtin_nontemporal_load(p + 3));
+  else
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// NT: the encode reads its input once (the length-only passes of the
+// calibration re-read it, and keep the normal loads)
+template <bool BF16, bool NT = false>
 __device__ __forceinline__ InVec<BF16> load_in(const void* x, uint64_t t, int v, bool valid) {
   InVec<BF16> in;
   if constexpr (BF16) {
     in.w = make_uint4(0u, 0u, 0u, 0u);
-    if (valid) in.w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + t * kTile + 8 * v);
+    if (valid) in.w = load16<NT>(reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(x) + t * kTile + 8 * v));
   } else {
     in.w0 = in.w1 = make_uint4(0u, 0u, 0u, 0u);
     if (valid) {
-      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + t * kTile + 8 * v);
-      in.w0 = p[0];
-      in.w1 = p[1];
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(reinterpret_cast<const float*>(x) + t * kTile + 8 * v);
+      in.w0 = load16<NT>(p);
+      in.w1 = load16<NT>(p + 4);
     }
   }
   return in;
@@ -297,7 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IN == 1 ? 8
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const uint64_t t = t_first + p * 16 + pslot;
-    in[p] = load_in<BF16>(a.x, t, v, t < a.n_tiles);
+    in[p] = load_in<BF16, !LEN_ONLY>(a.x, t, v, t < a.n_tiles);
   }
 
   if constexpr (LEN_ONLY) {
@@ -764,6 +777,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uin
 // loads all issued before the LDS stores; the words from w_end on read as
 // zero.  Every thread of the work-group calls it, after s_off[0..nt] is
 // visible; returns whether the span is sane (work-group uniform).
+template <bool NT = false>  // NT: the stream is read once per launch (a plain decode)
 __device__ __forceinline__ bool stage_chunk(const uint32_t* words, uint64_t n_words, const uint64_t* s_off,
                                             uint32_t nt, uint32_t* s_stage, uint64_t& w_first, int tid) {
   w_first = (s_off[0] >> 5) & ~3ull;
@@ -780,7 +794,7 @@ __device__ __forceinline__ bool stage_chunk(const uint32_t* words, uint64_t n_wo
       if (i4 < n4) {
         const uint64_t wg = w_first + 4ull * i4;
         if (wg + 4 <= n_words) {
-          q[j] = *reinterpret_cast<const uint4*>(words + wg);
+          q[j] = load16<NT>(words + wg);
         } else {
           q[j].x = words[wg];
           if (4 * i4 + 1 < n) q[j].y = words[wg + 1];
@@ -857,7 +871,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
   }
   __syncthreads();
   uint64_t w_first;
-  const bool span_ok = stage_chunk(a.words, a.n_words, s_off, nt, s_stage, w_first, tid);
+  const bool span_ok =
+      stage_chunk<OUT == kOutF32 || OUT == kOutBf16 || OUT == kOutRot>(a.words, a.n_words, s_off, nt, s_stage, w_first, tid);
   __syncthreads();
 
   // output scale: the lane sign and c_dec, then the signs of D (bf16: on the
