@@ -585,6 +585,31 @@ __device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t j) {
   return pos;
 }
 
+// The same from a table in LDS: lut[8 b + i] = position of the i-th set bit
+// of the byte b.  The byte holding bit j is found from the popcounts of the
+// low 8, 16 and 24 bits.
+struct SelectLut {
+  uint8_t v[256][8];
+};
+constexpr SelectLut make_select_lut() {
+  SelectLut t{};
+  for (int b = 0; b < 256; ++b) {
+    int n = 0;
+    for (int i = 0; i < 8; ++i)
+      if ((b >> i) & 1) t.v[b][n++] = (uint8_t)i;
+  }
+  return t;
+}
+__constant__ SelectLut kSelectLut = make_select_lut();
+
+__device__ __forceinline__ uint32_t select_bit_lut(uint32_t w, uint32_t j, const uint8_t* lut) {
+  const uint32_t c0 = __builtin_popcount(w & 0xFFu), c1 = __builtin_popcount(w & 0xFFFFu),
+                 c2 = __builtin_popcount(w & 0xFFFFFFu);
+  const uint32_t bi = (uint32_t)(j >= c0) + (uint32_t)(j >= c1) + (uint32_t)(j >= c2);
+  const uint32_t before = bi == 0 ? 0u : bi == 1 ? c0 : bi == 2 ? c1 : c2;
+  return 8u * bi + lut[8u * __builtin_amdgcn_ubfe(w, 8u * bi, 8u) + (j - before)];
+}
+
 // Lattice coordinates of the lane's 8 symbols (inverse zigzag and unstrip),
 // as fp32 real-space points.  With s = sext(bit 0 of m), 2*unzigzag(m) is
 // m ^ s, so a halved coordinate plus the raw bit is one v_xad_u32.
@@ -655,7 +680,8 @@ __device__ __forceinline__ uint32_t unary_starts_general(const uint32_t* s, uint
 // LDS per tile; tb: 16 bytes of LDS per tile.
 template <int L>
 __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uint32_t Lb, uint32_t k, int v, int r,
-                                           int lane, uint32_t* ust, uint8_t* tb, float p[8]) {
+                                           int lane, uint32_t* ust, uint8_t* tb, float p[8],
+                                           const uint8_t* sel_lut = nullptr) {
   constexpr uint32_t RAW = Lat<L>::raw;
   uint32_t raw = 0;
   if constexpr (RAW > 0) {
@@ -715,7 +741,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uin
       const uint32_t Iprev = wsel == 0 ? 0u : __builtin_amdgcn_ubfe(Td, 8 * (q4 & 3), 8);
       uint32_t wd = s[wA + min(wsel, 15u)];
       if (wsel == 0) wd &= ~0u << (ustart & 31);
-      start = (wA + wsel) * 32u + select_bit(wd, R - Iprev) + 1u;
+      start = (wA + wsel) * 32u + (sel_lut ? select_bit_lut(wd, R - Iprev, sel_lut) : select_bit(wd, R - Iprev)) + 1u;
     }
   } else {
     ok = unary_starts_general(s, ustart, uend, r, ust) == 128u;
@@ -849,6 +875,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
 
   if (tid <= (int)nt) s_off[tid] = a.offsets[t_first + tid];
   if (tid < (int)nt) s_k[tid] = a.kin[t_first + tid];
+  // the bit-select table (not with the scores' query block: LDS)
+  constexpr bool kLut = OUT != kOutScores;
+  __shared__ uint2 s_sel[kLut ? 256 : 1];
+  if constexpr (kLut) s_sel[tid] = reinterpret_cast<const uint2*>(&kSelectLut)[tid];
   if constexpr (OUT == kOutScores) {
     // rotate the head's queries: q~ = H D q, one query per 16-lane row (with
     // a dense rotation the queries arrive rotated: q~ = Q q)
@@ -906,7 +936,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
       const uint64_t Lr = o1 - o0;  // wraps past MAXREC when o1 < o0
       const bool ok = span_ok && k <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + k) && Lr <= MAXREC;
       if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, s_ust[pslot],
-                                       reinterpret_cast<uint8_t*>(&s_tb[pslot]), pv);
+                                       reinterpret_cast<uint8_t*>(&s_tb[pslot]), pv,
+                                       kLut ? reinterpret_cast<const uint8_t*>(s_sel) : nullptr);
       if (!good && r == 0) set_status(a.ws, 5);
       if constexpr (DITHER) {
         if (!good) {
