@@ -1186,7 +1186,7 @@ template <int L>
 __device__ __forceinline__ void attn_parse(const uint32_t* s_stage, const uint64_t* s_off, const uint32_t* s_k,
                                            uint64_t w_first, bool span_ok, bool valid, int slot, uint64_t tile_id,
                                            uint32_t key0, uint32_t key1, int v, int r, int lane, uint32_t* ust,
-                                           uint8_t* tb, WsHeader* ws, float pv[8]) {
+                                           uint8_t* tb, WsHeader* ws, float pv[8], const uint8_t* sel_lut) {
   constexpr uint32_t RAW = Lat<L>::raw;
   constexpr uint32_t MAXREC = RAW + 128u * 23u;
 #pragma unroll
@@ -1197,7 +1197,7 @@ __device__ __forceinline__ void attn_parse(const uint32_t* s_stage, const uint64
   const uint64_t Lr = o1 - o0;
   const bool ok = span_ok && k <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + k) && Lr <= MAXREC;
   bool good = false;
-  if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, ust, tb, pv);
+  if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, ust, tb, pv, sel_lut);
   if (!good) {
     if (r == 0) set_status(ws, 5);
 #pragma unroll
@@ -1231,6 +1231,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   __shared__ __align__(16) float s_qv[16][kTile];  // rotated queries (phase 1), a pass's values (phase 2)
   __shared__ float4 s_w[kKeys];                    // per key: the queries' scores, then weights
   __shared__ float s_ml[2][4][kAttnQ];            // per wave: maximum, then sum
+  __shared__ uint2 s_sel[256];                     // bit-select table
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
   const int v = lane_vector(r);
@@ -1245,6 +1246,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   float* s_wf = reinterpret_cast<float*>(s_w);
   float (*s_q)[kTile] = s_qv;
   float (*s_v)[kTile] = s_qv;
+  s_sel[tid] = reinterpret_cast<const uint2*>(&kSelectLut)[tid];  // visible after the first barrier below
 
   if (wv == 0 && grp < (int)nq) {  // rotate the queries: q~ = H D q (row-uniform branch)
     const float* qp = a.q + ((head * a.qph + q0 + grp) * kTile + 8 * v);
@@ -1289,7 +1291,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
       const bool valid = slot < (int)nt;
       float pv[8];
       attn_parse<L>(s_stage, s_off, s_k, w_first, span_ok, valid, slot, a.ktb + t_first + slot, a.key0, a.key1, v, r,
-                    lane, s_ust[pslot], reinterpret_cast<uint8_t*>(&s_tb[pslot]), a.ws, pv);
+                    lane, s_ust[pslot], reinterpret_cast<uint8_t*>(&s_tb[pslot]), a.ws, pv,
+                    reinterpret_cast<const uint8_t*>(s_sel));
 #pragma unroll
       for (int g = 0; g < (int)kAttnQ; ++g) {
         float d = 0.0f;
@@ -1348,7 +1351,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
       const bool valid = slot < (int)nt;
       float pv[8];
       attn_parse<L>(s_stage, s_off, s_k, w_first, span_ok, valid, slot, a.vtb + t_first + slot, a.key0, a.key1, v, r,
-                    lane, s_ust[pslot], reinterpret_cast<uint8_t*>(&s_tb[pslot]), a.ws, pv);
+                    lane, s_ust[pslot], reinterpret_cast<uint8_t*>(&s_tb[pslot]), a.ws, pv,
+                    reinterpret_cast<const uint8_t*>(s_sel));
       float4* vr = reinterpret_cast<float4*>(&s_v[pslot][8 * v]);  // zeros past the last key
       vr[0] = make_float4(pv[0], pv[1], pv[2], pv[3]);
       vr[1] = make_float4(pv[4], pv[5], pv[6], pv[7]);
