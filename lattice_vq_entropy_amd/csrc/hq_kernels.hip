@@ -1619,9 +1619,11 @@ __global__ __launch_bounds__(256) void gemm_k(GemmArgs g) {
   __shared__ uint64_t s_o1[32];
   __shared__ uint32_t s_k[32];
   __shared__ __align__(16) uint16_t s_B[2][32][kBS];
+  __shared__ uint2 s_sel[256];  // bit-select table
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
   const int v = lane_vector(r), pslot = wv * 4 + grp;
+  s_sel[tid] = reinterpret_cast<const uint2*>(&kSelectLut)[tid];
   const uint32_t r0 = blockIdx.x * 32u;
   const uint32_t b_lo = blockIdx.y * g.per;
   const uint32_t b_hi = b_lo + g.per < g.nblk ? b_lo + g.per : g.nblk;
@@ -1680,7 +1682,7 @@ __global__ __launch_bounds__(256) void gemm_k(GemmArgs g) {
       for (int e = 0; e < 8; ++e) pv[e] = 0.0f;
       bool good = false;
       if (ok) good = parse_lane<L>(sr, (uint32_t)(o0 & 31u), (uint32_t)Lr, kk, v, r, lane, s_ust[pslot],
-                                   reinterpret_cast<uint8_t*>(&s_tb[pslot]), pv);
+                                   reinterpret_cast<uint8_t*>(&s_tb[pslot]), pv, reinterpret_cast<const uint8_t*>(s_sel));
       if (valid && !good) {
         if (r == 0) set_status(g.ws, 5);
 #pragma unroll
