@@ -39,7 +39,6 @@ struct PlaceArgs {
   const uint32_t* stage;
   const uint32_t* agg;  // bits per chunk (padded to 64 entries)
   WsHeader* ws;
-  const uint64_t* E;
   const uint32_t* loc;
   const uint32_t* tailw;
   uint64_t n_tiles;

@@ -474,17 +474,17 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
       else if (1024u * j < cg) g[j] = *reinterpret_cast<const uint4*>(a.agg + (i < cg ? i : 0u));
     }
   }
-  // the first 256 * kSpecIters staging words are read before the chunk's length
-  // is known (enough below about 6 bits per scalar); longer chunks read the
-  // rest after it
+  // staging reads: in round j lane l holds the uint4 blocks 64 j + l - 1 and
+  // 64 j + l of the chunk's staged words; the first kSpecIters rounds are read
+  // before the chunk's offset is known (enough below about 6 bits per scalar)
   constexpr uint32_t kSpecIters = 3;
-  uint4 c0[kSpecIters];
-  uint32_t p0[kSpecIters];
+  const uint4* st4 = reinterpret_cast<const uint4*>(st);
+  uint4 u0[kSpecIters], u1[kSpecIters];
 #pragma unroll
   for (uint32_t j = 0; j < kSpecIters; ++j) {
-    const uint32_t i = 4u * lane + 256u * j;
-    c0[j] = live ? *reinterpret_cast<const uint4*>(st + i) : make_uint4(0u, 0u, 0u, 0u);
-    p0[j] = (live && i) ? st[i - 1u] : 0u;
+    const uint32_t q = lane + 64u * j;
+    u1[j] = live ? st4[q] : make_uint4(0u, 0u, 0u, 0u);
+    u0[j] = (live && q) ? st4[q - 1u] : make_uint4(0u, 0u, 0u, 0u);
   }
   const uint64_t B = a.base ? *a.base : 0ull;  // work-group uniform
   uint32_t tw = 0u;                            // wave uniform
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
     else if ((B & 31) && (B >> 5) < a.cap_words) tw = a.words[B >> 5] << (32u - (uint32_t)(B & 31));  // bits below B
     // (B past the capacity fails the capacity check below)
   }
-  if (lane == 0) p0[0] = tw;
+  if (lane == 0) u0[0].w = tw;  // staged word -1: the bits before the chunk's first
   const uint64_t t = (uint64_t)chunk * kChunkTiles + lane;
   const bool tl = live && lane < kChunkTiles && t < a.n_tiles;
   const uint32_t lc = tl ? a.loc[t] : 0u;
@@ -539,30 +539,44 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   const uint64_t endw = last ? (E1 + 31) >> 5 : E1 >> 5;
   const uint64_t stop = endw < a.cap_words ? endw : a.cap_words;
   const uint32_t nw = stop > first ? (uint32_t)(stop - first) : 0u;
-  // staging words i..i+3 with i < nw <= 2962 stay inside the slot
-  uint32_t j = 0;
-  for (uint32_t i = 4u * lane; i < nw; i += 256u, ++j) {
-    uint4 c;
-    uint32_t p;
-    if (j < kSpecIters) {  // (uniform)
-      c = j == 0 ? c0[0] : j == 1 ? c0[1] : c0[2];
-      p = j == 0 ? p0[0] : j == 1 ? p0[1] : p0[2];
+  // stream words first + i (i < nw) = (s[i] : s[i - 1]) >> (32 - sh), in
+  // 16-byte aligned groups: lane l of round j writes words g .. g + 3 with
+  // g = first - al + 4 (64 j + l), i.e. i = li .. li + 3, li = 4 (64 j + l) - al;
+  // its staged words s[li - 1 .. li + 3] are entries 3 - al .. 7 - al of the
+  // two blocks it holds.  Blocks read past the spec rounds have li < nw, so
+  // 4 q <= nw + 2 <= 2963: inside the slot.
+  const uint32_t al = (uint32_t)(first & 3u);  // (wave uniform)
+  auto group = [&](uint32_t j, const uint4& b0, const uint4& b1) {
+    const uint32_t q = lane + 64u * j;
+    const int32_t li = (int32_t)(4u * q) - (int32_t)al;
+    uint32_t w[5];
+    if (al == 0) {  // (uniform)
+      w[0] = b0.w; w[1] = b1.x; w[2] = b1.y; w[3] = b1.z; w[4] = b1.w;
+    } else if (al == 1) {
+      w[0] = b0.z; w[1] = b0.w; w[2] = b1.x; w[3] = b1.y; w[4] = b1.z;
+    } else if (al == 2) {
+      w[0] = b0.y; w[1] = b0.z; w[2] = b0.w; w[3] = b1.x; w[4] = b1.y;
     } else {
-      c = *reinterpret_cast<const uint4*>(st + i);
-      p = st[i - 1];
+      w[0] = b0.x; w[1] = b0.y; w[2] = b0.z; w[3] = b0.w; w[4] = b1.x;
     }
     uint32_t o[4];
-    if (sh) {
-      o[0] = __builtin_amdgcn_alignbit(c.x, p, 32 - sh);
-      o[1] = __builtin_amdgcn_alignbit(c.y, c.x, 32 - sh);
-      o[2] = __builtin_amdgcn_alignbit(c.z, c.y, 32 - sh);
-      o[3] = __builtin_amdgcn_alignbit(c.w, c.z, 32 - sh);
-    } else {
-      o[0] = c.x; o[1] = c.y; o[2] = c.z; o[3] = c.w;
-    }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (i + e < nw) a.words[first + i + e] = o[e];
+    for (int e = 0; e < 4; ++e) o[e] = sh ? __builtin_amdgcn_alignbit(w[e + 1], w[e], 32 - sh) : w[e + 1];
+    uint32_t* dst = a.words + (first - al) + 4u * q;
+    if (li >= 0 && li + 3 < (int32_t)nw) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (li + e >= 0 && li + e < (int32_t)nw) dst[e] = o[e];
+    }
+  };
+#pragma unroll
+  for (uint32_t j = 0; j < kSpecIters; ++j)
+    if ((int32_t)(4u * (lane + 64u * j)) - (int32_t)al < (int32_t)nw) group(j, u0[j], u1[j]);
+  for (uint32_t j = kSpecIters; 256u * j < nw + al; ++j) {
+    const uint32_t q = lane + 64u * j;
+    if ((int32_t)(4u * q) - (int32_t)al < (int32_t)nw) group(j, st4[q - 1u], st4[q]);
   }
 }
 
@@ -1114,7 +1128,6 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   pa.agg = a.agg;
   pa.ws = a.ws;
   pa.stage = a.stage;
-  pa.E = a.E;
   pa.loc = a.loc;
   pa.tailw = a.tailw;
   pa.n_tiles = a.n_tiles;
