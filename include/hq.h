@@ -36,7 +36,9 @@
  *     stream-ordered launches (pack per chunk, then placement, which sums the
  *     bit counts of the chunks before its own) up to 8192 chunks of 32 tiles,
  *     and three above (the bit counts of blocks of 1024 chunks between them;
- *     placement then adds the blocks' totals and its own block's counts).  Encode
+ *     placement then adds the totals of the blocks before its own and its own
+ *     block's counts), four above 65536 chunks (the block totals turned into
+ *     prefixes by a launch of their own).  Encode
  *     and decode allocate nothing and can be captured in a HIP graph.
  *   - Tensors are row-major; every 128 consecutive elements form one tile
  *     (weights: tiles along rows; KV [B, H, S, 128]: one tile per vector).

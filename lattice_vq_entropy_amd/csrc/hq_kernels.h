@@ -49,6 +49,7 @@ struct PlaceArgs {
   const uint64_t* base;  // append: the existing stream's end bit (device), else null
   const uint32_t* eloc;      // above the self-scan limit: chunk offsets within blocks of 1024
   const uint64_t* blockpre;  // and the bits of the blocks before each block
+  int block_totals;          // blockpre holds the blocks' own totals (at most 64): sum those before
 };
 
 struct DecArgs {

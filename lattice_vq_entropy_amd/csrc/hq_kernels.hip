@@ -408,9 +408,10 @@ __global__ __launch_bounds__(256) void blocksum_k(const uint32_t* agg, uint32_t 
   if (tid == 0) T[blockIdx.x] = (uint64_t)s_w[0] + s_w[1] + s_w[2] + s_w[3];
 }
 
-// Encode, step 2 of 3, second part: the block totals T[0..nb) replaced in place by their
-// exclusive prefix sums, by one work-group of 1024 threads (1024 blocks per
-// round, a carry between rounds).
+// Encode, step 2 of 3, second part (above 64 blocks; up to 64 the placement
+// sums the totals itself): the block totals T[0..nb) replaced in place by
+// their exclusive prefix sums, by one work-group of 1024 threads (1024 blocks
+// per round, a carry between rounds).
 __global__ __launch_bounds__(1024) void blockscan_k(uint64_t* T, uint32_t nb) {
   __shared__ uint64_t s_w[16];
   __shared__ uint64_t s_carry;
@@ -524,7 +525,16 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
     for (uint32_t w = 0; w < wv; ++w) before += live ? a.agg[cg + w] : 0u;
     E = B + s_part[0] + s_part[1] + s_part[2] + s_part[3] + before;  // at most 8192 * 94720 bits
   } else {  // the block's prefix plus the offset within the block (uniform loads)
-    E = live ? B + a.blockpre[chunk >> 10] + a.eloc[chunk] : 0ull;
+    uint64_t pre = 0;
+    if (a.block_totals) {  // at most 64 blocks: lane b adds the total of block b before this one
+      const uint32_t b = chunk >> 10;
+      pre = lane < b && live ? a.blockpre[lane] : 0ull;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) pre += __shfl_xor(pre, o);
+    } else if (live) {
+      pre = a.blockpre[chunk >> 10];
+    }
+    E = live ? B + pre + a.eloc[chunk] : 0ull;
   }
   if (!live) return;
   const uint64_t E1 = E + A;
@@ -1122,9 +1132,11 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
   if (!self_scan) {
     const uint32_t nb = (a.n_chunks + kScanBlock - 1) / kScanBlock;
     hipLaunchKernelGGL(blocksum_k, dim3(nb), dim3(256), 0, st, (const uint32_t*)a.agg, a.n_chunks, eloc, blockpre);
-    hipLaunchKernelGGL(blockscan_k, dim3(1), dim3(1024), 0, st, blockpre, nb);
+    // up to 64 blocks the placement sums the totals itself (one launch fewer)
+    if (nb > 64) hipLaunchKernelGGL(blockscan_k, dim3(1), dim3(1024), 0, st, blockpre, nb);
   }
   PlaceArgs pa;
+  pa.block_totals = !self_scan && (a.n_chunks + kScanBlock - 1) / kScanBlock <= 64;
   pa.agg = a.agg;
   pa.ws = a.ws;
   pa.stage = a.stage;

@@ -125,6 +125,19 @@ def test_weight_8192x28672(hq, orc, lat, bps):
     torch.cuda.empty_cache()
 
 
+def test_above_65536_chunks(hq, orc):
+    """More than 64 blocks of 1024 chunks of 32 tiles (2.1 M tiles, E8 at
+    4 bps): the block totals become prefixes in a launch of their own before
+    the placement; by sampled tiles."""
+    n = 65536 * 32 + 5000
+    g = torch.Generator(device="cuda").manual_seed(65537)
+    x = (torch.randn(n, 128, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    plan = calibrated_plan(hq, 3, 4.0, x)
+    check_stream(hq, orc, 3, x, plan, 4.0, seed=65537)
+    del x
+    torch.cuda.empty_cache()
+
+
 def test_kv_8x8x32768_d4_dithered(hq, orc):
     """K and V of one layer, D4 at 2 bps with subtractive dither; plus the
     per-vector bias check of q . k_hat on 4096 random queries."""
