@@ -147,6 +147,7 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   if (!len_only && (!words || !k)) return HQ_ERR_ARG;
   if (((uintptr_t)x & 15u) != 0) return HQ_ERR_ARG;
   if (((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+  if (!len_only && ((((uintptr_t)words & 15u) != 0) || (((uintptr_t)offsets & 7u) != 0))) return HQ_ERR_ARG;
   // chunk indices are 32-bit (grid x)
   if (hq::ws_chunks(n_tiles) > 0x7FFFFFFFull) return HQ_ERR_ARG;
   hq::EncArgs a{};

@@ -60,6 +60,10 @@ def test_argument_errors_are_synchronous(hq):
     # null workspace / pointers, bad dtype
     assert L.hq_encode(p.handle, None, 1, 4, None, 0, None, None, None, None) == hq.ERR_ARG
     assert L.hq_encode(p.handle, None, 5, 4, None, 0, None, None, C.c_void_p(256), None) == hq.ERR_ARG
+    # stream words 16-byte aligned, offsets 8-byte aligned
+    A = C.c_void_p(4096)
+    assert L.hq_encode(p.handle, A, 1, 4, C.c_void_p(4100), 64, A, A, A, None) == hq.ERR_ARG
+    assert L.hq_encode(p.handle, A, 1, 4, A, 64, C.c_void_p(4100), A, A, None) == hq.ERR_ARG
     assert L.hq_decode(p.handle, None, 0, None, None, 4, None, 0, None, None) == hq.ERR_ARG
     assert L.hq_kv_scores(p.handle, None, 0, None, None, 1, 1, 0, None, 17, None, None, None) == hq.ERR_ARG
     D = C.c_void_p(4096)
