@@ -267,7 +267,7 @@ def valu_for(op: str, ms: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the codec path is measured on one GPU: --gpus must be 1"}))
         sys.exit(2)
     import numpy as np
     import torch
