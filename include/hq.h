@@ -128,8 +128,11 @@ hq_status hq_calibrate(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n
                        float* alpha_out, double* bps_out);
 
 /* Encode n_tiles tiles of x (fp32 or bf16) [Methodology 1-3].
- * words: cap_words uint32 (see hq_encode_bound_words); offsets: n_tiles+1
- * uint64 bit offsets; k: n_tiles uint8 Rice parameters. */
+ * words: cap_words uint32 (see hq_encode_bound_words), 16-byte aligned;
+ * offsets: n_tiles+1 uint64 bit offsets, 8-byte aligned; k: n_tiles uint8
+ * Rice parameters.  Only words [0, ceil(offsets[n_tiles] / 32)) are written,
+ * and none at or past cap_words (a stream that does not fit reports
+ * HQ_ERR_CAPACITY). */
 hq_status hq_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles,
                     uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k,
                     void* ws, void* stream);

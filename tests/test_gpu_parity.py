@@ -162,6 +162,35 @@ def test_offset_paths_at_the_boundary(hq, orc):
     assert hq.status_sync(ws) == hq.ERR_CAPACITY
 
 
+@pytest.mark.parametrize("n_tiles,big", [(97, False), (3000, False), (8193 * 32, True)])
+def test_words_outside_the_stream_are_untouched(hq, orc, n_tiles, big):
+    """The placement writes exactly the stream's words: with a buffer filled
+    with a sentinel, the words past ceil(total / 32) keep it, and with
+    cap_words below the need (an HQ_ERR_CAPACITY) so do the words past
+    cap_words; both for the summing placement and (8193 chunks) the scan."""
+    g = torch.Generator().manual_seed(n_tiles)
+    x = (torch.randn(n_tiles, 128, generator=g) * 0.03).to(torch.bfloat16).cuda()
+    plan = hq.Plan(3, 4.0, SEED).set_alpha(0.004)
+    ws = plan.workspace(n_tiles)
+    sentinel = -0x21524111  # 0xDEADBEEF
+    words, offsets, k = hq.alloc_stream(plan, n_tiles, x.device)
+    words.fill_(sentinel)
+    enc = hq.encode(plan, x, ws, out=(words, offsets, k))
+    assert hq.status_sync(ws) == hq.OK
+    need = enc.used_words()
+    assert bool((words[need:] == sentinel).all())
+    ref = words[:need].clone()
+    for cap in (need - 1, need - 37, need // 2 + 3):
+        words.fill_(sentinel)
+        hq.encode(plan, x, ws, out=(words, offsets, k), cap_words=cap)
+        assert hq.status_sync(ws) == hq.ERR_CAPACITY
+        assert bool((words[cap:] == sentinel).all()), f"words past cap_words = {cap} written"
+    words.fill_(sentinel)
+    hq.encode(plan, x, ws, out=(words, offsets, k), cap_words=need)
+    assert hq.status_sync(ws) == hq.OK
+    assert torch.equal(words[:need], ref) and bool((words[need:] == sentinel).all())
+
+
 @pytest.mark.parametrize("n_tiles", [1, 31, 32, 33, 97])
 def test_small_and_ragged_sizes(hq, orc, n_tiles):
     g = torch.Generator().manual_seed(n_tiles)
