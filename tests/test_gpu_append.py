@@ -108,6 +108,30 @@ def test_append_large_pieces_and_decode(hq, orc):
     assert np.array_equal(g16[nz], oy[nz]) and np.all((g16[~nz] & 0x7FFF) == 0)
 
 
+def test_append_keeps_the_existing_stream(hq):
+    """An append writes no word below the one holding the existing stream's
+    end bit, keeps that word's bits below it, and nothing past its own end."""
+    g = torch.Generator().manual_seed(11)
+    plan = hq.Plan(3, 4.0, SEED).set_alpha(0.004)
+    x = (torch.randn(300, 128, generator=g) * 0.03).to(torch.bfloat16).cuda()
+    words, offsets, k = hq.alloc_stream(plan, 300, x.device)
+    sentinel = -0x21524111
+    words.fill_(sentinel)
+    ws = plan.workspace(300)
+    enc = hq.encode(plan, x[:77].contiguous(), ws, out=(words, offsets, k))
+    assert hq.status_sync(ws) == hq.OK
+    before = words.clone()
+    B = enc.total_bits()
+    enc = hq.append(plan, enc, x[77:].contiguous(), ws)
+    assert hq.status_sync(ws) == hq.OK
+    assert torch.equal(words[: B // 32], before[: B // 32])
+    if B % 32:
+        mask = (1 << (B % 32)) - 1
+        assert (int(words[B // 32]) & mask) == (int(before[B // 32]) & mask)
+    end = enc.used_words()
+    assert bool((words[end:] == sentinel).all())
+
+
 def test_append_capacity_error(hq):
     """An append that does not fit cap_words reports HQ_ERR_CAPACITY."""
     plan = hq.Plan(3, 4.0, SEED).set_alpha(0.004)

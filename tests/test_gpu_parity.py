@@ -191,6 +191,25 @@ def test_words_outside_the_stream_are_untouched(hq, orc, n_tiles, big):
     assert torch.equal(words[:need], ref) and bool((words[need:] == sentinel).all())
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_decode_writes_only_its_tiles(hq, orc, out_dtype):
+    """Decoding 1000 tiles into a larger, sentinel-filled buffer changes
+    exactly the first 1000 x 128 elements (plain and dithered)."""
+    g = torch.Generator().manual_seed(1000)
+    x = (torch.randn(1000, 128, generator=g) * 0.03).to(torch.bfloat16).cuda()
+    plan = hq.Plan(3, 4.0, SEED).set_alpha(0.004)
+    ws = plan.workspace(1000)
+    for dithered in (False, True):
+        enc = hq.encode(plan, x, ws, dithered=dithered, tile_base=3)
+        assert hq.status_sync(ws) == hq.OK
+        ref = hq.decode(plan, enc, ws, out_dtype=out_dtype)
+        big = torch.full((1000 * 128 + 4096,), -7.25, dtype=out_dtype, device="cuda")
+        hq.decode(plan, enc, ws, out=big[: 1000 * 128], out_dtype=out_dtype)
+        assert hq.status_sync(ws) == hq.OK
+        assert torch.equal(big[: 1000 * 128], ref)
+        assert bool((big[1000 * 128:] == -7.25).all())
+
+
 @pytest.mark.parametrize("n_tiles", [1, 31, 32, 33, 97])
 def test_small_and_ragged_sizes(hq, orc, n_tiles):
     g = torch.Generator().manual_seed(n_tiles)
