@@ -98,6 +98,35 @@ def full_parity(hq, orc, lat, x, alpha, dithered=False, tile_base=0, decode=True
     return enc
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_randomized_parity(hq, orc, case):
+    """Seeded random cases: 1 to 5000 tiles, any lattice, 1 to 8 bits per
+    scalar, plain or dithered at a random tile id, bf16 or fp32 input,
+    Gaussian, Student-t or sparse with outliers; the whole stream and both
+    reconstructions against the oracle."""
+    rng = np.random.default_rng(7000 + case)
+    n = int(rng.choice([1, 2, 31, 32, 33, 63, 64, 65]) if case < 6 else rng.integers(1, 5001))
+    lat = int(rng.integers(0, 4))
+    bps = float(rng.uniform(1.0, 8.0))
+    dithered = bool(rng.integers(0, 2))
+    tile_base = int(rng.integers(0, 1 << 40)) if dithered else 0
+    dtype = torch.bfloat16 if rng.integers(0, 2) else torch.float32
+    g = torch.Generator().manual_seed(7000 + case)
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        x = torch.randn(n, 128, generator=g)
+    elif kind == 1:
+        chi2 = (torch.randn(4, n, 128, generator=g) ** 2).sum(dim=0)  # Student-t with 4 degrees of freedom
+        x = torch.randn(n, 128, generator=g) / (chi2 / 4.0).sqrt()
+    else:
+        x = torch.randn(n, 128, generator=g) * (torch.rand(n, 128, generator=g) < 0.1)
+        x = x + 50.0 * (torch.rand(n, 128, generator=g) < 0.005)
+    x = (x * float(rng.uniform(0.001, 2.0))).to(dtype)
+    sigma = max(float(x.float().pow(2).mean().sqrt()), 1e-3)
+    alpha = alpha_for(lat, sigma, bps)
+    full_parity(hq, orc, lat, x.cuda(), alpha, dithered=dithered, tile_base=tile_base)
+
+
 def test_c1_config_bit_exact(hq, orc):
     """fp32 [4096, 128], E8 at the fixed alpha of the 4-bps operating point."""
     from lattice_vq_entropy_amd import workloads as W
