@@ -185,6 +185,19 @@ def test_attention_matches_oracle(hq, orc, lat, bps, heads, seq, qph, scale):
     run_case(hq, orc, lat, bps, heads, seq, qph, scale, data_seed=seq * 31 + qph)
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_attention_random_shapes(hq, orc, case):
+    """Seeded random cases: any lattice, 1-3 heads, 1-1299 keys, 1-16 queries
+    per head, scales from 0 to sharp and negative, random tile ids."""
+    rng = np.random.default_rng(97000 + 2 * case)
+    lat = int(rng.integers(0, 4))
+    heads, seq, qph = int(rng.integers(1, 4)), int(rng.integers(1, 1300)), int(rng.integers(1, 17))
+    scale = float(rng.choice([0.0, 0.004, 128 ** -0.5, 0.5, -0.3]))
+    bps = float(rng.uniform(1.5, 4.0))
+    run_case(hq, orc, lat, bps, heads, seq, qph, scale, data_seed=97000 + 2 * case,
+             kb=int(rng.integers(0, 1 << 20)), vb=int(rng.integers(1 << 20, 1 << 21)))
+
+
 @pytest.mark.parametrize("scale,first", [(0.0, False), (0.004, False), (0.004, True)])
 def test_attention_bound_sees_a_missing_key(orc, scale, first):
     """The bound is tight enough to fail a result that leaves out one key (the
