@@ -131,6 +131,20 @@ def test_gemm_other_lattices(hq, orc, lat):
     run(hq, orc, lat, w, x, 0.004)
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_gemm_random_shapes(hq, orc, case):
+    """Seeded random cases: Z, D4 or E8, 1-150 rows, 1-24 column blocks,
+    1-64 vectors, weights and vectors of random scale."""
+    rng = np.random.default_rng(31000 + case)
+    lat = int(rng.choice([0, 2, 3]))
+    rows, cols, nb = int(rng.integers(1, 151)), 128 * int(rng.integers(1, 25)), int(rng.integers(1, 65))
+    g = torch.Generator().manual_seed(31000 + case)
+    w = (torch.randn(rows, cols, generator=g) * float(rng.uniform(0.005, 0.5))).to(torch.bfloat16)
+    x = (torch.randn(nb, cols, generator=g) * float(rng.uniform(0.1, 10.0))).numpy().astype(np.float32)
+    alpha = float(np.float32(float(w.float().pow(2).mean().sqrt()) * float(rng.uniform(0.05, 0.5))))
+    run(hq, orc, lat, w, x, alpha)
+
+
 def test_gemm_large_codes(hq, orc):
     """Codes of 2^16 and more (alpha far below the data's scale), where the
     code's bf16 split is inexact and the 2^-16 term carries the error."""
