@@ -153,8 +153,16 @@ hq_status hq_kv_append(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n
                        uint64_t tile_base, uint32_t* words, uint64_t cap_words, uint64_t* offsets,
                        uint8_t* k, uint64_t n_prev, void* ws, void* stream);
 
-/* Decode n_tiles tiles into y (fp32 or bf16).  n_words bounds the reads of
- * words. */
+/* Decode n_tiles tiles into y (fp32 or bf16): the inverse of each encode step
+ * [Methodology 3: parse each record and restore the stripped bits;
+ * Methodology 2: the lattice point in real coordinates (A2: (i, j sqrt 3)),
+ * scaled by alpha; Methodology 1: the transposed transform D H^T / sqrt n,
+ * H symmetric, so x_hat = D (c_dec H u_hat) with c_dec = alpha / sqrt 128].
+ * y: n_tiles * 128 elements, 16-byte aligned, row-major like the input.
+ * n_words is the number of readable words at `words` (at least
+ * ceil(offsets[n_tiles] / 32)); records whose span leaves [0, n_words) are
+ * reported as HQ_ERR_CORRUPT instead of being read.  bf16 output rounds the
+ * fp32 value to nearest even.  ws: the codec workspace (its status word). */
 hq_status hq_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
                     const uint64_t* offsets, const uint8_t* k, uint64_t n_tiles, void* y,
                     hq_dtype out_dtype, void* ws, void* stream);
@@ -170,7 +178,11 @@ hq_status hq_kv_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
                        uint64_t tile_base, void* y, hq_dtype out_dtype, void* ws, void* stream);
 
 /* Attention scores against dithered compressed keys, without materialising
- * them: scores[(h*qph + g)*tiles_per_head + s] = q_{h,g} . k_hat_{h,s}
+ * them [Methodology 4: the dithered KV quantiser keeps every inner product
+ * q . k_hat unbiased; Methodology 1: the rotation is orthogonal, so
+ * q . k_hat = <R q, R k_hat> is taken in the rotated domain, where the
+ * decoder's k_hat is c_dec u_hat before its inverse transform]:
+ * scores[(h*qph + g)*tiles_per_head + s] = q_{h,g} . k_hat_{h,s}
  * = c_dec <H D q_{h,g}, u_hat_{h,s}> for the keys of n_heads heads stored as
  * tiles h*tiles_per_head + s of one encode (tile ids tile_base + that).
  * With a Haar plan, = alpha <Q q_{h,g}, u_hat_{h,s}> (Q orthogonal): the
@@ -180,7 +192,8 @@ hq_status hq_kv_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
  * hq_kv_scores_workspace_bytes(plan, n_heads, tiles_per_head, qph) bytes
  * (the codec workspace of the n_heads * tiles_per_head tiles suffices unless a
  * Haar plan has qph > tiles_per_head), zero-filled once, 16-byte aligned for a
- * Haar plan.  Corrupt records score 0 and set HQ_ERR_CORRUPT. */
+ * Haar plan.  n_words: readable words at `words`, as for hq_decode.
+ * Corrupt records score 0 and set HQ_ERR_CORRUPT. */
 size_t hq_kv_scores_workspace_bytes(hq_plan_t plan, uint32_t n_heads, uint64_t tiles_per_head, uint32_t qph);
 hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words,
                        const uint64_t* offsets, const uint8_t* k, uint32_t n_heads,

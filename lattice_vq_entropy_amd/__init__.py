@@ -136,6 +136,20 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError("input must be float32 or bfloat16")
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(t: torch.Tensor, nbytes: int, what: str):
+    """Raise ValueError (instead of a device out-of-bounds access) when the
+    buffer t holds fewer than nbytes bytes."""
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{what}: {_nbytes(t)} bytes, {nbytes} needed")
+
+
+WS_HEADER_BYTES = 256  # the status word and counters at the start of every workspace
+
+
 def _n_tiles(t: torch.Tensor) -> int:
     if t.numel() % TILE:
         raise ValueError("the number of elements must be a multiple of 128")
@@ -151,6 +165,7 @@ class Plan:
         _check(lib().hq_plan(lat, tile, float(bps), int(seed), C.byref(h)), "hq_plan")
         self._h = h
         self.lattice, self.bps, self.seed = lat, float(bps), int(seed)
+        self.rot = 0
 
     @classmethod
     def from_header(cls, header: bytes) -> "Plan":
@@ -162,6 +177,7 @@ class Plan:
         self = cls.__new__(cls)
         self._h = h
         self.lattice, self.bps, self.seed = int(info.lattice), float(info.bps), int(info.seed)
+        self.rot = 0
         return self
 
     def __del__(self):
@@ -182,6 +198,7 @@ class Plan:
         _check(lib().hq_plan_set_rotation(self._h, int(kind), _dptr(buf), _stream(stream) if buf is not None
                                           else C.c_void_p(0)), "hq_plan_set_rotation")
         self._rot_buf = buf
+        self.rot = int(kind)
         return self
 
     def rotation(self):
@@ -211,6 +228,11 @@ class Plan:
 
     def bound_words(self, n_tiles: int) -> int:
         return int(lib().hq_encode_bound_words(self._h, n_tiles))
+
+    def decode_workspace_bytes(self, n_tiles: int) -> int:
+        """Bytes a decode of n_tiles reads and writes in its workspace: the
+        status header, and with the Haar rotation the rotated tiles."""
+        return self.workspace_bytes(n_tiles) if self.rot else WS_HEADER_BYTES
 
     def workspace(self, n_tiles: int, device="cuda") -> torch.Tensor:
         """A zero-filled workspace (the zero fill is required once)."""
@@ -252,7 +274,12 @@ def encode(plan: Plan, x: torch.Tensor, ws: torch.Tensor, out=None, dithered: bo
     """hq_encode / hq_kv_encode (asynchronous; check hq_status_sync for data errors)."""
     n = _n_tiles(x)
     words, offsets, k = out if out is not None else alloc_stream(plan, n, x.device)
-    cap = words.numel() if cap_words is None else cap_words
+    cap = _nbytes(words) // 4 if cap_words is None else cap_words
+    if cap > _nbytes(words) // 4:
+        raise ValueError(f"cap_words {cap} exceeds the {_nbytes(words) // 4} words of the stream buffer")
+    _need(offsets, 8 * (n + 1), "offsets")
+    _need(k, n, "k")
+    _need(ws, plan.workspace_bytes(n), "workspace")
     if dithered:
         rc = lib().hq_kv_encode(plan.handle, _dptr(x), _dtype_code(x), n, tile_base, _dptr(words), cap,
                                 _dptr(offsets), _dptr(k), _dptr(ws), _stream(stream))
@@ -268,8 +295,9 @@ def append(plan: Plan, enc: Encoded, x: torch.Tensor, ws: torch.Tensor, stream=N
     (allocate them with room, e.g. alloc_stream(plan, capacity_tiles), and encode into them)."""
     n, n_prev = _n_tiles(x), enc.n_tiles
     words, offsets, k = enc.storage
-    if offsets.numel() < n_prev + n + 1 or k.numel() < n_prev + n:
+    if _nbytes(offsets) < 8 * (n_prev + n + 1) or _nbytes(k) < n_prev + n:
         raise ValueError("the stream's buffers have no room for the appended tiles")
+    _need(ws, plan.workspace_bytes(n), "workspace")
     if enc.dithered:
         rc = lib().hq_kv_append(plan.handle, _dptr(x), _dtype_code(x), n, enc.tile_base + n_prev, _dptr(words),
                                 words.numel(), _dptr(offsets), _dptr(k), n_prev, _dptr(ws), _stream(stream))
@@ -287,11 +315,16 @@ def decode(plan: Plan, enc: Encoded, ws: torch.Tensor, out: torch.Tensor | None 
     n = enc.n_tiles
     y = out if out is not None else torch.empty(n * TILE, dtype=out_dtype, device=enc.words.device)
     code = _dtype_code(y)
+    if y.numel() < n * TILE:
+        raise ValueError(f"output of {y.numel()} elements, {n * TILE} needed")
+    _need(enc.offsets, 8 * (n + 1), "offsets")
+    _need(enc.k, n, "k")
+    _need(ws, plan.decode_workspace_bytes(n), "workspace")
     if enc.dithered:
-        rc = lib().hq_kv_decode(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets),
+        rc = lib().hq_kv_decode(plan.handle, _dptr(enc.words), _nbytes(enc.words) // 4, _dptr(enc.offsets),
                                 _dptr(enc.k), n, enc.tile_base, _dptr(y), code, _dptr(ws), _stream(stream))
     else:
-        rc = lib().hq_decode(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),
+        rc = lib().hq_decode(plan.handle, _dptr(enc.words), _nbytes(enc.words) // 4, _dptr(enc.offsets), _dptr(enc.k),
                              n, _dptr(y), code, _dptr(ws), _stream(stream))
     _check(rc, "decode")
     return y
@@ -307,7 +340,9 @@ def kv_scores(plan: Plan, enc: Encoded, n_heads: int, tiles_per_head: int, q: to
         raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes, {need} needed")
     s = out if out is not None else torch.empty(n_heads * qph, tiles_per_head, dtype=torch.float32,
                                                 device=q.device)
-    rc = lib().hq_kv_scores(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),
+    _need(s, 4 * n_heads * qph * tiles_per_head, "scores")
+    _need(enc.offsets, 8 * (n_heads * tiles_per_head + 1), "offsets")
+    rc = lib().hq_kv_scores(plan.handle, _dptr(enc.words), _nbytes(enc.words) // 4, _dptr(enc.offsets), _dptr(enc.k),
                             n_heads, tiles_per_head, enc.tile_base, _dptr(q), qph, _dptr(s), _dptr(ws),
                             _stream(stream))
     _check(rc, "kv_scores")
@@ -329,7 +364,9 @@ def gemv(plan: Plan, enc: Encoded, rows: int, cols: int, x: torch.Tensor, ws: to
         raise ValueError("matrix-vector products take an undithered weight stream")
     nb = x.numel() // cols
     y = out if out is not None else torch.empty(nb, rows, dtype=torch.float32, device=x.device)
-    rc = lib().hq_gemv(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),
+    _need(y, 4 * nb * rows, "y")
+    _need(ws, int(lib().hq_gemv_workspace_bytes(rows, cols, nb)), "workspace")
+    rc = lib().hq_gemv(plan.handle, _dptr(enc.words), _nbytes(enc.words) // 4, _dptr(enc.offsets), _dptr(enc.k),
                        rows, cols, _dptr(x), nb, _dptr(y), _dptr(ws), _stream(stream))
     _check(rc, "gemv")
     return y
@@ -350,7 +387,9 @@ def gemm(plan: Plan, enc: Encoded, rows: int, cols: int, x: torch.Tensor, ws: to
         raise ValueError("matrix products take an undithered weight stream")
     nb = x.numel() // cols
     y = out if out is not None else torch.empty(nb, rows, dtype=torch.float32, device=x.device)
-    rc = lib().hq_gemm(plan.handle, _dptr(enc.words), enc.words.numel(), _dptr(enc.offsets), _dptr(enc.k),
+    _need(y, 4 * nb * rows, "y")
+    _need(ws, int(lib().hq_gemm_workspace_bytes(rows, cols, nb)), "workspace")
+    rc = lib().hq_gemm(plan.handle, _dptr(enc.words), _nbytes(enc.words) // 4, _dptr(enc.offsets), _dptr(enc.k),
                        rows, cols, _dptr(x), nb, _dptr(y), _dptr(ws), _stream(stream))
     _check(rc, "gemm")
     return y
@@ -374,9 +413,11 @@ def kv_attention(plan_k: Plan, enc_k: Encoded, plan_v: Plan, enc_v: Encoded, n_h
     if enc_k.n_tiles < n_heads * seq or enc_v.n_tiles < n_heads * seq:
         raise ValueError("the streams hold fewer than n_heads*seq tiles")
     o = out if out is not None else torch.empty(n_heads * qph, TILE, dtype=torch.float32, device=q.device)
-    rc = lib().hq_kv_attention(plan_k.handle, _dptr(enc_k.words), enc_k.words.numel(), _dptr(enc_k.offsets),
+    _need(o, 4 * n_heads * qph * TILE, "out")
+    _need(ws, int(lib().hq_kv_attention_workspace_bytes(n_heads, seq, qph)), "workspace")
+    rc = lib().hq_kv_attention(plan_k.handle, _dptr(enc_k.words), _nbytes(enc_k.words) // 4, _dptr(enc_k.offsets),
                                _dptr(enc_k.k), enc_k.tile_base, plan_v.handle, _dptr(enc_v.words),
-                               enc_v.words.numel(), _dptr(enc_v.offsets), _dptr(enc_v.k), enc_v.tile_base,
+                               _nbytes(enc_v.words) // 4, _dptr(enc_v.offsets), _dptr(enc_v.k), enc_v.tile_base,
                                n_heads, seq, _dptr(q), qph, scale, _dptr(o), _dptr(ws), _stream(stream))
     _check(rc, "kv_attention")
     return o

@@ -52,6 +52,12 @@ bool lattice_ok(int lat) { return lat >= HQ_Z && lat <= HQ_E8; }
 
 hq_status dev_err(hipError_t e) { return e == hipSuccess ? HQ_OK : HQ_ERR_DEVICE; }
 
+// A stream as the decode kernels read it: words in whole 16-byte groups from
+// the 16-byte boundary below each chunk's first record, offsets as uint64.
+bool stream_aligned(const uint32_t* words, const uint64_t* offsets) {
+  return (((uintptr_t)words & 15u) == 0) && (((uintptr_t)offsets & 7u) == 0);
+}
+
 // The fp32 scale constants for alpha: the RHT folds 1/sqrt(128) in, the
 // (orthonormal) Haar matrix does not.
 void plan_scales(hq_plan_s* p, float alpha) {
@@ -200,7 +206,8 @@ hq_status decode_impl(hq_plan_t plan, const uint32_t* words, uint64_t n_words, c
   if (out_dtype != HQ_F32 && out_dtype != HQ_BF16) return HQ_ERR_ARG;
   if (n_tiles == 0) return HQ_OK;
   if (!words || !offsets || !k || !y || !ws) return HQ_ERR_ARG;
-  if (((uintptr_t)y & 15u) != 0) return HQ_ERR_ARG;
+  if (((uintptr_t)y & 15u) != 0 || ((uintptr_t)ws & 15u) != 0 || !stream_aligned(words, offsets)) return HQ_ERR_ARG;
+  if (hq::ws_chunks(n_tiles) > 0x7FFFFFFFull) return HQ_ERR_ARG;
   hq::DecArgs a{};
   a.words = words;
   a.n_words = n_words;
@@ -448,6 +455,7 @@ hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words, 
   if (!words || !offsets || !k || !q || !scores || !ws) return HQ_ERR_ARG;
   const uint64_t cph = (tiles_per_head + hq::kChunkTiles - 1) / hq::kChunkTiles;
   if (cph > 0x7FFFFFFFull || n_heads > 65535u) return HQ_ERR_ARG;
+  if (!stream_aligned(words, offsets) || ((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
   if (plan->rot == 1 && ((((uintptr_t)q | (uintptr_t)ws) & 15u) != 0)) return HQ_ERR_ARG;
   hq::DecArgs a{};
   a.words = words;
@@ -495,7 +503,7 @@ hq_status hq_gemv(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const
   if (cols == 0 || cols % 128 || nb == 0 || nb > 16) return HQ_ERR_ARG;
   if (rows == 0) return HQ_OK;
   if (!words || !offsets || !k || !x || !y || !ws) return HQ_ERR_ARG;
-  if (((uintptr_t)x & 15u) != 0 || ((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+  if (((uintptr_t)x & 15u) != 0 || ((uintptr_t)ws & 15u) != 0 || !stream_aligned(words, offsets)) return HQ_ERR_ARG;
   const uint64_t nblk = cols / 128, n_tiles = rows * nblk;
   if (rows > 0xFFFFFFFFull || n_tiles / nblk != rows || n_tiles > 0xFFFFFFFFull || (uint64_t)nb * rows > 0xFFFFFFFFull ||
       (uint64_t)nb * nblk > 0xFFFFFFFFull)
@@ -562,7 +570,7 @@ hq_status hq_gemm(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const
   if (cols == 0 || cols % 128 || nb == 0 || nb > hq::kGemmMaxVec) return HQ_ERR_ARG;
   if (rows == 0) return HQ_OK;
   if (!words || !offsets || !k || !x || !y || !ws) return HQ_ERR_ARG;
-  if (((uintptr_t)x & 15u) != 0 || ((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+  if (((uintptr_t)x & 15u) != 0 || ((uintptr_t)ws & 15u) != 0 || !stream_aligned(words, offsets)) return HQ_ERR_ARG;
   const uint64_t nblk = cols / 128;
   if (rows > 0x7FFFFFFFull || nblk > 0xFFFFFFFFull || rows * nblk / nblk != rows || (uint64_t)nb * rows > 0xFFFFFFFFull)
     return HQ_ERR_ARG;
@@ -617,6 +625,7 @@ hq_status hq_kv_attention(hq_plan_t plan_k, const uint32_t* k_words, uint64_t k_
   if (seq == 0 || !k_words || !k_offsets || !k_k || !v_words || !v_offsets || !v_k || !q || !out || !ws)
     return HQ_ERR_ARG;
   if (((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
+  if (!stream_aligned(k_words, k_offsets) || !stream_aligned(v_words, v_offsets)) return HQ_ERR_ARG;
   if (plan_k->rot == 1 && ((((uintptr_t)q | (uintptr_t)out) & 15u) != 0)) return HQ_ERR_ARG;
   const uint64_t groups = (seq + hq::kAttnChunks * hq::kChunkTiles - 1) / (hq::kAttnChunks * hq::kChunkTiles);
   if (n_heads > 65535u || groups > 0x7FFFFFFFull || seq > (1ull << 40)) return HQ_ERR_ARG;

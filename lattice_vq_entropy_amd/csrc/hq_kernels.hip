@@ -1,10 +1,16 @@
 // hq_kernels.hip -- HIP kernels of the HyperQuant per-tile codec for gfx950.
 //
 // encode_k  : RHT -> (dither) -> nearest point -> strip -> zigzag -> Rice k ->
-//             tile lengths -> work-group scan -> single-pass decoupled look-back
-//             for the global bit offset -> LDS bit assembly -> coalesced stores.
-//             [HQ Methodology 1-4; decoupled look-back after Merrill & Garland,
-//             "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016]
+//             tile lengths -> scan within the chunk -> LDS bit assembly -> the
+//             chunk's bits staged in the workspace, its bit count recorded.
+//             [HQ Methodology 1-4]
+// blocksum_k, blockscan_k (large tensors only): bit counts of blocks of 1024
+//             chunks, and their exclusive prefixes.
+// place_k   : each chunk's global bit offset from the counts before it, then
+//             its staged bits funnel-shifted into the stream with aligned
+//             16-byte stores; per-tile offsets.  No work-group waits on
+//             another: the stream-ordered launches are the only
+//             synchronisation.
 // decode_k  : per tile, remainders at fixed positions and the unary section by
 //             a 16-lane popcount scan and in-word select, then unstrip,
 //             (dither), inverse RHT, scale, bf16/fp32 stores; or, in score
