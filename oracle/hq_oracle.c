@@ -23,6 +23,13 @@
 #define RANGE_LIMIT 1048576.0f /* 2^20: codes stay below 2^21 */
 #define M_LIMIT (1u << 22)    /* largest zigzag symbol a valid stream holds */
 
+/* Host threads for whole-tensor encode, decode and rate passes (1: the plain
+ * serial loops).  With more, the per-tile steps run on that many OpenMP
+ * threads; see the parallel section below.  The results do not depend on it. */
+static int g_threads = 1;
+void orc_set_threads(int n) { g_threads = n > 0 ? n : 1; }
+int orc_get_threads(void) { return g_threads; }
+
 /* ------------------------------------------------------------------------ */
 /* Philox4x32-10 [Philox]: ten rounds of two 32x32->64 multiplies with the   */
 /* published multipliers, the key bumped by the published Weyl constants.    */
@@ -500,22 +507,39 @@ static int tile_symbols(int lat, const int32_t codes[128], uint32_t m[128], uint
 /*   stream bit P is bit (P & 31) of uint32 word P >> 5; records abut.       */
 /* ------------------------------------------------------------------------ */
 static void put_bit(uint32_t *w, uint64_t pos) { w[pos >> 5] |= 1u << (pos & 31); }
+/* the same when several threads write records that share a boundary word */
+static void put_bit_atomic(uint32_t *w, uint64_t pos) {
+  __atomic_fetch_or(&w[pos >> 5], 1u << (pos & 31), __ATOMIC_RELAXED);
+}
 static int get_bit(const uint32_t *w, uint64_t pos) { return (int)((w[pos >> 5] >> (pos & 31)) & 1u); }
 
-static void write_record(uint32_t *words, uint64_t off, int raw_bits, uint32_t raw,
-                         const uint32_t m[128], int k) {
+static void write_record_with(void (*put)(uint32_t *, uint64_t), uint32_t *words, uint64_t off, int raw_bits,
+                              uint32_t raw, const uint32_t m[128], int k) {
   uint64_t p = off;
   for (int b = 0; b < raw_bits; ++b, ++p)
-    if ((raw >> b) & 1u) put_bit(words, p);
+    if ((raw >> b) & 1u) put(words, p);
   for (int i = 0; i < N; ++i)
     for (int b = 0; b < k; ++b, ++p)
-      if ((m[i] >> b) & 1u) put_bit(words, p);
+      if ((m[i] >> b) & 1u) put(words, p);
   for (int i = 0; i < N; ++i) {
     p += m[i] >> k;
-    put_bit(words, p);
+    put(words, p);
     ++p;
   }
 }
+
+static void write_record(uint32_t *words, uint64_t off, int raw_bits, uint32_t raw,
+                         const uint32_t m[128], int k) {
+  write_record_with(put_bit, words, off, raw_bits, raw, m, k);
+}
+
+static int encode_par(int lat, uint64_t seed, const rot_ctx *r, const void *x, int dtype, uint64_t n_tiles,
+                      int dithered, uint64_t tile_base, uint32_t *words, uint64_t cap_words, uint64_t *offsets,
+                      uint8_t *k);
+static int total_bits_par(int lat, uint64_t seed, const rot_ctx *r, const void *x, int dtype, uint64_t n_tiles,
+                          int dithered, uint64_t tile_base, uint64_t *bits);
+static int decode_par(int lat, uint64_t seed, const rot_ctx *r, const uint32_t *words, const uint64_t *offsets,
+                      const uint8_t *k, uint64_t n_tiles, int dithered, uint64_t tile_base, void *y, int dtype);
 
 uint64_t orc_write_record_codes(int lat, const int32_t codes[128], uint32_t *words,
                                 uint64_t off, int *k_out) {
@@ -541,6 +565,11 @@ int orc_encode_r(int lat, uint64_t seed, float alpha, int rot, const void *x, in
   if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
   rot_ctx r;
   if (ctx_init(&r, rot, seed, alpha) != ORC_OK) return ORC_ERR_ARG;
+  if (g_threads > 1) {
+    int st = encode_par(lat, seed, &r, x, dtype, n_tiles, dithered, tile_base, words, cap_words, offsets, k);
+    ctx_free(&r);
+    return st;
+  }
   int status = ORC_OK;
   uint64_t off = 0, zeroed = 0; /* words [0, zeroed) have been cleared */
   offsets[0] = 0;
@@ -583,6 +612,11 @@ int orc_total_bits_r(int lat, uint64_t seed, float alpha, int rot, const void *x
   if (lat_dim(lat) == 0 || !(alpha > 0.0f) || !isfinite(alpha)) return ORC_ERR_ARG;
   rot_ctx r;
   if (ctx_init(&r, rot, seed, alpha) != ORC_OK) return ORC_ERR_ARG;
+  if (g_threads > 1) {
+    int st = total_bits_par(lat, seed, &r, x, dtype, n_tiles, dithered, tile_base, bits);
+    ctx_free(&r);
+    return st;
+  }
   uint64_t total = 0;
   for (uint64_t t = 0; t < n_tiles; ++t) {
     float xt[N];
@@ -704,6 +738,11 @@ int orc_decode_r(int lat, uint64_t seed, float alpha, int rot, const uint32_t *w
   if (dtype != ORC_F32 && dtype != ORC_BF16) return ORC_ERR_ARG;
   rot_ctx r;
   if (ctx_init(&r, rot, seed, alpha) != ORC_OK) return ORC_ERR_ARG;
+  if (g_threads > 1) {
+    int st = decode_par(lat, seed, &r, words, offsets, k, n_tiles, dithered, tile_base, y, dtype);
+    ctx_free(&r);
+    return st;
+  }
   int status = ORC_OK;
   for (uint64_t t = 0; t < n_tiles; ++t) {
     int32_t codes[N];
@@ -722,6 +761,121 @@ int orc_decode_r(int lat, uint64_t seed, float alpha, int rot, const uint32_t *w
     }
   }
   ctx_free(&r);
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The same whole-tensor passes on g_threads host threads (OpenMP), for      */
+/* large tensors.  Each tile's steps are those of the serial loops; the      */
+/* exclusive scan of the record lengths stays serial; records are written    */
+/* in parallel, a bit at a time with an atomic OR (every stream bit has one  */
+/* writer and OR commutes, so no word depends on the order of the writes).   */
+/* Status: the serial encoder and rate pass stop at the first failing tile,  */
+/* so these report the first failing tile's status too; the serial decoder   */
+/* keeps the last failing tile's status, and so does decode_par.  Statuses,  */
+/* and the outputs of every call that succeeds (and every decode), therefore */
+/* equal the serial functions'; a failing encode's outputs are unspecified.  */
+/* ------------------------------------------------------------------------ */
+static int encode_par(int lat, uint64_t seed, const rot_ctx *r, const void *x, int dtype, uint64_t n_tiles,
+                      int dithered, uint64_t tile_base, uint32_t *words, uint64_t cap_words, uint64_t *offsets,
+                      uint8_t *k) {
+  uint32_t *m = (uint32_t *)malloc(sizeof(uint32_t) * N * (n_tiles ? n_tiles : 1));
+  uint32_t *raw = (uint32_t *)malloc(sizeof(uint32_t) * (n_tiles ? n_tiles : 1));
+  uint64_t *len = (uint64_t *)malloc(sizeof(uint64_t) * (n_tiles ? n_tiles : 1));
+  int *tst = (int *)malloc(sizeof(int) * (n_tiles ? n_tiles : 1));
+  if (!m || !raw || !len || !tst) {
+    free(m); free(raw); free(len); free(tst);
+    return ORC_ERR_ARG;
+  }
+  const int raw_bits = lat == ORC_E8 ? 16 : 0;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+  for (int64_t ti = 0; ti < (int64_t)n_tiles; ++ti) {
+    const uint64_t t = (uint64_t)ti;
+    float xt[N];
+    int32_t codes[N];
+    for (int i = 0; i < N; ++i) xt[i] = load_elem(x, dtype, t * N + (uint64_t)i);
+    tst[t] = quantize_tile_s(lat, seed, r, xt, dithered, tile_base + t, codes);
+    if (tst[t] != ORC_OK) continue;
+    tile_symbols(lat, codes, &m[t * N], &raw[t]);
+    const int kt = orc_rice_kstar(&m[t * N], raw_bits);
+    k[t] = (uint8_t)kt;
+    len[t] = orc_rice_len(&m[t * N], kt, raw_bits);
+  }
+  int status = ORC_OK;
+  for (uint64_t t = 0; t < n_tiles; ++t)
+    if (tst[t] != ORC_OK) { status = tst[t]; break; }
+  if (status == ORC_OK) {
+    offsets[0] = 0;
+    uint64_t n_fit = 0; /* records written: those whose last word fits, a prefix of the tiles */
+    for (uint64_t t = 0; t < n_tiles; ++t) {
+      offsets[t + 1] = offsets[t] + len[t];
+      if ((offsets[t + 1] + 31) / 32 <= cap_words && n_fit == t) n_fit = t + 1;
+    }
+    if (n_fit < n_tiles) status = ORC_ERR_CAPACITY;
+    const uint64_t wend = (offsets[n_fit] + 31) / 32;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t w = 0; w < (int64_t)wend; ++w) words[w] = 0u;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t ti = 0; ti < (int64_t)n_fit; ++ti) {
+      const uint64_t t = (uint64_t)ti;
+      write_record_with(put_bit_atomic, words, offsets[t], raw_bits, raw[t], &m[t * N], (int)k[t]);
+    }
+  }
+  free(m); free(raw); free(len); free(tst);
+  return status;
+}
+
+static int total_bits_par(int lat, uint64_t seed, const rot_ctx *r, const void *x, int dtype, uint64_t n_tiles,
+                          int dithered, uint64_t tile_base, uint64_t *bits) {
+  int *tst = (int *)malloc(sizeof(int) * (n_tiles ? n_tiles : 1));
+  if (!tst) return ORC_ERR_ARG;
+  const int raw_bits = lat == ORC_E8 ? 16 : 0;
+  uint64_t total = 0;
+#pragma omp parallel for num_threads(g_threads) schedule(static) reduction(+ : total)
+  for (int64_t ti = 0; ti < (int64_t)n_tiles; ++ti) {
+    const uint64_t t = (uint64_t)ti;
+    float xt[N];
+    int32_t codes[N];
+    uint32_t m[N], raw;
+    for (int i = 0; i < N; ++i) xt[i] = load_elem(x, dtype, t * N + (uint64_t)i);
+    tst[t] = quantize_tile_s(lat, seed, r, xt, dithered, tile_base + t, codes);
+    if (tst[t] != ORC_OK) continue;
+    tile_symbols(lat, codes, m, &raw);
+    total += orc_rice_len(m, orc_rice_kstar(m, raw_bits), raw_bits);
+  }
+  int status = ORC_OK;
+  for (uint64_t t = 0; t < n_tiles; ++t)
+    if (tst[t] != ORC_OK) { status = tst[t]; break; }
+  free(tst);
+  if (status == ORC_OK) *bits = total;
+  return status;
+}
+
+static int decode_par(int lat, uint64_t seed, const rot_ctx *r, const uint32_t *words, const uint64_t *offsets,
+                      const uint8_t *k, uint64_t n_tiles, int dithered, uint64_t tile_base, void *y, int dtype) {
+  int *tst = (int *)malloc(sizeof(int) * (n_tiles ? n_tiles : 1));
+  if (!tst) return ORC_ERR_ARG;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+  for (int64_t ti = 0; ti < (int64_t)n_tiles; ++ti) {
+    const uint64_t t = (uint64_t)ti;
+    int32_t codes[N];
+    float v[N];
+    tst[t] = orc_parse_tile(lat, words, offsets[t], offsets[t + 1], (int)k[t], codes);
+    if (tst[t] != ORC_OK) {
+      for (int i = 0; i < N; ++i) v[i] = 0.0f;
+    } else {
+      dequant_codes(lat, seed, codes, dithered, tile_base + t, v);
+      ctx_inverse(r, v);
+    }
+    for (int i = 0; i < N; ++i) {
+      if (dtype == ORC_BF16) ((uint16_t *)y)[t * N + (uint64_t)i] = f32_to_bf16_rne(v[i]);
+      else ((float *)y)[t * N + (uint64_t)i] = v[i];
+    }
+  }
+  int status = ORC_OK;
+  for (uint64_t t = 0; t < n_tiles; ++t)
+    if (tst[t] != ORC_OK) status = tst[t];
+  free(tst);
   return status;
 }
 

@@ -142,6 +142,14 @@ int orc_gemv(int lat, uint64_t seed, float alpha, const uint32_t *words, const u
 
 /* Rate calibration: bisection on log2(alpha) for the payload rate
  * (bits per scalar).  Returns an ORC_ status. */
+/* Host threads of the whole-tensor encode, decode and rate passes (default
+ * 1: the plain serial loops).  With n > 1 they run the per-tile steps on n
+ * OpenMP threads (the length scan stays serial, record bits are ORed in
+ * atomically); statuses and the outputs of successful calls do not depend
+ * on n.  Not thread-safe against concurrent codec calls. */
+void orc_set_threads(int n);
+int orc_get_threads(void);
+
 /* Haar rotation variant (rot = 1; rot = 0 is the RHT): the matrix and the
  * codec calls with a rotation argument. */
 void orc_haar(uint64_t seed, float q32[128 * 128]);

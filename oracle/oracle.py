@@ -32,7 +32,7 @@ MAX_RECORD_BITS = {Z: 128 * 23, A2: 128 * 23, D4: 128 * 23, E8: 16 + 128 * 23}
 # -O2 without -ffast-math and with contraction off: each fp32 operation is one
 # IEEE binary32 operation in source order.
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11",
-          "-D_GNU_SOURCE", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+          "-D_GNU_SOURCE", "-Wall", "-Wextra", "-Wno-unused-parameter", "-fopenmp"]
 
 
 def build(force: bool = False) -> str:
@@ -92,6 +92,8 @@ def lib():
             "orc_decode_r": (_i, [_i, _u64, _f, _i, _p, _p, _p, _u64, _i, _u64, _p, _i]),
             "orc_calibrate_r": (_i, [_i, _u64, _f, _i, _p, _i, _u64, _i, _u64, _p, _p, _p]),
             "orc_crc32": (C.c_uint32, [_p, C.c_size_t]),
+            "orc_set_threads": (None, [_i]),
+            "orc_get_threads": (_i, []),
             "orc_header_write": (None, [_i, _u64, _f, _f, _i, _i, _u64, _u64, _u64, _p]),
             "orc_header_write_r": (None, [_i, _u64, _f, _f, _i, _i, _i, _u64, _u64, _u64, _p]),
             "orc_side_pack": (_i, [_p, _p, _u64, _p]),
@@ -245,6 +247,32 @@ def quantize_tile(lat: int, seed: int, alpha: float, x: np.ndarray, dithered=Fal
 # --------------------------------------------------------------------------- #
 def bound_words(lat: int, n_tiles: int) -> int:
     return (n_tiles * MAX_RECORD_BITS[lat] + 31) // 32
+
+
+def set_threads(n: int) -> None:
+    """Host threads of the whole-tensor encode, decode, rate and calibration
+    passes (1: the plain serial loops; the results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().orc_get_threads())
+
+
+class threads:
+    """with threads(n): ... -- the oracle on n host threads inside the block."""
+
+    def __init__(self, n: int):
+        self.n, self.prev = int(n), None
+
+    def __enter__(self):
+        self.prev = get_threads()
+        set_threads(self.n)
+        return self
+
+    def __exit__(self, *exc):
+        set_threads(self.prev)
+        return False
 
 
 def encode(lat: int, seed: int, alpha: float, x: np.ndarray, dithered=False, tile_base=0,
