@@ -137,6 +137,25 @@ hq_status hq_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_ti
                     uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k,
                     void* ws, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: hq_encode
+ * with its workspace in the library's own static device scratch instead of a
+ * caller's buffer.  The scratch is one fixed array per GPU (the codec
+ * workspace of HQ_NOALLOC_MAX_TILES tiles, about 12 MB), created with the
+ * library's device code on each GPU that runs the call and held until the
+ * process ends; the call itself allocates nothing.
+ * Arguments as hq_encode, except: no ws; status is a caller-owned device
+ * block of 256 bytes, 16-byte aligned, zero-filled once, where data errors
+ * are recorded (read and clear it with hq_status_sync(status, stream)).
+ * n_tiles above HQ_NOALLOC_MAX_TILES, and plans with the Haar rotation,
+ * return HQ_ERR_ARG.  Every call on one GPU uses that GPU's one scratch, which
+ * keeps the last call's contents: calls that overlap on one GPU (on two
+ * streams, or from two threads without ordering) race; calls ordered on one
+ * stream do not.  The result equals hq_encode's bit for bit. */
+#define HQ_NOALLOC_MAX_TILES 32768u
+hq_status hq_encode_noalloc(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint32_t* words,
+                            uint64_t cap_words, uint64_t* offsets, uint8_t* k, void* status, void* stream);
+
 /* Append n_tiles tiles of x to a stream that holds n_prev tiles: the new
  * records start at bit offsets[n_prev] (read on the device, so the call stays
  * asynchronous), the existing bits below it are kept, and offsets[n_prev ..

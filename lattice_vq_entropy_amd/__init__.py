@@ -42,6 +42,7 @@ _SIGNATURES = {
     "hq_encode_bound_words": (_u64, [_p, _u64]),
     "hq_calibrate": (_i, [_p, _p, _i, _u64, _i, _u64, _p, _p, C.POINTER(_f), C.POINTER(C.c_double)]),
     "hq_encode": (_i, [_p, _p, _i, _u64, _p, _u64, _p, _p, _p, _p]),
+    "hq_encode_noalloc": (_i, [_p, _p, _i, _u64, _p, _u64, _p, _p, _p, _p]),
     "hq_decode": (_i, [_p, _p, _u64, _p, _p, _u64, _p, _i, _p, _p]),
     "hq_kv_encode": (_i, [_p, _p, _i, _u64, _u64, _p, _u64, _p, _p, _p, _p]),
     "hq_kv_decode": (_i, [_p, _p, _u64, _p, _p, _u64, _u64, _p, _i, _p, _p]),
@@ -288,6 +289,34 @@ def encode(plan: Plan, x: torch.Tensor, ws: torch.Tensor, out=None, dithered: bo
                              _dptr(k), _dptr(ws), _stream(stream))
     _check(rc, "encode")
     return Encoded(words, offsets[:n + 1], k[:max(n, 1)], n, tile_base, dithered, storage=(words, offsets, k))
+
+
+NOALLOC_MAX_TILES = 32768  # HQ_NOALLOC_MAX_TILES
+STATUS_BLOCK_BYTES = 256
+
+
+def status_block(device="cuda") -> torch.Tensor:
+    """A zero-filled status block for encode_noalloc (read with status_sync/check)."""
+    return torch.zeros(STATUS_BLOCK_BYTES, dtype=torch.uint8, device=device)
+
+
+def encode_noalloc(plan: Plan, x: torch.Tensor, status: torch.Tensor, out, cap_words: int | None = None,
+                   stream=None) -> Encoded:
+    """hq_encode_noalloc: hq_encode with the library's static device scratch as
+    its workspace (nothing is allocated by the call; out = (words, offsets, k)
+    must be given).  Data errors land in the status block."""
+    n = _n_tiles(x)
+    words, offsets, k = out
+    cap = _nbytes(words) // 4 if cap_words is None else cap_words
+    if cap > _nbytes(words) // 4:
+        raise ValueError(f"cap_words {cap} exceeds the {_nbytes(words) // 4} words of the stream buffer")
+    _need(offsets, 8 * (n + 1), "offsets")
+    _need(k, n, "k")
+    _need(status, STATUS_BLOCK_BYTES, "status block")
+    rc = lib().hq_encode_noalloc(plan.handle, _dptr(x), _dtype_code(x), n, _dptr(words), cap, _dptr(offsets),
+                                 _dptr(k), _dptr(status), _stream(stream))
+    _check(rc, "encode_noalloc")
+    return Encoded(words, offsets[:n + 1], k[:max(n, 1)], n, 0, False, storage=(words, offsets, k))
 
 
 def append(plan: Plan, enc: Encoded, x: torch.Tensor, ws: torch.Tensor, stream=None) -> Encoded:

@@ -6,6 +6,7 @@
 #include <cstdlib>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/hq.h"
@@ -136,9 +137,12 @@ void fill_common(const hq_plan_s* p, uint32_t sl16[4], uint32_t sl32[4], uint32_
   k1 = (uint32_t)(p->seed >> 32);
 }
 
+// status: where the kernels record data errors (the workspace's own header
+// unless given).
 hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, bool dither,
                       uint64_t tile_base, uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k,
-                      void* ws, void* stream, bool len_only, bool append = false, bool rotated = false) {
+                      void* ws, void* stream, bool len_only, bool append = false, bool rotated = false,
+                      hq::WsHeader* status = nullptr) {
   if (!plan) return HQ_ERR_ARG;
   if (!plan->has_alpha) return HQ_ERR_NOALPHA;
   if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_ARG;
@@ -147,7 +151,7 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   if (!len_only && !offsets) return HQ_ERR_ARG;
   if (n_tiles == 0) {
     if (len_only || append) return HQ_OK;
-    return dev_err(hipMemsetAsync(offsets, 0, sizeof(uint64_t), st));
+    return dev_err(hq::launch_set_u64(offsets, 0, st));
   }
   if (!x) return HQ_ERR_ARG;
   if (!len_only && (!words || !k)) return HQ_ERR_ARG;
@@ -166,7 +170,7 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   fill_common(plan, a.sl16, a.sl32, a.key0, a.key1);
   a.c_enc = plan->c_enc;
   a.tile_base = tile_base;
-  a.ws = (hq::WsHeader*)ws;
+  a.ws = status ? status : (hq::WsHeader*)ws;
   const hq::WsLayout lay = hq::ws_layout(n_tiles);
   a.n_chunks = (uint32_t)hq::ws_chunks(n_tiles);
   a.agg = (uint32_t*)((char*)ws + lay.agg);
@@ -302,6 +306,38 @@ uint32_t crc32_ieee(const uint8_t* p, size_t n) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Workspace of hq_encode_noalloc: a fixed device array, one copy per GPU that
+// runs it, held until the process ends.  Sized for HQ_NOALLOC_MAX_TILES tiles
+// (the codec workspace layout of hq_ws.h; its header region is unused, the
+// call records data errors in the caller's status block instead).  In host
+// code `scratch` names a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[hq::ws_bytes(HQ_NOALLOC_MAX_TILES)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // per device: the device address of scratch, null until set up
+
+// The current device's scratch address, looked up on the device's first call.
+hq_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HQ_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HQ_ERR_DEVICE;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return HQ_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 hq_status hq_plan(hq_lattice lattice, int tile, float bps, uint64_t seed, hq_plan_t* out) {
@@ -402,6 +438,20 @@ uint64_t hq_encode_bound_words(hq_plan_t plan, uint64_t n_tiles) {
 hq_status hq_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint32_t* words,
                     uint64_t cap_words, uint64_t* offsets, uint8_t* k, void* ws, void* stream) {
   return encode_impl(plan, x, dtype, n_tiles, false, 0, words, cap_words, offsets, k, ws, stream, false);
+}
+
+hq_status hq_encode_noalloc(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint32_t* words,
+                            uint64_t cap_words, uint64_t* offsets, uint8_t* k, void* status, void* stream) {
+  if (!plan) return HQ_ERR_ARG;
+  if (!plan->has_alpha) return HQ_ERR_NOALPHA;
+  if (plan->rot != 0) return HQ_ERR_ARG;  // the scratch holds no rotated tiles
+  if (n_tiles > HQ_NOALLOC_MAX_TILES) return HQ_ERR_ARG;
+  if (!status || ((uintptr_t)status & 15u) != 0) return HQ_ERR_ARG;
+  void* ws = nullptr;
+  const hq_status s = scratch_address(&ws);
+  if (s != HQ_OK) return s;
+  return encode_impl(plan, x, dtype, n_tiles, false, 0, words, cap_words, offsets, k, ws, stream, false, false, false,
+                     (hq::WsHeader*)status);
 }
 
 hq_status hq_kv_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint64_t tile_base,
@@ -688,7 +738,7 @@ hq_status hq_side_pack(const uint64_t* offsets, const uint8_t* k, uint64_t n_til
 
 hq_status hq_side_unpack(const void* side, uint64_t n_tiles, uint64_t* offsets, uint8_t* k, void* stream) {
   if (!offsets) return HQ_ERR_ARG;
-  if (n_tiles == 0) return dev_err(hipMemsetAsync(offsets, 0, sizeof(uint64_t), (hipStream_t)stream));
+  if (n_tiles == 0) return dev_err(hq::launch_set_u64(offsets, 0, (hipStream_t)stream));
   if (!side || !k) return HQ_ERR_ARG;
   if (((uintptr_t)side & 15u) != 0 || ((uintptr_t)offsets & 7u) != 0) return HQ_ERR_ARG;
   if ((n_tiles + 255) / 256 > 0x7FFFFFFFull) return HQ_ERR_ARG;

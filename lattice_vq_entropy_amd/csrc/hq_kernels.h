@@ -147,5 +147,6 @@ hipError_t launch_side(bool pack, const uint64_t* offsets_in, const uint8_t* k_i
                        hipStream_t st);
 hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
                         hipStream_t st);
+hipError_t launch_set_u64(uint64_t* p, uint64_t v, hipStream_t st);
 
 }  // namespace hq

@@ -1963,6 +1963,16 @@ hipError_t launch_side(bool pack, const uint64_t* offsets_in, const uint8_t* k_i
   return hipGetLastError();
 }
 
+// One uint64 written by a kernel (the offsets[0] = 0 of an empty stream): a
+// launch instead of hipMemsetAsync, so that a captured graph holds no memset
+// node.
+__global__ void set_u64_k(uint64_t* p, uint64_t v) { *p = v; }
+
+hipError_t launch_set_u64(uint64_t* p, uint64_t v, hipStream_t st) {
+  hipLaunchKernelGGL(set_u64_k, dim3(1), dim3(1), 0, st, p, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
                         hipStream_t st) {
   uint64_t blocks = (n + 255) / 256;

@@ -25,8 +25,8 @@ constexpr int kSlotWords = 2964;
 // decode: LDS words holding one chunk's stream span
 constexpr int kStageWords = kChunkTiles * kMaxRecordWords + 4;
 
-inline uint64_t ws_chunks(uint64_t n_tiles) { return (n_tiles + kChunkTiles - 1) / kChunkTiles; }
-inline uint64_t ws_align(uint64_t b) { return (b + 255) & ~uint64_t(255); }
+constexpr uint64_t ws_chunks(uint64_t n_tiles) { return (n_tiles + kChunkTiles - 1) / kChunkTiles; }
+constexpr uint64_t ws_align(uint64_t b) { return (b + 255) & ~uint64_t(255); }
 
 // Regions after the header: agg (u32 per chunk), E (u64 per chunk + 1; the
 // length-only pass keeps its per-chunk partials here), loc (u32 per tile
@@ -35,9 +35,9 @@ inline uint64_t ws_align(uint64_t b) { return (b + 255) & ~uint64_t(255); }
 struct WsLayout {
   uint64_t agg, E, loc, tailw, stage, bytes;
 };
-inline WsLayout ws_layout(uint64_t n_tiles) {
+constexpr WsLayout ws_layout(uint64_t n_tiles) {
   const uint64_t c = ws_chunks(n_tiles);
-  WsLayout L;
+  WsLayout L{};
   L.agg = sizeof(WsHeader);
   L.E = L.agg + ws_align(4 * c);  // 64 counts a block: the scan reads whole uint4
   L.loc = L.E + ws_align(8 * (c + 1));
@@ -46,6 +46,6 @@ inline WsLayout ws_layout(uint64_t n_tiles) {
   L.bytes = L.stage + 4 * c * (uint64_t)kSlotWords;
   return L;
 }
-inline uint64_t ws_bytes(uint64_t n_tiles) { return ws_layout(n_tiles).bytes; }
+constexpr uint64_t ws_bytes(uint64_t n_tiles) { return ws_layout(n_tiles).bytes; }
 
 }  // namespace hq

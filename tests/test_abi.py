@@ -71,6 +71,12 @@ def test_argument_errors_are_synchronous(hq):
     assert L.hq_kv_append(p.handle, D, 1, 4, 0, D, 8, D, None, 2, D, None) == hq.ERR_ARG  # no k
     assert L.hq_append(p.handle, D, 1, 0, D, 8, D, D, 2, D, None) == hq.OK              # nothing to append
     assert L.hq_status_sync(None, None) == hq.ERR_ARG
+    # the allocation-free encode: size limit and status block checked on the host
+    big = hq.NOALLOC_MAX_TILES + 1
+    assert L.hq_encode_noalloc(p.handle, A, 1, big, A, 64, A, A, A, None) == hq.ERR_ARG
+    assert L.hq_encode_noalloc(p.handle, A, 1, 4, A, 64, A, A, None, None) == hq.ERR_ARG
+    assert L.hq_encode_noalloc(p.handle, A, 1, 4, A, 64, A, A, C.c_void_p(4100), None) == hq.ERR_ARG
+    assert L.hq_encode_noalloc(None, A, 1, 4, A, 64, A, A, A, None) == hq.ERR_ARG
     assert hq.status_str(hq.ERR_CORRUPT) == "corrupt stream"
     # matrix-vector products: shape and batch limits, null and misaligned pointers
     D = C.c_void_p(4096)
