@@ -847,17 +847,19 @@ hq_status hq_calibrate(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n
   hipStream_t st = (hipStream_t)stream;
   hq::WsHeader* h = (hq::WsHeader*)ws;
   const uint64_t n = n_tiles * 128ull;
-  double* partials = (double*)((char*)ws + sizeof(hq::WsHeader));
+  uint32_t* partials = (uint32_t*)((char*)ws + sizeof(hq::WsHeader));
   const uint64_t chunks = hq::ws_chunks(n_tiles);
-  if (hq::launch_sumsq(x, dtype == HQ_BF16, n, partials, (uint32_t)(chunks < 1024 ? chunks : 1024), &h->sumsq, st) !=
+  if (hq::launch_absmax(x, dtype == HQ_BF16, n, partials, (uint32_t)(chunks < 1024 ? chunks : 1024), &h->absmax, st) !=
       hipSuccess)
     return HQ_ERR_DEVICE;
-  double ss = 0.0;
-  if (hipMemcpyAsync(&ss, &h->sumsq, sizeof(double), hipMemcpyDeviceToHost, st) != hipSuccess) return HQ_ERR_DEVICE;
+  uint32_t amax_bits = 0;
+  if (hipMemcpyAsync(&amax_bits, &h->absmax, sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return HQ_ERR_DEVICE;
   if (hipStreamSynchronize(st) != hipSuccess) return HQ_ERR_DEVICE;
-  if (!std::isfinite(ss)) return HQ_ERR_NONFINITE;
-  const double sigma = std::sqrt(ss / (double)n);
-  if (!(sigma > 0.0)) return HQ_ERR_ARG;
+  if (amax_bits >= 0x7F800000u) return HQ_ERR_NONFINITE;
+  if (amax_bits == 0u) return HQ_ERR_ARG;
+  float amax;
+  std::memcpy(&amax, &amax_bits, sizeof(amax));
   if (plan->rot == 1) {  // the dense rotation once; every trial then scales it
     hq::RotArgs r{};
     r.x = x;
@@ -869,10 +871,20 @@ hq_status hq_calibrate(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n
     r.n_tiles = n_tiles;
     if (hq::launch_rot(r, st) != hipSuccess) return HQ_ERR_DEVICE;
   }
-  static const double nu[4] = {1.0, 1.8612097182041991, 1.1892071150027210, 2.0};
-  const double a0 = std::sqrt(2.0 * M_PI * M_E) * sigma / (nu[plan->lattice] * std::pow(2.0, (double)plan->bps));
+  // The bracket starts from exact integers only: the binary exponent eA of
+  // max |x|, eN = ceil(log2 N) and floor(bps); the high-resolution estimate
+  // sqrt(2 pi e) sigma / (nu 2^R), with sigma in [max/sqrt N, max] and nu in
+  // [1, 2], lies within [eA - floor(R) - 4 - ceil(eN/2), eA - floor(R) + 4]
+  // in log2, and the bracket widens by 4 octaves while it does not hold the
+  // target.  Nothing here depends on the order of a floating-point sum, so
+  // every exact evaluation of the rate takes the same path.
+  int eA1 = 0;
+  std::frexp((double)amax, &eA1);  // floor(log2 amax) = eA1 - 1
+  int eN = 0;
+  while ((1ull << eN) < n) ++eN;
+  const double eA = (double)(eA1 - 1), Rf = std::floor((double)plan->bps);
   const double target = (double)plan->bps;
-  double lo = std::floor(std::log2(a0)) - 4.0, hi = std::floor(std::log2(a0)) + 4.0;
+  double lo = eA - Rf - 4.0 - (double)((eN + 1) / 2), hi = eA - Rf + 4.0;
   float best_a = 0.0f;
   double best_r = 0.0, best_err = INFINITY;
   auto consider = [&](float a, double r) {

@@ -145,8 +145,8 @@ hipError_t launch_rot(const RotArgs& a, hipStream_t st);
 hipError_t launch_side(bool pack, const uint64_t* offsets_in, const uint8_t* k_in, const uint8_t* side_in,
                        uint64_t n, uint8_t* side_out, uint64_t* offsets_out, uint8_t* k_out, WsHeader* ws,
                        hipStream_t st);
-hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
-                        hipStream_t st);
+hipError_t launch_absmax(const void* x, bool bf16, uint64_t n, uint32_t* partials, uint32_t max_blocks, uint32_t* out,
+                         hipStream_t st);
 hipError_t launch_set_u64(uint64_t* p, uint64_t v, hipStream_t st);
 
 }  // namespace hq

@@ -1054,43 +1054,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
   }
 }
 
-// Sum of squares (fp64) for the calibration start point: one partial per
-// work-group (no same-address atomics), reduced in a fixed order.  16-byte
-// loads (8 bf16 or 4 fp32 values), four in flight per thread.
-__device__ __forceinline__ double sumsq_u4(const uint4& w, int bf16) {
+// Largest |x| of a calibration input, as the bit pattern of |x| (fp32
+// layout; bf16 values shifted up): for finite values the unsigned order of
+// these patterns is the numeric order, and a NaN or an infinity gives a
+// pattern >= 0x7F800000.  A maximum is exact and independent of the order
+// of evaluation.  One partial per work-group (no same-address atomics).
+__device__ __forceinline__ uint32_t absmax_u4(const uint4& w, int bf16) {
   const uint32_t q[4] = {w.x, w.y, w.z, w.w};
-  double acc = 0.0;
+  uint32_t m = 0u;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if (bf16) {
-      const double lo = (double)__builtin_bit_cast(float, q[j] << 16);
-      const double hi = (double)__builtin_bit_cast(float, q[j] & 0xFFFF0000u);
-      acc = __builtin_fma(lo, lo, acc);
-      acc = __builtin_fma(hi, hi, acc);
-    } else {
-      const double f = (double)__builtin_bit_cast(float, q[j]);
-      acc = __builtin_fma(f, f, acc);
-    }
+    if (bf16)  // the pair's high and low values, each as |x| in the fp32 layout
+      m = max(m, max(q[j] & 0x7FFF0000u, (q[j] << 16) & 0x7FFF0000u));
+    else
+      m = max(m, q[j] & 0x7FFFFFFFu);
   }
-  return acc;
+  return m;
 }
 
-__global__ __launch_bounds__(256) void sumsq_k(const void* x, int bf16, uint64_t n, double* partials) {
-  __shared__ double s_w[4];
+__global__ __launch_bounds__(256) void absmax_k(const void* x, int bf16, uint64_t n, uint32_t* partials) {
+  __shared__ uint32_t s_w[4];
   const uint4* p = reinterpret_cast<const uint4*>(x);
   const uint64_t n4 = bf16 ? n / 8 : n / 4;  // n is a multiple of 128
   const uint64_t stride = (uint64_t)gridDim.x * 256u;
-  double acc = 0.0;
   uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  uint32_t acc = 0u;
   for (; i + 3 * stride < n4; i += 4 * stride) {
     const uint4 w0 = p[i], w1 = p[i + stride], w2 = p[i + 2 * stride], w3 = p[i + 3 * stride];
-    acc += ((sumsq_u4(w0, bf16) + sumsq_u4(w1, bf16)) + (sumsq_u4(w2, bf16) + sumsq_u4(w3, bf16)));
+    acc = max(acc, max(max(absmax_u4(w0, bf16), absmax_u4(w1, bf16)), max(absmax_u4(w2, bf16), absmax_u4(w3, bf16))));
   }
-  for (; i < n4; i += stride) acc += sumsq_u4(p[i], bf16);
-  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  for (; i < n4; i += stride) acc = max(acc, absmax_u4(p[i], bf16));
+  for (int o = 32; o >= 1; o >>= 1) acc = max(acc, (uint32_t)__shfl_xor((int)acc, o));
   if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) partials[blockIdx.x] = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+  if (threadIdx.x == 0) partials[blockIdx.x] = max(max(s_w[0], s_w[1]), max(s_w[2], s_w[3]));
+}
+
+__global__ __launch_bounds__(1024) void reduce_max_k(const uint32_t* p, uint32_t n, uint32_t* out) {
+  __shared__ uint32_t s[1024];
+  const uint32_t tid = threadIdx.x;
+  uint32_t acc = 0u;
+  for (uint32_t i = tid; i < n; i += 1024u) acc = max(acc, p[i]);
+  s[tid] = acc;
+  __syncthreads();
+  for (int w = 512; w >= 1; w >>= 1) {
+    if ((int)tid < w) s[tid] = max(s[tid], s[tid + w]);
+    __syncthreads();
+  }
+  if (tid == 0) *out = s[0];
 }
 
 // One work-group of 1024 threads sums p[0..n) in a fixed order (eight loads
@@ -1973,13 +1984,13 @@ hipError_t launch_set_u64(uint64_t* p, uint64_t v, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_sumsq(const void* x, bool bf16, uint64_t n, double* partials, uint32_t max_blocks, double* out,
-                        hipStream_t st) {
+hipError_t launch_absmax(const void* x, bool bf16, uint64_t n, uint32_t* partials, uint32_t max_blocks, uint32_t* out,
+                         hipStream_t st) {
   uint64_t blocks = (n + 255) / 256;
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(sumsq_k, dim3((uint32_t)blocks), dim3(256), 0, st, x, bf16 ? 1 : 0, n, partials);
-  hipLaunchKernelGGL(reduce_k<double>, dim3(1), dim3(1024), 0, st, (const double*)partials, (uint32_t)blocks, out);
+  hipLaunchKernelGGL(absmax_k, dim3((uint32_t)blocks), dim3(256), 0, st, x, bf16 ? 1 : 0, n, partials);
+  hipLaunchKernelGGL(reduce_max_k, dim3(1), dim3(1024), 0, st, (const uint32_t*)partials, (uint32_t)blocks, out);
   return hipGetLastError();
 }
 

@@ -11,7 +11,8 @@ struct WsHeader {
   uint32_t reserved0[3];
   uint32_t status;          // bit (1 << code) for every error seen since the last sync
   unsigned long long bits;  // total payload bits of a length-only pass
-  double sumsq;             // sum of squares of a calibration input
+  uint32_t absmax;          // bit pattern of the largest |x| of a calibration input
+  uint32_t reserved1;
   uint32_t pad[56];
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");

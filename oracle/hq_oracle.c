@@ -1139,20 +1139,30 @@ int orc_calibrate_r(int lat, uint64_t seed, float bps, int rot, const void *x, i
                     uint64_t n_tiles, int dithered, uint64_t tile_base,
                     float *alpha_out, double *bps_out, int *iters_out) {
   if (lat_dim(lat) == 0 || n_tiles == 0 || !(bps > 0.0f)) return ORC_ERR_ARG;
-  double ss = 0.0;
+  /* The bracket starts from exact integers only -- the binary exponent of
+   * max |x|, ceil(log2 N) and floor(bps) -- so that any implementation that
+   * evaluates the rate exactly takes the same bisection path (a start from
+   * the RMS would depend on how its sum of squares was rounded).  With
+   * sigma = RMS(x) in [max/sqrt N, max] and the high-resolution estimate
+   * alpha ~ sqrt(2 pi e) sigma / (nu 2^R), nu in [1, 2], the estimate lies in
+   * [2^(eA - R - eN/2 + 1.05), 2^(eA - R + 3.05)]: the bracket below holds
+   * it with 4 octaves to spare at the bottom and about one at the top, and
+   * widens by 4 octaves at a time while it does not hold the target. */
+  float amax = 0.0f;
   uint64_t n = n_tiles * (uint64_t)N;
   for (uint64_t i = 0; i < n; ++i) {
-    double v = (double)load_elem(x, dtype, i);
+    float v = fabsf(load_elem(x, dtype, i));
     if (!isfinite(v)) return ORC_ERR_NONFINITE;
-    ss += v * v;
+    if (v > amax) amax = v;
   }
-  double sigma = sqrt(ss / (double)n);
-  if (!(sigma > 0.0)) return ORC_ERR_ARG;
-  static const double nu[4] = {1.0, 1.8612097182041991 /* sqrt(2 sqrt3) */,
-                               1.1892071150027210 /* 2^(1/4) */, 2.0};
-  double a0 = sqrt(2.0 * M_PI * M_E) * sigma / (nu[lat] * pow(2.0, (double)bps));
+  if (!(amax > 0.0f)) return ORC_ERR_ARG;
+  int eA1;
+  frexp((double)amax, &eA1); /* amax = f 2^eA1, f in [0.5, 1): floor(log2 amax) = eA1 - 1 */
+  int eN = 0;                /* ceil(log2 n) */
+  while ((1ull << eN) < n) ++eN;
+  const double eA = (double)(eA1 - 1), Rf = floor((double)bps);
   double target = (double)bps;
-  double lo = floor(log2(a0)) - 4.0, hi = floor(log2(a0)) + 4.0;
+  double lo = eA - Rf - 4.0 - (double)((eN + 1) / 2), hi = eA - Rf + 4.0;
   int st, iters = 0;
   float best_a = 0.0f;
   double best_r = 0.0, best_err = INFINITY;

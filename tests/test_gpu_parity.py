@@ -337,6 +337,47 @@ def test_calibrate_matches_oracle(hq, orc, lat, bps, dithered):
     assert abs(r - bps) <= 0.002
 
 
+def _near_integer_alpha0_input(rng, lat, bps, n_tiles):
+    """fp32 input whose high-resolution start log2(sqrt(2 pi e) sigma /
+    (nu 2^R)) lies within about 1e-9 of an integer (a start taken from the
+    RMS would then depend on how its sum of squares was rounded)."""
+    import math
+    nu = {0: 1.0, 1: math.sqrt(2 * math.sqrt(3.0)), 2: 2 ** 0.25, 3: 2.0}[lat]
+    x = rng.standard_normal(n_tiles * 128) * 0.02
+    for _ in range(4):
+        xf = x.astype(np.float32)
+        sigma = math.sqrt(math.fsum(float(v) * float(v) for v in xf.astype(np.float64)) / xf.size)
+        l2 = math.log2(math.sqrt(2 * math.pi * math.e) * sigma / (nu * 2.0 ** bps))
+        x = xf.astype(np.float64) * 2.0 ** (round(l2) - l2)
+    return x.astype(np.float32), l2
+
+
+@pytest.mark.parametrize("case", ["max_power_of_two", "max_below_power_of_two", "alpha0_near_integer"])
+def test_calibrate_matches_oracle_at_boundaries(hq, orc, case):
+    """The calibration starts from exact integers (the binary exponent of
+    max |x|, ceil(log2 N), floor(bps)), so the GPU and the oracle take the
+    same bisection path even where max |x| sits on a power of two or where
+    the RMS-based estimate sits on an integer octave."""
+    rng = np.random.default_rng(55)
+    lat, bps = 3, 4.0
+    if case == "alpha0_near_integer":
+        x, l2 = _near_integer_alpha0_input(rng, lat, bps, 512)
+        assert abs(l2 - round(l2)) < 1e-8
+    else:
+        x = (rng.standard_normal(512 * 128) * 0.02).astype(np.float32)
+        top = np.float32(0.125)  # above every other |x| of N(0, 0.02^2) at this size
+        x[777] = top if case == "max_power_of_two" else np.nextafter(top, np.float32(0))
+        assert np.max(np.abs(x)) == x[777]
+    plan = hq.Plan(lat, bps, SEED)
+    xd = torch.from_numpy(x).cuda()
+    ws = plan.workspace(512)
+    a, r = plan.calibrate(xd, ws)
+    st, oa, orate, _ = orc.calibrate(lat, SEED, bps, x)
+    assert st == 0
+    assert (a, r) == (oa, orate)
+    assert abs(r - bps) <= 0.002
+
+
 def test_error_statuses(hq, orc):
     plan = hq.Plan(3, 4.0, SEED).set_alpha(0.003)
     x = (torch.randn(40, 128) * 0.02).cuda()
