@@ -707,11 +707,10 @@ __device__ __forceinline__ uint32_t unary_starts_general(const uint32_t* s, uint
 // bit base, length Lb, Rice parameter k) and return the dequantised
 // real-space lattice coordinates.  Returns false when the record is corrupt
 // (the verdict is uniform over the 16 lanes of the tile).  ust: 16 words of
-// LDS per tile; tb: 16 bytes of LDS per tile.
+// LDS per tile.
 template <int L>
 __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uint32_t Lb, uint32_t k, int v, int r,
-                                           int lane, uint32_t* ust, uint8_t* tb, float p[8],
-                                           const uint8_t* sel_lut = nullptr) {
+                                           int lane, uint32_t* ust, float p[8], const uint8_t* sel_lut = nullptr) {
   constexpr uint32_t RAW = Lat<L>::raw;
   uint32_t raw = 0;
   if constexpr (RAW > 0) {
@@ -740,49 +739,54 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uin
     }
   }
   // unary section [ustart, uend): 128 ones; lane v's 8 codes start after the
-  // (8v)-th one
+  // (8v)-th one.  The record parses only if the section holds 128 ones and
+  // the last one is its last bit.
   const uint32_t ustart = base + RAW + 128u * k, uend = base + Lb;
   const uint32_t wA = ustart >> 5, nW = ((uend - 1u) >> 5) - wA + 1u;
+  const uint32_t lastbit = (s[(uend - 1u) >> 5] >> ((uend - 1u) & 31)) & 1u;
   uint32_t start;
-  bool ok = true;
+  bool ok = lastbit != 0;
   if (nW <= 16) {
-    // one word per lane: inclusive one-counts I_r, kept as bytes in LDS
+    // one word per lane: the ones of ranks [E, I) lie in word r
     uint32_t word = (uint32_t)r < nW ? s[wA + r] : 0u;
     if (r == 0) word &= ~0u << (ustart & 31);
     if ((uint32_t)r == nW - 1 && (uend & 31)) word &= (1u << (uend & 31)) - 1u;
-    const uint32_t I = row_scan_u32(__builtin_popcount(word));
-    if (r == 15) ok = I == 128u;
-    tb[r] = (uint8_t)(I < 127u ? I : 127u);
+    const uint32_t c = __builtin_popcount(word);
+    const uint32_t I = row_scan_u32(c);
+    if (r == 15) ok &= I == 128u;
+    if (((__ballot(!ok) >> (lane & ~15)) & 0xFFFFull) != 0) return false;
+    // Word r holds the first one of vector u's codes minus one, the one of
+    // rank 8u - 1, for u in [vlo, vhi] (at most 4 of them, u = 1..15): it
+    // records itself and its E for those u (the rest of the writes go to the
+    // unused entry 0).  With 128 ones every entry 1..15 is written once.
+    const uint32_t E = I - c;
+    const uint32_t vlo = (E + 8u) >> 3, vhi = min(I >> 3, 15u);
+    const uint32_t ent = (uint32_t)r | (E << 8);
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) {
+      const uint32_t u = vlo + j;
+      ust[u <= vhi ? u : 0u] = ent;
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint4 T = *reinterpret_cast<const uint4*>(tb);
     start = ustart;
     if (v > 0) {
-      // word holding rank R = 8v-1: the number of words with I_w <= R, by a
-      // packed-byte compare (byte 0x80 + R - I_w keeps bit 7 iff I_w <= R;
-      // 7 <= R <= 119 and I_w <= 127, so no byte borrows)
-      const uint32_t R = 8u * (uint32_t)v - 1u;
-      const uint32_t key = (R * 0x01010101u) | 0x80808080u;
-      const uint32_t wsel = __builtin_popcount((key - T.x) & 0x80808080u) + __builtin_popcount((key - T.y) & 0x80808080u) +
-                            __builtin_popcount((key - T.z) & 0x80808080u) + __builtin_popcount((key - T.w) & 0x80808080u);
-      const uint32_t q4 = wsel == 0 ? 0u : wsel - 1u;  // byte index of I_(w-1)
-      const uint32_t Td = q4 < 4 ? T.x : q4 < 8 ? T.y : q4 < 12 ? T.z : T.w;
-      const uint32_t Iprev = wsel == 0 ? 0u : __builtin_amdgcn_ubfe(Td, 8 * (q4 & 3), 8);
-      uint32_t wd = s[wA + min(wsel, 15u)];
-      if (wsel == 0) wd &= ~0u << (ustart & 31);
-      start = (wA + wsel) * 32u + (sel_lut ? select_bit_lut(wd, R - Iprev, sel_lut) : select_bit(wd, R - Iprev)) + 1u;
+      const uint32_t e = ust[v];
+      const uint32_t wr = e & 15u;
+      uint32_t wd = s[wA + wr];
+      if (wr == 0) wd &= ~0u << (ustart & 31);
+      const uint32_t j = 8u * (uint32_t)v - 1u - (e >> 8);  // rank of the one within the word
+      start = (wA + wr) * 32u + (sel_lut ? select_bit_lut(wd, j, sel_lut) : select_bit(wd, j)) + 1u;
     }
   } else {
-    ok = unary_starts_general(s, ustart, uend, r, ust) == 128u;
+    ok &= unary_starts_general(s, ustart, uend, r, ust) == 128u;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (((__ballot(!ok) >> (lane & ~15)) & 0xFFFFull) != 0) return false;
     start = v == 0 ? ustart : ust[v];
   }
-  const uint32_t lastbit = (s[(uend - 1u) >> 5] >> ((uend - 1u) & 31)) & 1u;
-  ok &= lastbit != 0;
-  if (((__ballot(!ok) >> (lane & ~15)) & 0xFFFFull) != 0) return false;
   // the lane's 8 unary codes: q zeros then a one, from start
   uint32_t m[8];
   const uint32_t qlim = kMLimit >> k;
@@ -829,50 +833,68 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uin
 }
 
 // Stream words [w_first, w_end) of a chunk into LDS from the 16-byte
-// boundary below its first record (s_stage[i] = word w_first + i), in uint4
-// loads all issued before the LDS stores; the words from w_end on read as
-// zero.  Every thread of the work-group calls it, after s_off[0..nt] is
+// boundary below its first record (s_stage[i] = word w_first + i), in whole
+// uint4 loads, all issued before the LDS stores.  The words after w_end in
+// the last group are what the buffer holds there (the next records' bits):
+// a record never reads past its own end, and the checks that decide whether
+// a record parses mask them off.  A group that would leave the buffer (only
+// at the stream's end) is read word by word.  One zero group follows the
+// span.  Every thread of the work-group calls it, after s_off[0..nt] is
 // visible; returns whether the span is sane (work-group uniform).
 template <bool NT = false>  // NT: the stream is read once per launch (a plain decode)
 __device__ __forceinline__ bool stage_chunk(const uint32_t* words, uint64_t n_words, const uint64_t* s_off,
                                             uint32_t nt, uint32_t* s_stage, uint64_t& w_first, int tid) {
-  w_first = (s_off[0] >> 5) & ~3ull;
-  const uint64_t w_end = (s_off[nt] + 31) >> 5;
-  const bool span_ok = s_off[nt] >= s_off[0] && (w_end - w_first) <= (uint64_t)kStageWords - 8 && w_end <= n_words;
+  const uint64_t o_first = s_off[0], o_end = s_off[nt];
+  w_first = (o_first >> 5) & ~3ull;
+  const uint64_t w_end = (o_end + 31) >> 5;
+  const bool span_ok = o_end >= o_first && (w_end - w_first) <= (uint64_t)kStageWords - 8 && w_end <= n_words;
   if (span_ok) {
-    const uint32_t n = (uint32_t)(w_end - w_first);
-    const uint32_t n4 = (n + 3) >> 2;
+    const uint32_t n4 = (uint32_t)((w_end - w_first + 3) >> 2);
+    const uint64_t full4 = (n_words - w_first) >> 2;  // groups wholly inside the buffer
+    const uint32_t* src = words + w_first;
+    uint4* dst = reinterpret_cast<uint4*>(s_stage);
     uint4 q[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const uint32_t i4 = (uint32_t)tid + 256u * j;
       q[j] = make_uint4(0u, 0u, 0u, 0u);
       if (i4 < n4) {
-        const uint64_t wg = w_first + 4ull * i4;
-        if (wg + 4 <= n_words) {
-          q[j] = load16<NT>(words + wg);
-        } else {
-          q[j].x = words[wg];
-          if (4 * i4 + 1 < n) q[j].y = words[wg + 1];
-          if (4 * i4 + 2 < n) q[j].z = words[wg + 2];
+        if ((uint64_t)i4 < full4) {
+          q[j] = load16<NT>(src + 4u * i4);
+        } else {  // the buffer ends inside this group: its words below n_words
+          const uint64_t left = n_words - w_first - 4ull * i4;  // 1..3
+          q[j].x = src[4u * i4];
+          if (left > 1) q[j].y = src[4u * i4 + 1];
+          if (left > 2) q[j].z = src[4u * i4 + 2];
         }
       }
     }
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const uint32_t i4 = (uint32_t)tid + 256u * j;
-      if (i4 <= n4) {  // one zero uint4 after the last
-        uint4 v4 = q[j];
-        const uint32_t i = 4 * i4;
-        if (i + 0 >= n) v4.x = 0u;
-        if (i + 1 >= n) v4.y = 0u;
-        if (i + 2 >= n) v4.z = 0u;
-        if (i + 3 >= n) v4.w = 0u;
-        reinterpret_cast<uint4*>(s_stage)[i4] = v4;
-      }
+      if (i4 < n4) dst[i4] = q[j];
     }
+    if (tid == 0) dst[n4] = make_uint4(0u, 0u, 0u, 0u);
   }
   return span_ok;
+}
+
+// Per tile of a chunk, what a lane needs to parse its record, from one thread
+// per tile after the offsets and Rice parameters are in LDS: the record's
+// bit in the staged span, its length, k, and whether it is sane (k <= 22,
+// length between the shortest and the longest possible record, span staged).
+template <int L>
+__device__ __forceinline__ void tile_records(const uint64_t* s_off, const uint32_t* s_k, uint32_t nt, uint64_t w_first,
+                                             bool span_ok, uint4* s_rec, int tid) {
+  constexpr uint32_t RAW = Lat<L>::raw;
+  constexpr uint32_t MAXREC = RAW + 128u * 23u;
+  if (tid < (int)nt) {
+    const uint64_t o0 = s_off[tid], o1 = s_off[tid + 1];
+    const uint32_t k = s_k[tid];
+    const uint64_t Lr = o1 - o0;  // wraps past MAXREC when o1 < o0
+    const bool ok = span_ok && k <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + k) && Lr <= MAXREC;
+    s_rec[tid] = make_uint4((uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, ok ? 1u : 0u);
+  }
 }
 
 template <int L, bool DITHER, int OUT>
@@ -883,7 +905,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
   __shared__ uint64_t s_off[kChunkTiles + 1];
   __shared__ uint32_t s_k[kChunkTiles];
   __shared__ uint32_t s_ust[16][16];
-  __shared__ uint4 s_tb[16];  // per tile of a pass: 16 one-count bytes
+  __shared__ uint4 s_rec[kChunkTiles];  // per tile: record bit, length, k, sane
   __shared__ float s_q[OUT == kOutScores ? 16 : 1][kTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
@@ -933,6 +955,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
   uint64_t w_first;
   const bool span_ok =
       stage_chunk<OUT == kOutF32 || OUT == kOutBf16 || OUT == kOutRot>(a.words, a.n_words, s_off, nt, s_stage, w_first, tid);
+  tile_records<L>(s_off, s_k, nt, w_first, span_ok, s_rec, tid);
   __syncthreads();
 
   // output scale: the lane sign and c_dec, then the signs of D (bf16: on the
@@ -961,13 +984,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOut
     }
     bool good = false;
     if (valid) {
-      const uint64_t o0 = s_off[slot], o1 = s_off[slot + 1];
-      const uint32_t k = s_k[slot];
-      const uint64_t Lr = o1 - o0;  // wraps past MAXREC when o1 < o0
-      const bool ok = span_ok && k <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + k) && Lr <= MAXREC;
-      if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, s_ust[pslot],
-                                       reinterpret_cast<uint8_t*>(&s_tb[pslot]), pv,
-                                       kLut ? reinterpret_cast<const uint8_t*>(s_sel) : nullptr);
+      const uint4 rec = s_rec[slot];
+      if (rec.w) good = parse_lane<L>(s_stage, rec.x, rec.y, rec.z, v, r, lane, s_ust[pslot], pv,
+                                          kLut ? reinterpret_cast<const uint8_t*>(s_sel) : nullptr);
       if (!good && r == 0) set_status(a.ws, 5);
       if constexpr (DITHER) {
         if (!good) {
@@ -1228,7 +1247,7 @@ template <int L>
 __device__ __forceinline__ void attn_parse(const uint32_t* s_stage, const uint64_t* s_off, const uint32_t* s_k,
                                            uint64_t w_first, bool span_ok, bool valid, int slot, uint64_t tile_id,
                                            uint32_t key0, uint32_t key1, int v, int r, int lane, uint32_t* ust,
-                                           uint8_t* tb, WsHeader* ws, float pv[8], const uint8_t* sel_lut) {
+                                           WsHeader* ws, float pv[8], const uint8_t* sel_lut) {
   constexpr uint32_t RAW = Lat<L>::raw;
   constexpr uint32_t MAXREC = RAW + 128u * 23u;
 #pragma unroll
@@ -1239,7 +1258,7 @@ __device__ __forceinline__ void attn_parse(const uint32_t* s_stage, const uint64
   const uint64_t Lr = o1 - o0;
   const bool ok = span_ok && k <= (uint32_t)kKMax && Lr >= RAW + 128u * (1u + k) && Lr <= MAXREC;
   bool good = false;
-  if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, ust, tb, pv, sel_lut);
+  if (ok) good = parse_lane<L>(s_stage, (uint32_t)(o0 - 32 * w_first), (uint32_t)Lr, k, v, r, lane, ust, pv, sel_lut);
   if (!good) {
     if (r == 0) set_status(ws, 5);
 #pragma unroll
@@ -1269,7 +1288,6 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   __shared__ uint64_t s_off[kChunkTiles + 1];
   __shared__ uint32_t s_k[kChunkTiles];
   __shared__ uint32_t s_ust[16][16];
-  __shared__ uint4 s_tb[16];
   __shared__ __align__(16) float s_qv[16][kTile];  // rotated queries (phase 1), a pass's values (phase 2)
   __shared__ float4 s_w[kKeys];                    // per key: the queries' scores, then weights
   __shared__ float s_ml[2][4][kAttnQ];            // per wave: maximum, then sum
@@ -1333,7 +1351,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
       const bool valid = slot < (int)nt;
       float pv[8];
       attn_parse<L>(s_stage, s_off, s_k, w_first, span_ok, valid, slot, a.ktb + t_first + slot, a.key0, a.key1, v, r,
-                    lane, s_ust[pslot], reinterpret_cast<uint8_t*>(&s_tb[pslot]), a.ws, pv,
+                    lane, s_ust[pslot], a.ws, pv,
                     reinterpret_cast<const uint8_t*>(s_sel));
 #pragma unroll
       for (int g = 0; g < (int)kAttnQ; ++g) {
@@ -1393,7 +1411,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
       const bool valid = slot < (int)nt;
       float pv[8];
       attn_parse<L>(s_stage, s_off, s_k, w_first, span_ok, valid, slot, a.vtb + t_first + slot, a.key0, a.key1, v, r,
-                    lane, s_ust[pslot], reinterpret_cast<uint8_t*>(&s_tb[pslot]), a.ws, pv,
+                    lane, s_ust[pslot], a.ws, pv,
                     reinterpret_cast<const uint8_t*>(s_sel));
       float4* vr = reinterpret_cast<float4*>(&s_v[pslot][8 * v]);  // zeros past the last key
       vr[0] = make_float4(pv[0], pv[1], pv[2], pv[3]);
@@ -1656,7 +1674,6 @@ __global__ __launch_bounds__(256) void gemm_k(GemmArgs g) {
   constexpr int kBS = kTile + 8;  // B row stride (bf16): conflict-free 16-byte reads
   __shared__ __align__(16) uint32_t s_rec[16][kGemmRecWords];
   __shared__ uint32_t s_ust[16][16];
-  __shared__ uint4 s_tb[16];
   __shared__ uint64_t s_o[33];
   __shared__ uint64_t s_o1[32];
   __shared__ uint32_t s_k[32];
@@ -1724,7 +1741,7 @@ __global__ __launch_bounds__(256) void gemm_k(GemmArgs g) {
       for (int e = 0; e < 8; ++e) pv[e] = 0.0f;
       bool good = false;
       if (ok) good = parse_lane<L>(sr, (uint32_t)(o0 & 31u), (uint32_t)Lr, kk, v, r, lane, s_ust[pslot],
-                                   reinterpret_cast<uint8_t*>(&s_tb[pslot]), pv, reinterpret_cast<const uint8_t*>(s_sel));
+                                   pv, reinterpret_cast<const uint8_t*>(s_sel));
       if (valid && !good) {
         if (r == 0) set_status(g.ws, 5);
 #pragma unroll
