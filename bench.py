@@ -43,23 +43,74 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(x_host_bits, alpha, seed, reps):
-    """The oracle (single-threaded C) on the same tensor: encode + decode."""
-    import numpy as np  # noqa: F401
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x_host_bits, alpha, seed, reps, c1_bits, c1_alpha):
+    """The oracle on the host cores, same input bytes as the GPU: encode +
+    decode of the whole 4096 x 4096 bf16 tensor, once on one thread and once
+    on all cores (its OpenMP passes: per-tile steps in parallel, serial
+    length scan).  Also the fp32 4096 x 128 case end to end (encode, decode,
+    round-trip check) in seconds, single-threaded."""
+    import hashlib
+
+    import numpy as np
     from oracle import oracle as O
     O.lib()
     n_bytes = x_host_bits.size * 2
-    t_total = 0.0
-    for _ in range(reps):
+    legs = {}
+    n_all = max(1, min(int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1),
+                       os.cpu_count() or 1))
+    for nt, r in ((1, reps), (n_all, 4 * reps)):
+        with O.threads(nt):
+            t_total = 0.0
+            for _ in range(r):
+                t0 = time.perf_counter()
+                st, w, off, k = O.encode(O.E8, seed, alpha, x_host_bits)
+                st2, y = O.decode(O.E8, seed, alpha, w, off, k, out_dtype=O.BF16)
+                t_total += time.perf_counter() - t0
+                assert st == 0 and st2 == 0
+        legs[nt] = (round(2.0 * n_bytes * r / t_total / 1e9, 4), r, t_total)
+    # the small fp32 case: encode, decode and the round-trip check, one thread
+    with O.threads(1):
         t0 = time.perf_counter()
-        st, w, off, k = O.encode(O.E8, seed, alpha, x_host_bits)
-        st2, y = O.decode(O.E8, seed, alpha, w, off, k, out_dtype=O.BF16)
-        t_total += time.perf_counter() - t0
+        st, w, off, k = O.encode(O.E8, seed, c1_alpha, c1_bits)
+        st2, y = O.decode(O.E8, seed, c1_alpha, w, off, k)
+        err = float(np.max(np.abs(y.reshape(-1) - c1_bits.reshape(-1))))
+        c1_s = time.perf_counter() - t0
         assert st == 0 and st2 == 0
-    return {"value": round(2.0 * n_bytes * reps / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"whole 4096x4096 bf16 tensor, encode+decode, {reps} repetitions, "
-                      f"{t_total:.1f} s single-threaded"}
+    v_all, r_all, t_all = legs[n_all]
+    v_one, r_one, t_one = legs[1]
+    return {"value": v_all, "unit": "GB/s", "cores": n_all, "kind": "oracle",
+            "sample": f"whole 4096x4096 bf16 tensor, encode+decode, {r_all} repetitions in {t_all:.2f} s on "
+                      f"{n_all} threads (OpenMP over tiles, serial length scan)",
+            "single_thread": {"value": v_one, "unit": "GB/s", "cores": 1,
+                              "sample": f"same tensor, {r_one} repetitions in {t_one:.1f} s"},
+            "fp32_4096x128_oracle_seconds": round(c1_s, 4),
+            "fp32_4096x128_max_roundtrip_error": err,
+            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
+            "input_sha256": hashlib.sha256(x_host_bits.tobytes()).hexdigest()}
+
+
+def copy_ceiling(torch, dev, nbytes=1 << 30, iters=20):
+    """Measured HBM ceiling: device-to-device copy of 1 GiB (hipMemcpyAsync
+    through torch), median over iters, read + write bytes per second."""
+    a = torch.empty(nbytes // 8, dtype=torch.int64, device=dev)
+    b = torch.ones(nbytes // 8, dtype=torch.int64, device=dev)
+    ms = _time(torch, lambda: a.copy_(b), iters)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"GBps": round(2.0 * nbytes / (ms * 1e-3) / 1e9, 1), "bytes_moved": 2 * nbytes, "ms": round(ms, 4),
+            "method": "torch copy_ (hipMemcpyAsync device to device) of 1 GiB, median of 20, read + write bytes"}
 
 
 def _time(torch, fn, iters):
@@ -373,6 +424,8 @@ def main():
     dec_ms = op_ms(g_dec)
     hq.check(ws)
 
+    ceiling = copy_ceiling(torch, dev)
+
     total_bits = encs[0].total_bits()
     payload_bytes = total_bits / 8.0
     side_bytes = 8.0 * (n_tiles + 1) + n_tiles
@@ -420,14 +473,19 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (traffic_for(dominant) or {}).get("total_bytes"),
             "algorithmic_bytes_per_launch": int(alg_bytes),
+            "measured_copy_GBps": ceiling["GBps"],
+            "frac_of_measured_copy": round(achieved / ceiling["GBps"], 4),
         },
+        "hbm_copy_ceiling": ceiling,
         "valu": {"encode": valu_for("encode", enc_ms), "decode": valu_for("decode", dec_ms)},
     }
     if not args.no_rows:
         line["rows"] = workload_rows(hq, W, torch, np, args.row_iters)
     if not args.no_cpu_baseline:
         xb = x0.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
-        line["cpu_baseline"] = cpu_baseline(xb, alpha, seed, args.cpu_reps)
+        c1 = W.c1("cpu").numpy().reshape(-1)
+        c1_alpha = float(np.float32(np.sqrt(2 * np.pi * np.e) * W.c1_sigma_eff() / 32.0))
+        line["cpu_baseline"] = cpu_baseline(xb, alpha, seed, args.cpu_reps, c1, c1_alpha)
     print(json.dumps(line), flush=True)
 
 

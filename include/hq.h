@@ -60,8 +60,11 @@
 extern "C" {
 #endif
 
-typedef enum { HQ_Z = 0, HQ_A2 = 1, HQ_D4 = 2, HQ_E8 = 3 } hq_lattice;
-typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
+/* (The last enumerator of each enum only gives the type the range of a 32-bit
+ * int, so that an out-of-range value a caller passes is a checked argument
+ * error, not undefined behaviour in the library.) */
+typedef enum { HQ_Z = 0, HQ_A2 = 1, HQ_D4 = 2, HQ_E8 = 3, HQ_LATTICE_INT_RANGE_ = 0x7FFFFFFF } hq_lattice;
+typedef enum { HQ_F32 = 0, HQ_BF16 = 1, HQ_DTYPE_INT_RANGE_ = 0x7FFFFFFF } hq_dtype;
 typedef enum {
   HQ_OK = 0,
   HQ_ERR_ARG = 1,        /* bad argument (null pointer, tile != 128, size) */
@@ -70,7 +73,8 @@ typedef enum {
   HQ_ERR_CAPACITY = 4,   /* the stream does not fit cap_words */
   HQ_ERR_CORRUPT = 5,    /* a record does not parse (decode) */
   HQ_ERR_DEVICE = 6,     /* a HIP runtime call failed */
-  HQ_ERR_NOALPHA = 7     /* the plan has no alpha yet */
+  HQ_ERR_NOALPHA = 7,    /* the plan has no alpha yet */
+  HQ_STATUS_INT_RANGE_ = 0x7FFFFFFF
 } hq_status;
 
 typedef struct hq_plan_s* hq_plan_t;

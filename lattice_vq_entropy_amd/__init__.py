@@ -14,7 +14,8 @@ import re
 import torch  # noqa: F401  (loads the HIP runtime libhq links against)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libhq.so")
+# HQ_SANITIZE=1 loads the host-sanitized build (build.py --sanitize)
+LIB_PATH = os.path.join(HERE, "libhq_san.so" if os.environ.get("HQ_SANITIZE") == "1" else "libhq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "hq.h")
 
 Z, A2, D4, E8 = 0, 1, 2, 3

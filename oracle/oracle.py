@@ -18,7 +18,13 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "hq_oracle.c")
-LIB = os.path.join(HERE, "liboracle.so")
+# ORC_SANITIZE=1: a separate AddressSanitizer + UndefinedBehaviorSanitizer
+# build (load it with gcc's libasan preloaded, e.g.
+#   ORC_SANITIZE=1 LD_PRELOAD=$(gcc -print-file-name=libasan.so) \
+#   ASAN_OPTIONS=detect_leaks=0 python -m pytest tests -m "not gpu" -k oracle)
+SANITIZE = os.environ.get("ORC_SANITIZE") == "1"
+LIB = os.path.join(HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 Z, A2, D4, E8 = 0, 1, 2, 3
 F32, BF16 = 0, 1
@@ -39,7 +45,7 @@ def build(force: bool = False) -> str:
     """Compile liboracle.so next to its source (gcc)."""
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp"
-        subprocess.run(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"], check=True)
+        subprocess.run(["gcc", *CFLAGS, *(SAN_FLAGS if SANITIZE else []), "-o", tmp, SRC, "-lm"], check=True)
         os.replace(tmp, LIB)
     return LIB
 
