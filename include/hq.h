@@ -29,8 +29,9 @@
  *     When several data errors occur, the lowest code is reported.
  *   - Workspace: a device buffer of hq_workspace_bytes() bytes (about 12 KB
  *     per 32 tiles: it holds each chunk's staged bits between the launches of
- *     one encode), 16-byte aligned, zero-filled by the caller once before its
- *     first use.  One workspace must not be used by two calls that can run
+ *     one encode; about 3.5 KB at 4 bits per scalar for a plan with a compact
+ *     workspace, hq_plan_set_compact_workspace), 16-byte aligned, zero-filled
+ *     by the caller once before its first use.  One workspace must not be used by two calls that can run
  *     concurrently (e.g. on two streams).
  *   - No call waits on another work-group's progress; encode is two
  *     stream-ordered launches (pack per chunk, then placement, which sums the
@@ -118,6 +119,18 @@ void hq_plan_destroy(hq_plan_t plan);
 
 /* Workspace bytes for calls on up to n_tiles tiles. */
 size_t hq_workspace_bytes(hq_plan_t plan, uint64_t n_tiles);
+
+/* Staging slots of the plan's encodes (hq_workspace_bytes follows the mode:
+ * set it before sizing a workspace; 0 or 1, else HQ_ERR_ARG).  0, the
+ * default: each chunk of 32 tiles is staged in a slot that holds its longest
+ * possible record bits, 11.9 KB per chunk (1.45x the bytes of its bf16
+ * input).  1, compact: slots of 128 (bps + 2.5) + 8 words in whole uint4,
+ * bps being the plan's rate (the workspace then takes 3.5 KB per chunk at
+ * 4 bps, 0.43x the bf16 input); a chunk whose bits do not fit its slot is encoded again by the
+ * placement launch, from its input, straight into the stream, so the result
+ * is the same whatever the data.  The placement of a compact plan carries
+ * that path and runs about 10 % slower on the measured weights. */
+hq_status hq_plan_set_compact_workspace(hq_plan_t plan, int on);
 
 /* Words that always suffice for the stream of n_tiles tiles (the longest
  * record is 16 + 128*23 bits for E8, 128*23 otherwise). */

@@ -40,6 +40,7 @@ _SIGNATURES = {
     "hq_plan_get": (_i, [_p, C.POINTER(_f), C.POINTER(_f), C.POINTER(_f)]),
     "hq_plan_destroy": (None, [_p]),
     "hq_workspace_bytes": (C.c_size_t, [_p, _u64]),
+    "hq_plan_set_compact_workspace": (_i, [_p, _i]),
     "hq_encode_bound_words": (_u64, [_p, _u64]),
     "hq_calibrate": (_i, [_p, _p, _i, _u64, _i, _u64, _p, _p, C.POINTER(_f), C.POINTER(C.c_double)]),
     "hq_encode": (_i, [_p, _p, _i, _u64, _p, _u64, _p, _p, _p, _p]),
@@ -211,6 +212,12 @@ class Plan:
         _check(lib().hq_plan_get_rotation(self._h, C.byref(kind), q.ctypes.data_as(C.c_void_p)),
                "hq_plan_get_rotation")
         return kind.value, q.reshape(TILE, TILE)
+
+    def set_compact_workspace(self, on: bool = True):
+        """hq_plan_set_compact_workspace: staging slots sized from the plan's rate
+        (a chunk that does not fit is encoded again by the placement)."""
+        _check(lib().hq_plan_set_compact_workspace(self._h, int(bool(on))), "hq_plan_set_compact_workspace")
+        return self
 
     def set_alpha(self, alpha: float):
         _check(lib().hq_plan_set_alpha(self._h, float(alpha)), "hq_plan_set_alpha")

@@ -22,6 +22,7 @@ struct hq_plan_s {
   uint32_t sgn[4];              // bit c: coordinate c of D is -1
   uint32_t sl16[4], sl32[4];    // the same in the kernels' lane layouts
   int rot;                      // 0: the RHT; 1: the Haar matrix
+  bool compact;                 // staging slots sized from bps (hq_plan_set_compact_workspace)
   float* q;                     // Haar: Q (128 x 128 fp32, row-major, host), owned by the plan
   float* dq;                    // Haar: device copy (caller's memory): Q^T, then Q
 };
@@ -110,7 +111,16 @@ void haar_host(uint64_t seed, float* q32) {
 }
 
 // Workspace: the rotated tiles (fp32) of a Haar plan follow the codec regions.
-uint64_t rot_buffer_offset(uint64_t n_tiles) { return hq::ws_align(hq::ws_bytes(n_tiles)); }
+// Staging slot words of the plan's encodes: full-size, or with a compact
+// workspace sized from the plan's rate (hq_ws.h, slot_words_for).
+uint32_t plan_slot_words(const hq_plan_s* p) {
+  return p->compact ? hq::slot_words_for(p->bps) : (uint32_t)hq::kSlotWords;
+}
+
+// Haar plans: the rotated tiles (or queries) follow the codec's regions.
+uint64_t rot_buffer_offset(const hq_plan_s* p, uint64_t n_tiles) {
+  return hq::ws_align(hq::ws_bytes(n_tiles, plan_slot_words(p)));
+}
 
 // The signs of D (bit c of the 128: coordinate c is -1) in the two layouts the
 // kernels read.  The lane holding vector v (coordinates 8v..8v+7) takes word
@@ -142,7 +152,7 @@ void fill_common(const hq_plan_s* p, uint32_t sl16[4], uint32_t sl32[4], uint32_
 hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, bool dither,
                       uint64_t tile_base, uint32_t* words, uint64_t cap_words, uint64_t* offsets, uint8_t* k,
                       void* ws, void* stream, bool len_only, bool append = false, bool rotated = false,
-                      hq::WsHeader* status = nullptr) {
+                      hq::WsHeader* status = nullptr, bool noalloc_slots = false) {
   if (!plan) return HQ_ERR_ARG;
   if (!plan->has_alpha) return HQ_ERR_NOALPHA;
   if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_ERR_ARG;
@@ -171,18 +181,20 @@ hq_status encode_impl(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_
   a.c_enc = plan->c_enc;
   a.tile_base = tile_base;
   a.ws = status ? status : (hq::WsHeader*)ws;
-  const hq::WsLayout lay = hq::ws_layout(n_tiles);
+  const uint32_t slot = noalloc_slots ? (uint32_t)hq::kSlotWords : plan_slot_words(plan);
+  const hq::WsLayout lay = hq::ws_layout(n_tiles, slot);
   a.n_chunks = (uint32_t)hq::ws_chunks(n_tiles);
   a.agg = (uint32_t*)((char*)ws + lay.agg);
   a.E = (uint64_t*)((char*)ws + lay.E);
   a.loc = (uint32_t*)((char*)ws + lay.loc);
   a.tailw = (uint32_t*)((char*)ws + lay.tailw);
   a.stage = (uint32_t*)((char*)ws + lay.stage);
+  a.slot_words = slot;
   a.partials = (unsigned long long*)a.E;
   a.base = append ? offsets : nullptr;
   int in = dtype == HQ_BF16 ? 1 : 0;
   if (plan->rot == 1) {  // the dense rotation first (skipped when the caller has it in the workspace)
-    float* rbuf = (float*)((char*)ws + rot_buffer_offset(n_tiles));
+    float* rbuf = (float*)((char*)ws + rot_buffer_offset(plan, n_tiles));
     if (!rotated) {
       hq::RotArgs r{};
       r.x = x;
@@ -226,7 +238,7 @@ hq_status decode_impl(hq_plan_t plan, const uint32_t* words, uint64_t n_words, c
   const dim3 grid((uint32_t)hq::ws_chunks(n_tiles));
   if (plan->rot == 1) {  // the codes in the rotated domain, then the dense inverse rotation
     if (((uintptr_t)ws & 15u) != 0) return HQ_ERR_ARG;
-    float* rbuf = (float*)((char*)ws + rot_buffer_offset(n_tiles));
+    float* rbuf = (float*)((char*)ws + rot_buffer_offset(plan, n_tiles));
     a.y = rbuf;
     if (hq::launch_decode(plan->lattice, dither, hq::kOutRot, a, grid, (hipStream_t)stream) != hipSuccess)
       return HQ_ERR_DEVICE;
@@ -380,8 +392,14 @@ void hq_plan_destroy(hq_plan_t plan) {
 }
 
 size_t hq_workspace_bytes(hq_plan_t plan, uint64_t n_tiles) {
-  if (plan && plan->rot == 1) return (size_t)(rot_buffer_offset(n_tiles) + 512ull * n_tiles);
-  return (size_t)hq::ws_bytes(n_tiles);
+  if (plan && plan->rot == 1) return (size_t)(rot_buffer_offset(plan, n_tiles) + 512ull * n_tiles);
+  return (size_t)hq::ws_bytes(n_tiles, plan ? plan_slot_words(plan) : (uint32_t)hq::kSlotWords);
+}
+
+hq_status hq_plan_set_compact_workspace(hq_plan_t plan, int on) {
+  if (!plan || (on != 0 && on != 1)) return HQ_ERR_ARG;
+  plan->compact = on == 1;
+  return HQ_OK;
 }
 
 size_t hq_rotation_bytes(void) { return 2 * 128 * 128 * sizeof(float); }
@@ -451,7 +469,7 @@ hq_status hq_encode_noalloc(hq_plan_t plan, const void* x, hq_dtype dtype, uint6
   const hq_status s = scratch_address(&ws);
   if (s != HQ_OK) return s;
   return encode_impl(plan, x, dtype, n_tiles, false, 0, words, cap_words, offsets, k, ws, stream, false, false, false,
-                     (hq::WsHeader*)status);
+                     (hq::WsHeader*)status, true);
 }
 
 hq_status hq_kv_encode(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n_tiles, uint64_t tile_base,
@@ -488,10 +506,10 @@ hq_status hq_kv_decode(hq_plan_t plan, const uint32_t* words, uint64_t n_words, 
 size_t hq_kv_scores_workspace_bytes(hq_plan_t plan, uint32_t n_heads, uint64_t tiles_per_head, uint32_t qph) {
   const uint64_t n = (uint64_t)n_heads * tiles_per_head;
   if (plan && plan->rot == 1) {  // the rotated queries follow the codec's regions
-    const uint64_t a = hq_workspace_bytes(plan, n), b = rot_buffer_offset(n) + 512ull * n_heads * qph;
+    const uint64_t a = hq_workspace_bytes(plan, n), b = rot_buffer_offset(plan, n) + 512ull * n_heads * qph;
     return (size_t)(a > b ? a : b);
   }
-  return (size_t)hq::ws_bytes(n);
+  return hq_workspace_bytes(plan, n);
 }
 
 hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words, const uint64_t* offsets,
@@ -522,7 +540,7 @@ hq_status hq_kv_scores(hq_plan_t plan, const uint32_t* words, uint64_t n_words, 
   a.qph = qph;
   a.tiles_per_head = tiles_per_head;
   if (plan->rot == 1) {  // q~ = Q q (fp32 chains, as the encoder rotates the keys) into the workspace
-    float* qr = (float*)((char*)ws + rot_buffer_offset(a.n_tiles));
+    float* qr = (float*)((char*)ws + rot_buffer_offset(plan, a.n_tiles));
     hq::RotArgs r{};
     r.x = q;
     r.in_bf16 = 0;
@@ -864,7 +882,7 @@ hq_status hq_calibrate(hq_plan_t plan, const void* x, hq_dtype dtype, uint64_t n
     hq::RotArgs r{};
     r.x = x;
     r.in_bf16 = dtype == HQ_BF16;
-    r.y = (float*)((char*)ws + rot_buffer_offset(n_tiles));
+    r.y = (float*)((char*)ws + rot_buffer_offset(plan, n_tiles));
     r.out_bf16 = 0;
     r.mt = plan->dq;
     r.scale = 1.0f;

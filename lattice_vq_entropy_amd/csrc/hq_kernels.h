@@ -28,28 +28,18 @@ struct EncArgs {
   uint64_t* E;       // chunk bit offsets, n_chunks + 1
   uint32_t* loc;     // chunk-local bit offset per tile
   uint32_t* tailw;   // last 32 stream bits of each chunk
-  uint32_t* stage;   // kSlotWords staging words per chunk
+  uint32_t* stage;   // slot_words staging words per chunk
+  uint32_t slot_words;  // a multiple of 4, at most kSlotWords
   unsigned long long* partials;  // length-only pass: bits per chunk
   const uint64_t* base;  // append: the existing stream's end bit (device), else null
   const void* x0;        // pre-rotated input (x is the rotated tiles): the original, for error kinds
   int x0_bf16;
-};
-
-struct PlaceArgs {
-  const uint32_t* stage;
-  const uint32_t* agg;  // bits per chunk (padded to 64 entries)
-  WsHeader* ws;
-  const uint32_t* loc;
-  const uint32_t* tailw;
-  uint64_t n_tiles;
-  uint32_t n_chunks;
-  uint32_t* words;
-  uint64_t cap_words;
-  uint64_t* offsets;
-  const uint64_t* base;  // append: the existing stream's end bit (device), else null
-  const uint32_t* eloc;      // above the self-scan limit: chunk offsets within blocks of 1024
-  const uint64_t* blockpre;  // and the bits of the blocks before each block
-  int block_totals;          // blockpre holds the blocks' own totals (at most 64): sum those before
+  // placement above the self-scan limit: chunk offsets within blocks of 1024,
+  // and the bits of the blocks before each block (or, at most 64 blocks, the
+  // blocks' own totals: block_totals)
+  const uint32_t* eloc;
+  const uint64_t* blockpre;
+  int block_totals;
 };
 
 struct DecArgs {

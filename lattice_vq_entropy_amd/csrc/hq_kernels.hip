@@ -294,32 +294,86 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
          __builtin_amdgcn_readlane(x, 48);
 }
 
-// Encode, step 1 of 3: one chunk of kChunkTiles tiles per work-group, chunk =
-// blockIdx.x.  Per pass of 16 tiles: front, tile lengths, offsets within the
-// chunk, packing into LDS.  Then the chunk's bits go to its staging slot, its
-// bit count to agg, and per tile the chunk-local bit offset and k.  No
-// work-group waits on another.  LEN_ONLY: the chunk's bit count only.
-template <int L, bool DITHER, int IN, bool LEN_ONLY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IN == 1 ? 8 : 1))) void encode_k(EncArgs a) {
+// One chunk's records assembled in LDS by the whole work-group (256 threads):
+// per pass of 16 tiles, front, tile lengths, offsets within the chunk,
+// packing into the zero-filled s_stage.  Per tile slot: s_lo the chunk-local
+// bit offset, s_k the Rice parameter.  Returns the chunk's bit count
+// (work-group uniform); s_stage is complete when it returns.  NT: the input is
+// read once per launch (non-temporal loads).
+template <int L, bool DITHER, int IN, bool NT>
+__device__ __forceinline__ uint32_t pack_chunk(const EncArgs& a, uint32_t chunk, uint32_t* s_stage, uint32_t* s_len,
+                                               uint32_t* s_lo, uint32_t* s_k) {
   constexpr bool BF16 = IN == 1, PRE = IN == 2;  // input: fp32, bf16, or fp32 already rotated
-  __shared__ __align__(16) uint32_t s_stage[kSlotWords];
-  __shared__ uint32_t s_len[kChunkTiles], s_lo[kChunkTiles], s_k[kChunkTiles];
-
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
   const int v = lane_vector(r);
   const int pslot = wv * 4 + grp;
   const LaneConst<BF16> lc(a, v);
-  const uint32_t chunk = blockIdx.x;
   const uint64_t t_first = (uint64_t)chunk * kChunkTiles;
-
   InVec<BF16> in[kPasses];
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const uint64_t t = t_first + p * 16 + pslot;
-    in[p] = load_in<BF16, !LEN_ONLY>(a.x, t, v, t < a.n_tiles);
+    in[p] = load_in<BF16, NT>(a.x, t, v, t < a.n_tiles);
   }
+  for (int i = tid; i < kSlotWords / 4; i += 256) reinterpret_cast<uint4*>(s_stage)[i] = make_uint4(0u, 0u, 0u, 0u);
+  // lane permute addresses: the row's lane of slot pslot, and of vector r
+  const int paddr = ((lane & ~15) | pslot) << 2, vaddr = ((lane & ~15) | v) << 2;
+  uint32_t base = 0;  // wave-uniform bit offset of the current pass
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int slot = p * 16 + pslot;
+    const uint64_t t = t_first + slot;
+    const bool valid = t < a.n_tiles;
+    TileSyms ts;
+    tile_front<L, DITHER, BF16, PRE>(a, lc, in[p], t, valid, v, r, grp, ts);
+    if (r == 0) {
+      s_len[slot] = ts.L;
+      s_k[slot] = ts.k;
+    }
+    __syncthreads();
+    // offsets within the pass: every row scans the pass's 16 lengths
+    const uint32_t len = s_len[p * 16 + r];
+    const uint32_t incl = row_scan_u32(len);
+    const uint32_t tb = base + (uint32_t)__builtin_amdgcn_ds_bpermute(paddr, (int)(incl - len));
+    if (r == 0) s_lo[slot] = tb;
+    base += __builtin_amdgcn_readlane(incl, 15);
+    tile_pack<L>(s_stage, tb, ts, v, r, vaddr, grp, valid);
+  }
+  __syncthreads();
+  return base;  // >= 256: every chunk holds a tile
+}
+
+// Whole uint4 blocks of a chunk's staging: its used words and at least one
+// zero word after them.  A chunk is staged when one more block still fits its
+// slot (slot_words, a multiple of 4: place_k's loads reach one block past the
+// staged ones); otherwise place_k encodes it again.
+__device__ __forceinline__ uint32_t staged_blocks(uint32_t A) { return ((A >> 5) + 2u + 3u) >> 2; }
+__device__ __forceinline__ bool is_staged(uint32_t A, uint32_t slot_words) { return staged_blocks(A) < (slot_words >> 2); }
+
+// Encode, step 1 of 3: one chunk of kChunkTiles tiles per work-group, chunk =
+// blockIdx.x: its records in LDS (pack_chunk), then its bits to its staging
+// slot when they fit, its bit count to agg, its last 32 bits to tailw, and per
+// tile the chunk-local bit offset and k.  No work-group waits on another.
+// LEN_ONLY: the chunk's bit count only.
+template <int L, bool DITHER, int IN, bool LEN_ONLY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IN == 1 ? 8 : 1))) void encode_k(EncArgs a) {
+  constexpr bool BF16 = IN == 1, PRE = IN == 2;
+  __shared__ __align__(16) uint32_t s_stage[LEN_ONLY ? 4 : kSlotWords];
+  __shared__ uint32_t s_len[kChunkTiles], s_lo[kChunkTiles], s_k[kChunkTiles];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t chunk = blockIdx.x;
+  const uint64_t t_first = (uint64_t)chunk * kChunkTiles;
 
   if constexpr (LEN_ONLY) {
+    const int grp = lane >> 4, r = lane & 15, v = lane_vector(r), pslot = wv * 4 + grp;
+    const LaneConst<BF16> lc(a, v);
+    InVec<BF16> in[kPasses];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const uint64_t t = t_first + p * 16 + pslot;
+      in[p] = load_in<BF16, false>(a.x, t, v, t < a.n_tiles);
+    }
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int slot = p * 16 + pslot;
@@ -334,38 +388,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IN == 1 ? 8
       if (lane == 0) a.partials[chunk] = A;
     }
   } else {
-    for (int i = tid; i < kSlotWords / 4; i += 256) reinterpret_cast<uint4*>(s_stage)[i] = make_uint4(0u, 0u, 0u, 0u);
-    // lane permute addresses: the row's lane of slot pslot, and of vector r
-    const int paddr = ((lane & ~15) | pslot) << 2, vaddr = ((lane & ~15) | v) << 2;
-    uint32_t base = 0;  // wave-uniform bit offset of the current pass
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int slot = p * 16 + pslot;
-      const uint64_t t = t_first + slot;
-      const bool valid = t < a.n_tiles;
-      TileSyms ts;
-      tile_front<L, DITHER, BF16, PRE>(a, lc, in[p], t, valid, v, r, grp, ts);
-      if (r == 0) {
-        s_len[slot] = ts.L;
-        s_k[slot] = ts.k;
+    const uint32_t A = pack_chunk<L, DITHER, IN, true>(a, chunk, s_stage, s_len, s_lo, s_k);
+    const uint32_t n4 = staged_blocks(A);
+    if (is_staged(A, a.slot_words)) {
+      uint4* dst = reinterpret_cast<uint4*>(a.stage + (uint64_t)chunk * a.slot_words);
+      for (uint32_t i = tid; i < n4; i += 256) {
+        const uint4 q = reinterpret_cast<const uint4*>(s_stage)[i];
+        store_nt4(&dst[i].x, q.x, q.y, q.z, q.w);
       }
-      __syncthreads();
-      // offsets within the pass: every row scans the pass's 16 lengths
-      const uint32_t len = s_len[p * 16 + r];
-      const uint32_t incl = row_scan_u32(len);
-      const uint32_t tb = base + (uint32_t)__builtin_amdgcn_ds_bpermute(paddr, (int)(incl - len));
-      if (r == 0) s_lo[slot] = tb;
-      base += __builtin_amdgcn_readlane(incl, 15);
-      tile_pack<L>(s_stage, tb, ts, v, r, vaddr, grp, valid);
-    }
-    const uint32_t A = base;  // >= 256: every chunk holds a tile
-    __syncthreads();
-    // the used words and at least one zero word after them, in whole uint4
-    const uint32_t n4 = ((A >> 5) + 2u + 3u) >> 2;
-    uint4* dst = reinterpret_cast<uint4*>(a.stage + (uint64_t)chunk * kSlotWords);
-    for (uint32_t i = tid; i < n4; i += 256) {
-      const uint4 q = reinterpret_cast<const uint4*>(s_stage)[i];
-      store_nt4(&dst[i].x, q.x, q.y, q.z, q.w);
     }
     if (tid < kChunkTiles) {
       const uint64_t t = t_first + tid;
@@ -443,6 +473,79 @@ __global__ __launch_bounds__(1024) void blockscan_k(uint64_t* T, uint32_t nb) {
   }
 }
 
+// Placement (step 3): chunks per work-group (one per wave), and the chunk
+// count up to which each work-group sums the counts before its own.
+constexpr uint32_t kSelfScanChunks = 8192;
+constexpr uint32_t kPlaceChunks = 4;
+
+// Stream words of one chunk from its bits in LDS, by the whole work-group:
+// the chunk's bits go to stream bits [E, E + A) with a funnel shift, stream
+// word first + i (i < nw) = (s[i] : s[i - 1]) >> (32 - sh), s[-1] holding the
+// 32 stream bits before the chunk, in aligned 16-byte groups: thread q writes
+// stream words g .. g + 3 with g = first - al + 4 q, i.e. i = li .. li + 3,
+// li = 4 q - al, from s[li - 1 .. li + 3] (li - 1 >= -4: s has 4 words before
+// it; li + 3 <= nw + 2 <= 2963).  The last chunk also writes its partial last
+// word; the others leave it to the chunk after them.
+__device__ __forceinline__ void put_chunk_words(uint32_t* words, uint64_t cap_words, const uint32_t* s, uint64_t E,
+                                                uint32_t A, bool last, uint32_t tid) {
+  const uint64_t E1 = E + A, first = E >> 5;
+  const uint32_t sh = (uint32_t)(E & 31);
+  const uint64_t endw = last ? (E1 + 31) >> 5 : E1 >> 5;
+  const uint64_t stop = endw < cap_words ? endw : cap_words;
+  const uint32_t nw = stop > first ? (uint32_t)(stop - first) : 0u;
+  const uint32_t al = (uint32_t)(first & 3u);
+  for (uint32_t q = tid; 4u * q < nw + al; q += 256u) {
+    const int32_t li = (int32_t)(4u * q) - (int32_t)al;
+    const uint32_t* src = s + li - 1;
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = sh ? __builtin_amdgcn_alignbit(src[e + 1], src[e], 32 - sh) : src[e + 1];
+    uint32_t* dst = words + (first - al) + 4u * q;
+    if (li >= 0 && li + 3 < (int32_t)nw) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (li + e >= 0 && li + e < (int32_t)nw) dst[e] = o[e];
+    }
+  }
+}
+
+// place_k's second part for plans with a compact workspace: the chunks of
+// the work-group that were not staged, encoded again by the whole work-group
+// and written straight into the stream (E: the calling wave's chunk offset).
+template <int L, bool DITHER, int IN>
+__device__ __forceinline__ void place_unstaged(const EncArgs& a, uint32_t cg, uint64_t E, uint64_t B) {
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+  // chunks that were not staged, after the staged ones so that only E is
+  // live here (uniform: every wave reads the same four counts)
+  uint32_t redo = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kPlaceChunks; ++w)
+    if (cg + w < a.n_chunks && !is_staged(a.agg[cg + w], a.slot_words)) redo |= 1u << w;
+  if (redo) {
+    __shared__ __align__(16) uint32_t s_buf[4 + kSlotWords];
+    __shared__ uint32_t s_len[kChunkTiles], s_lo[kChunkTiles], s_k[kChunkTiles];
+    __shared__ unsigned long long s_E[kPlaceChunks];
+    if (lane == 0) s_E[wv] = E;
+    __syncthreads();
+    for (uint32_t w = 0; w < kPlaceChunks; ++w) {  // (uniform)
+      if (!((redo >> w) & 1u)) continue;
+      const uint32_t c = cg + w;
+      const uint32_t A2 = pack_chunk<L, DITHER, IN, false>(a, c, s_buf + 4, s_len, s_lo, s_k);
+      if (tid == 0) {  // the 32 stream bits before the chunk
+        uint32_t t2 = 0u;
+        if (c > 0) t2 = a.tailw[c - 1];
+        else if ((B & 31) && (B >> 5) < a.cap_words) t2 = a.words[B >> 5] << (32u - (uint32_t)(B & 31));
+        s_buf[3] = t2;
+      }
+      __syncthreads();
+      put_chunk_words(a.words, a.cap_words, s_buf + 4, s_E[w], A2, c == a.n_chunks - 1, tid);
+      __syncthreads();  // before s_buf is filled again
+    }
+  }
+}
+
 // Encode, step 3 of 3: one chunk per wave, kPlaceChunks chunks per
 // work-group.  The chunk's staged bits go to stream bits [B + E[c], B + E[c+1])
 // with a funnel shift, four words per lane (the first kSpecIters uint4 of
@@ -456,16 +559,20 @@ __global__ __launch_bounds__(1024) void blockscan_k(uint64_t* T, uint32_t nb) {
 // first (all reads of one small array that the L2 serves) and each wave adds
 // those of the work-group's chunks before its own, so step 2 is skipped; above
 // that as the bits of the blocks of 1024 chunks before its own (step 2) plus
-// the counts in its block before it.
-constexpr uint32_t kSelfScanChunks = 8192;
-constexpr uint32_t kPlaceChunks = 4;  // one per wave
-template <bool SELF_SCAN>
-__global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
+// the counts in its block before it.  REDO (plans with a compact workspace,
+// whose slots are sized from the plan's rate with a margin): a chunk that did
+// not fit its slot (rare) is encoded again here by the whole work-group, from
+// its input, straight into the stream.  That path needs the encode's
+// registers, which costs the common path a tighter register budget, so plans
+// with full-size slots (every chunk fits) run the instance without it.
+template <int L, bool DITHER, int IN, bool SELF_SCAN, bool REDO>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(REDO ? 8 : 1))) void place_k(EncArgs a) {
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
   const uint32_t cg = blockIdx.x * kPlaceChunks;  // the work-group's first chunk
   const uint32_t chunk = cg + wv;
   const bool live = chunk < a.n_chunks;  // (wave-uniform)
-  const uint32_t* st = a.stage + (uint64_t)chunk * kSlotWords;
+  const uint32_t sb = a.slot_words >> 2;  // uint4 blocks per slot
+  const uint32_t* st = a.stage + (uint64_t)chunk * a.slot_words;
   // SELF_SCAN: the counts [0, cg) as uint4 (the count array is padded to 64
   // entries), loaded first so that summing them waits for these loads only;
   // only the rounds of 1024 that hold counts below cg are loaded, and lanes
@@ -488,10 +595,10 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
   const uint4* st4 = reinterpret_cast<const uint4*>(st);
   uint4 u0[kSpecIters], u1[kSpecIters];
 #pragma unroll
-  for (uint32_t j = 0; j < kSpecIters; ++j) {
+  for (uint32_t j = 0; j < kSpecIters; ++j) {  // (within the slot)
     const uint32_t q = lane + 64u * j;
-    u1[j] = live ? st4[q] : make_uint4(0u, 0u, 0u, 0u);
-    u0[j] = (live && q) ? st4[q - 1u] : make_uint4(0u, 0u, 0u, 0u);
+    u1[j] = live && q < sb ? st4[q] : make_uint4(0u, 0u, 0u, 0u);
+    u0[j] = (live && q && q <= sb) ? st4[q - 1u] : make_uint4(0u, 0u, 0u, 0u);
   }
   const uint64_t B = a.base ? *a.base : 0ull;  // work-group uniform
   uint32_t tw = 0u;                            // wave uniform
@@ -542,58 +649,63 @@ __global__ __launch_bounds__(256) void place_k(PlaceArgs a) {
     }
     E = live ? B + pre + a.eloc[chunk] : 0ull;
   }
-  if (!live) return;
-  const uint64_t E1 = E + A;
-  if (lane == 0 && chunk == a.n_chunks - 1 && (E1 + 31) / 32 > a.cap_words) atomicOr(&a.ws->status, 1u << 4);
-  if (tl) {
-    a.offsets[t] = E + lc;
-    if (t == a.n_tiles - 1) a.offsets[a.n_tiles] = E1;
-  }
-  const bool last = chunk == a.n_chunks - 1;
-  const uint64_t first = E >> 5;
-  const uint32_t sh = (uint32_t)(E & 31);
-  const uint64_t endw = last ? (E1 + 31) >> 5 : E1 >> 5;
-  const uint64_t stop = endw < a.cap_words ? endw : a.cap_words;
-  const uint32_t nw = stop > first ? (uint32_t)(stop - first) : 0u;
-  // stream words first + i (i < nw) = (s[i] : s[i - 1]) >> (32 - sh), in
-  // 16-byte aligned groups: lane l of round j writes words g .. g + 3 with
-  // g = first - al + 4 (64 j + l), i.e. i = li .. li + 3, li = 4 (64 j + l) - al;
-  // its staged words s[li - 1 .. li + 3] are entries 3 - al .. 7 - al of the
-  // two blocks it holds.  Blocks read past the spec rounds have li < nw, so
-  // 4 q <= nw + 2 <= 2963: inside the slot.
-  const uint32_t al = (uint32_t)(first & 3u);  // (wave uniform)
-  auto group = [&](uint32_t j, const uint4& b0, const uint4& b1) {
-    const uint32_t q = lane + 64u * j;
-    const int32_t li = (int32_t)(4u * q) - (int32_t)al;
-    uint32_t w[5];
-    if (al == 0) {  // (uniform)
-      w[0] = b0.w; w[1] = b1.x; w[2] = b1.y; w[3] = b1.z; w[4] = b1.w;
-    } else if (al == 1) {
-      w[0] = b0.z; w[1] = b0.w; w[2] = b1.x; w[3] = b1.y; w[4] = b1.z;
-    } else if (al == 2) {
-      w[0] = b0.y; w[1] = b0.z; w[2] = b0.w; w[3] = b1.x; w[4] = b1.y;
-    } else {
-      w[0] = b0.x; w[1] = b0.y; w[2] = b0.z; w[3] = b0.w; w[4] = b1.x;
+  if (live) {
+    const uint64_t E1 = E + A;
+    if (lane == 0 && chunk == a.n_chunks - 1 && (E1 + 31) / 32 > a.cap_words) atomicOr(&a.ws->status, 1u << 4);
+    if (tl) {
+      a.offsets[t] = E + lc;
+      if (t == a.n_tiles - 1) a.offsets[a.n_tiles] = E1;
     }
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = sh ? __builtin_amdgcn_alignbit(w[e + 1], w[e], 32 - sh) : w[e + 1];
-    uint32_t* dst = a.words + (first - al) + 4u * q;
-    if (li >= 0 && li + 3 < (int32_t)nw) {
-      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (li + e >= 0 && li + e < (int32_t)nw) dst[e] = o[e];
+    const bool last = chunk == a.n_chunks - 1;
+    const uint64_t first = E >> 5;
+    const uint32_t sh = (uint32_t)(E & 31);
+    const uint64_t endw = last ? (E1 + 31) >> 5 : E1 >> 5;
+    const uint64_t stop = endw < a.cap_words ? endw : a.cap_words;
+    const uint32_t nw = stop > first ? (uint32_t)(stop - first) : 0u;
+    // stream words first + i (i < nw) = (s[i] : s[i - 1]) >> (32 - sh), in
+    // 16-byte aligned groups: lane l of round j writes words g .. g + 3 with
+    // g = first - al + 4 (64 j + l), i.e. i = li .. li + 3, li = 4 (64 j + l) - al;
+    // its staged words s[li - 1 .. li + 3] are entries 3 - al .. 7 - al of the
+    // two blocks it holds.  Blocks read past the spec rounds have li < nw, so
+    // 4 q <= nw + 2 <= (A >> 5) + 4, q <= staged_blocks(A) < slot_words / 4:
+    // inside the slot.
+    const uint32_t al = (uint32_t)(first & 3u);  // (wave uniform)
+    auto group = [&](uint32_t j, const uint4& b0, const uint4& b1) {
+      const uint32_t q = lane + 64u * j;
+      const int32_t li = (int32_t)(4u * q) - (int32_t)al;
+      uint32_t w[5];
+      if (al == 0) {  // (uniform)
+        w[0] = b0.w; w[1] = b1.x; w[2] = b1.y; w[3] = b1.z; w[4] = b1.w;
+      } else if (al == 1) {
+        w[0] = b0.z; w[1] = b0.w; w[2] = b1.x; w[3] = b1.y; w[4] = b1.z;
+      } else if (al == 2) {
+        w[0] = b0.y; w[1] = b0.z; w[2] = b0.w; w[3] = b1.x; w[4] = b1.y;
+      } else {
+        w[0] = b0.x; w[1] = b0.y; w[2] = b0.z; w[3] = b0.w; w[4] = b1.x;
+      }
+      uint32_t o[4];
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = sh ? __builtin_amdgcn_alignbit(w[e + 1], w[e], 32 - sh) : w[e + 1];
+      uint32_t* dst = a.words + (first - al) + 4u * q;
+      if (li >= 0 && li + 3 < (int32_t)nw) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+      } else {
+  #pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (li + e >= 0 && li + e < (int32_t)nw) dst[e] = o[e];
+      }
+    };
+    if (is_staged(A, a.slot_words)) {  // else its words come from place_unstaged
+  #pragma unroll
+      for (uint32_t j = 0; j < kSpecIters; ++j)
+        if ((int32_t)(4u * (lane + 64u * j)) - (int32_t)al < (int32_t)nw) group(j, u0[j], u1[j]);
+      for (uint32_t j = kSpecIters; 256u * j < nw + al; ++j) {
+        const uint32_t q = lane + 64u * j;
+        if ((int32_t)(4u * q) - (int32_t)al < (int32_t)nw) group(j, st4[q - 1u], st4[q]);
+      }
     }
-  };
-#pragma unroll
-  for (uint32_t j = 0; j < kSpecIters; ++j)
-    if ((int32_t)(4u * (lane + 64u * j)) - (int32_t)al < (int32_t)nw) group(j, u0[j], u1[j]);
-  for (uint32_t j = kSpecIters; 256u * j < nw + al; ++j) {
-    const uint32_t q = lane + 64u * j;
-    if ((int32_t)(4u * q) - (int32_t)al < (int32_t)nw) group(j, st4[q - 1u], st4[q]);
   }
+  if constexpr (REDO) place_unstaged<L, DITHER, IN>(a, cg, E, B);  // (full-size slots: every chunk was staged)
 }
 
 // ===========================================================================
@@ -899,8 +1011,6 @@ __device__ __forceinline__ void tile_records(const uint64_t* s_off, const uint32
 
 template <int L, bool DITHER, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OUT == kOutScores ? 1 : 8))) void decode_k(DecArgs a) {
-  constexpr uint32_t RAW = Lat<L>::raw;
-  constexpr uint32_t MAXREC = RAW + 128u * 23u;
   __shared__ __align__(16) uint32_t s_stage[kStageWords];
   __shared__ uint64_t s_off[kChunkTiles + 1];
   __shared__ uint32_t s_k[kChunkTiles];
@@ -1171,26 +1281,20 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
     // up to 64 blocks the placement sums the totals itself (one launch fewer)
     if (nb > 64) hipLaunchKernelGGL(blockscan_k, dim3(1), dim3(1024), 0, st, blockpre, nb);
   }
-  PlaceArgs pa;
-  pa.block_totals = !self_scan && (a.n_chunks + kScanBlock - 1) / kScanBlock <= 64;
-  pa.agg = a.agg;
-  pa.ws = a.ws;
-  pa.stage = a.stage;
-  pa.loc = a.loc;
-  pa.tailw = a.tailw;
-  pa.n_tiles = a.n_tiles;
-  pa.n_chunks = a.n_chunks;
-  pa.words = a.words;
-  pa.cap_words = a.cap_words;
-  pa.offsets = a.offsets;
-  pa.base = a.base;
-  pa.eloc = eloc;
-  pa.blockpre = blockpre;
+  a.block_totals = !self_scan && (a.n_chunks + kScanBlock - 1) / kScanBlock <= 64;
+  a.eloc = eloc;
+  a.blockpre = blockpre;
   const dim3 pgrid((a.n_chunks + kPlaceChunks - 1) / kPlaceChunks);
-  if (self_scan)
-    hipLaunchKernelGGL(place_k<true>, pgrid, dim3(256), 0, st, pa);
-  else
-    hipLaunchKernelGGL(place_k<false>, pgrid, dim3(256), 0, st, pa);
+  // rate-sized slots take the placement that can encode a chunk again; with
+  // full-size slots every chunk is staged and the lean one runs
+  const bool redo = a.slot_words < (uint32_t)kSlotWords;
+  if (self_scan) {
+    if (redo) hipLaunchKernelGGL((place_k<L, DITHER, IN, true, true>), pgrid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((place_k<L, DITHER, IN, true, false>), pgrid, dim3(256), 0, st, a);
+  } else {
+    if (redo) hipLaunchKernelGGL((place_k<L, DITHER, IN, false, true>), pgrid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((place_k<L, DITHER, IN, false, false>), pgrid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -43,6 +43,24 @@ def test_sizes(hq):
     assert hq.Plan("Z", 4.0, 1).bound_words(32) == 32 * 128 * 23 // 32
     assert p.workspace_bytes(1) >= 256 + 16
     assert p.workspace_bytes(4096) >= 256 + 128 * 16
+    # full-size staging slots by default; a compact workspace follows the
+    # plan's rate: under half the bf16 bytes of the tiles at 4 bps, full-size
+    # slots from about 21 bps
+    n = 131072
+    full = p.workspace_bytes(n)
+    assert full > 1.4 * 256 * n
+    assert hq.Plan("E8", 1.0, 1).workspace_bytes(n) == full
+    c = lambda bps: hq.Plan("E8", bps, 1).set_compact_workspace().workspace_bytes(n)
+    assert c(4.0) < 0.5 * 256 * n
+    assert c(1.0) < c(4.0) < c(8.0) < full
+    assert c(22.0) == c(1e6) == full
+    assert p.set_compact_workspace(False).workspace_bytes(n) == full
+    assert L_compact_arg_error(hq, p)
+
+
+def L_compact_arg_error(hq, p):
+    return hq.lib().hq_plan_set_compact_workspace(p.handle, 2) == hq.ERR_ARG and \
+        hq.lib().hq_plan_set_compact_workspace(None, 1) == hq.ERR_ARG
 
 
 def test_argument_errors_are_synchronous(hq):
