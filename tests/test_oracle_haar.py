@@ -1,7 +1,8 @@
 """Pins of the oracle's Haar-rotation variant (the QJL rotation the HyperQuant
 explainer compares with the RHT for the KV cache; Methodology 1 and 4).
 
-  * Q is orthogonal to fp32 rounding;
+  * Q is orthogonal to fp32 rounding, and is the orthogonal factor of the
+    seeded Gaussian matrix by an independent QR (LAPACK Householder);
   * Q is Haar distributed: over many seeds the trace has mean 0 and second
     moment 1, and a column's entries have fourth moment 3 / (n (n + 2)), the
     values for the uniform measure on O(n) and on the sphere
@@ -35,6 +36,35 @@ def test_haar_is_orthogonal_and_seeded(orc):
     assert np.abs(q @ q.T - np.eye(128)).max() <= 2 * 2.0 ** -24
     assert np.array_equal(orc.haar(SEED), orc.haar(SEED))
     assert not np.array_equal(orc.haar(SEED), orc.haar(SEED + 1))
+
+
+def test_haar_is_the_qr_factor_of_its_gaussian_matrix(orc):
+    """Q is the orthogonal factor, with a positive diagonal of R, of the
+    seeded Gaussian matrix G (Gram-Schmidt on its columns): against LAPACK's
+    Householder QR (numpy.linalg.qr, an independent algorithm) of the same G,
+    the fp64 factors agree to ~1e-13, so the oracle's fp32 Q must equal the
+    rounded LAPACK Q except where rounding sits on a boundary (one ulp).  G:
+    Box-Muller pairs from Philox4x32-10 counters (p, 0, 0, "HAAR") under the
+    seed's key, row-major.  libhq's Q is compared with this one bit for bit
+    elsewhere, so the pin covers both."""
+    key = np.array([SEED & 0xFFFFFFFF, SEED >> 32], dtype=np.uint32)
+    r = np.stack([orc.philox(np.array([p, 0, 0, 0x48414152], dtype=np.uint32), key) for p in range(128 * 64)])
+    u1 = (r[:, 0].astype(np.float64) + 1.0) / 2.0**32
+    u2 = r[:, 1].astype(np.float64) / 2.0**32
+    rad, ang = np.sqrt(-2.0 * np.log(u1)), 2.0 * np.pi * u2
+    g = np.empty(128 * 128)
+    g[0::2], g[1::2] = rad * np.cos(ang), rad * np.sin(ang)
+    qn, rn = np.linalg.qr(g.reshape(128, 128))
+    qn = qn * np.sign(np.diag(rn))[None, :]
+    qo = orc.haar(SEED)
+    q32 = qn.astype(np.float32)
+    diff = np.abs(qo.astype(np.float64) - qn)
+    ulp = np.spacing(np.abs(q32)).astype(np.float64)
+    assert np.all(diff <= ulp), diff.max()
+    assert np.mean(qo == q32) > 0.999, np.mean(qo == q32)
+    # a transposed or sign-flipped recipe is far off
+    assert np.abs(qo.astype(np.float64) - qn.T).max() > 0.1
+    assert np.abs(qo.astype(np.float64) + qn).max() > 0.1
 
 
 def test_haar_moments(orc):
