@@ -1399,7 +1399,6 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
   const int v = lane_vector(r);
-  const int pslot = wv * 4 + grp;
   const FwhtSigns fs = fwht_signs(v);
   const uint64_t head = blockIdx.y;
   const uint64_t s_first = (uint64_t)blockIdx.x * kKeys;  // first key of the group
@@ -1784,8 +1783,7 @@ __global__ __launch_bounds__(256) void gemm_k(GemmArgs g) {
   __shared__ __align__(16) uint16_t s_B[2][32][kBS];
   __shared__ uint2 s_sel[256];  // bit-select table
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = lane >> 4, r = lane & 15;
-  const int v = lane_vector(r), pslot = wv * 4 + grp;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   s_sel[tid] = reinterpret_cast<const uint2*>(&kSelectLut)[tid];
   const uint32_t r0 = blockIdx.x * 32u;
   const uint32_t b_lo = blockIdx.y * g.per;
