@@ -1082,12 +1082,18 @@ int orc_gemv(int lat, uint64_t seed, float alpha, const uint32_t *words, const u
   const uint64_t nblk = cols / N;
   for (uint64_t i = 0; i < (uint64_t)nb * rows; ++i) y[i] = 0.0;
   int status = ORC_OK;
-  for (uint64_t r = 0; r < rows; ++r) {
+  /* rows are independent: with g_threads > 1 they are shared out among host
+   * threads; each row's sums are formed in the same order either way (the only
+   * error a tile can give is ORC_ERR_CORRUPT, so the status is the same too) */
+#pragma omp parallel for num_threads(g_threads) schedule(dynamic, 8) if (g_threads > 1)
+  for (int64_t ri = 0; ri < (int64_t)rows; ++ri) {
+    const uint64_t r = (uint64_t)ri;
     for (uint64_t b = 0; b < nblk; ++b) {
       const uint64_t t = r * nblk + b;
       int32_t codes[N];
       int st = orc_parse_tile(lat, words, offsets[t], offsets[t + 1], (int)k[t], codes);
       if (st != ORC_OK) {
+#pragma omp atomic write
         status = st;
         continue;
       }
@@ -1114,9 +1120,9 @@ int orc_gemv(int lat, uint64_t seed, float alpha, const uint32_t *words, const u
 /* high-resolution estimate alpha0 = sqrt(2 pi e) sigma / (nu 2^R), with     */
 /* sigma the RMS of the tensor and nu the per-dimension cell edge of the     */
 /* embedding (Z 1, A2 sqrt(2 sqrt3), D4 2^(1/4), 2E8 2); bracket the target  */
-/* in log2(alpha) from floor(log2 alpha0) -/+ 4 (an integer, so the bracket  */
-/* does not depend on the rounding of sigma) in steps of 4, then bisect on   */
-/* the exact payload rate                                                    */
+/* in log2(alpha) from exact integers that contain log2 alpha0 (the binary   */
+/* exponent of max |x|, ceil(log2 N) and floor(bps): see below), widen it by */
+/* 4 while it does not hold the target, then bisect on the exact payload rate */
 /* until it is within 0.002 bps, at most 40 times.  The fp32 alpha with the  */
 /* closest rate wins; ties go to the larger alpha.                           */
 /* ------------------------------------------------------------------------ */

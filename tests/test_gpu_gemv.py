@@ -113,12 +113,14 @@ def test_gemv_weight_4096x4096(hq, orc):
     check(hq, orc, 3, w, x, alpha)
 
 
-def test_gemv_weight_8192x28672_sampled_rows(hq, orc):
-    """The 8192x28672 workload matrix (E8, calibrated 4 bps), one vector: 48
-    sampled rows (first, last and random) against the oracle, which encodes and
-    multiplies each sampled row on its own (rows are independent without
-    dither)."""
+def test_gemv_weight_8192x28672_all_rows(hq, orc):
+    """The 8192x28672 workload matrix (E8, calibrated 4 bps), one vector, every
+    one of the 8192 outputs against the oracle's product (the oracle encodes
+    the whole matrix and multiplies it on all host threads; rows are
+    independent, so its sums are the single-thread ones)."""
+    import os
     from lattice_vq_entropy_amd import workloads as W
+    threads = max(1, min(16, os.cpu_count() or 1))
     w = W.c4("cuda")
     rows, cols = w.shape
     plan = hq.Plan(3, 4.0, SEED)
@@ -131,18 +133,18 @@ def test_gemv_weight_8192x28672_sampled_rows(hq, orc):
     y = hq.gemv(plan, enc, rows, cols, torch.from_numpy(x).cuda(), gws)
     assert hq.status_sync(gws) == hq.OK
     y = y.cpu().numpy().astype(np.float64)
-    rng = np.random.default_rng(8192)
-    sample = sorted(set([0, 1, rows - 1] + rng.choice(rows, size=45, replace=False).tolist()))
-    wr = w[torch.tensor(sample, device=w.device)].cpu()
-    for i, r in enumerate(sample):
-        st, ow, oo, ok = orc.encode(3, SEED, alpha, host_bits(wr[i:i + 1]))
-        assert st == 0
-        st, yo = orc.gemv(3, SEED, alpha, ow, oo, ok, 1, cols, x)
-        assert st == 0
-        b = bound(orc, 3, alpha, ow, oo, ok, 1, cols, x)
-        assert abs(y[0, r] - yo[0, 0]) <= b[0, 0], (r, y[0, r], yo[0, 0], b[0, 0])
-    del w
+    wh = host_bits(w)
+    del w, enc, ws
     torch.cuda.empty_cache()
+    print(f"gemv 8192x28672: oracle on {threads} threads", flush=True)
+    with orc.threads(threads):
+        st, ow, oo, ok = orc.encode(3, SEED, alpha, wh)
+        assert st == 0
+        st, yo = orc.gemv(3, SEED, alpha, ow, oo, ok, rows, cols, x)
+        assert st == 0
+        b = bound(orc, 3, alpha, ow, oo, ok, rows, cols, x)
+    err = np.abs(y - yo)
+    assert np.all(err <= b), f"max err/bound {float((err / b).max()):.3f} at {np.unravel_index(np.argmax(err / b), b.shape)}"
 
 
 def test_gemv_corrupt_record(hq, orc):

@@ -90,3 +90,26 @@ def test_parallel_statuses_equal_serial(orc):
             ys.append(y)
     assert np.array_equal(ys[0], ys[1])
     assert np.all(ys[0].reshape(-1, 128)[17] == 0)
+
+
+def test_parallel_gemv_equals_serial(orc):
+    """The product over rows on several threads: the same sums (each row's
+    in the same order) and the same status for a record that does not parse."""
+    rng = np.random.default_rng(92)
+    rows, cols = 37, 640
+    x = inputs(rng, rows * cols // 128, bf16=True)
+    v = rng.standard_normal((3, cols)).astype(np.float32)
+    with orc.threads(1):
+        st, w, off, k = orc.encode(3, SEED, 0.004, x)
+        assert st == 0
+    k2 = k.copy()
+    k2[50] = 30
+    out = {}
+    for nt in (1, 7):
+        with orc.threads(nt):
+            out[nt] = (orc.gemv(3, SEED, 0.004, w, off, k, rows, cols, v),
+                       orc.gemv(3, SEED, 0.004, w, off, k2, rows, cols, v))
+    (s1, y1), (c1, z1) = out[1]
+    (s7, y7), (c7, z7) = out[7]
+    assert s1 == s7 == 0 and c1 == c7 == orc.ERR_CORRUPT
+    assert np.array_equal(y1, y7) and np.array_equal(z1, z7)
