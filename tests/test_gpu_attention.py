@@ -270,9 +270,9 @@ def test_attention_corrupt_key_record(hq, orc):
 
 def test_attention_1x8x131072_e8(hq, orc):
     """The long-context workload: K and V of 8 heads x 131072 tokens, E8 at
-    1.7 bps with dither, 32 queries (4 per head); every head on the GPU, heads
-    0 and 7 against the oracle, which encodes those heads itself (tile ids as
-    in the whole-layer streams)."""
+    1.7 bps with dither, 32 queries (4 per head); every head on the GPU and
+    every head against the oracle, which encodes each head itself (tile ids
+    as in the whole-layer streams)."""
     from lattice_vq_entropy_amd import workloads as W
     heads, seq, qph, scale = 8, 131072, 4, 128 ** -0.5
     k, v, q = W.c5("cpu")
@@ -291,11 +291,15 @@ def test_attention_1x8x131072_e8(hq, orc):
     assert np.isfinite(out).all()
     kb16, vb16 = host_bits(k).reshape(heads, seq * 128), host_bits(v).reshape(heads, seq * 128)
     qn = q.numpy()
-    for h in (0, 7):
-        st, w, o, kk = orc.encode(3, SEED, ak, kb16[h], dithered=True, tile_base=h * seq)
-        assert st == 0
-        st, w2, o2, kk2 = orc.encode(3, SEED, av, vb16[h], dithered=True, tile_base=vb + h * seq)
-        assert st == 0
+    import os
+    threads = max(1, min(16, os.cpu_count() or 1))
+    for h in range(heads):
+        print(f"attention 1x8x131072: head {h} against the oracle", flush=True)
+        with orc.threads(threads):
+            st, w, o, kk = orc.encode(3, SEED, ak, kb16[h], dithered=True, tile_base=h * seq)
+            assert st == 0
+            st, w2, o2, kk2 = orc.encode(3, SEED, av, vb16[h], dithered=True, tile_base=vb + h * seq)
+            assert st == 0
         qh = qn[h * qph:(h + 1) * qph]
         st, ref = orc.kv_attention(3, SEED, ak, (w, o, kk), h * seq, av, (w2, o2, kk2), vb + h * seq, 1, seq, qh,
                                    qph, scale)
