@@ -101,6 +101,48 @@ def cpu_baseline(x_host_bits, alpha, seed, reps, c1_bits, c1_alpha):
             "input_sha256": hashlib.sha256(x_host_bits.tobytes()).hexdigest()}
 
 
+def cpu_per_workload(torch, hq, W, dev, seed):
+    """The oracle on a bounded slice of each of the other workloads (encode +
+    decode, bf16 in), on all host cores and on one thread, at the alpha the
+    GPU calibration gives the slice: the large weight's first 512 rows, one
+    KV head of the 8x8x32768 tensor, one KV head of the 1x8x131072 tensor."""
+    import numpy as np
+    from oracle import oracle as O
+    O.lib()
+    n_all = max(1, min(int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1),
+                       os.cpu_count() or 1))
+    cases = [("bf16 8192x28672 weight, rows 0..511 (1/16 of it)", lambda: W.c4(dev)[:512], 3, 4.0, False),
+             ("KV bf16 [8,8,32768,128] K, batch 0 head 0 (1/64 of it)", lambda: W.c3(dev)[0][0, 0], 2, 2.0, True),
+             ("KV bf16 [1,8,131072,128] K, head 0 (1/8 of it)", lambda: W.c5(dev)[0][0, 0], 3, 1.7, True)]
+    out = []
+    for name, make, lat, bps, dith in cases:
+        x = make().contiguous()
+        n_tiles = x.numel() // 128
+        plan = hq.Plan(lat, bps, seed)
+        ws = plan.workspace(n_tiles)
+        alpha, rate = plan.calibrate(x, ws, dithered=dith)
+        xb = x.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+        del x, ws
+        torch.cuda.empty_cache()
+        n_bytes = xb.size * 2
+        res = {"sample": name, "lattice": ["Z", "A2", "D4", "E8"][lat], "bps": round(rate, 4), "dithered": dith}
+        for nt, budget in ((n_all, 1.0), (1, 0.5)):
+            with O.threads(nt):
+                reps, t_total = 0, 0.0
+                while t_total < budget or reps == 0:
+                    t0 = time.perf_counter()
+                    st, w, off, k = O.encode(lat, seed, alpha, xb, dithered=dith)
+                    st2, y = O.decode(lat, seed, alpha, w, off, k, dithered=dith, out_dtype=O.BF16)
+                    t_total += time.perf_counter() - t0
+                    reps += 1
+                    assert st == 0 and st2 == 0
+            key = "all_cores" if nt == n_all else "single_thread"
+            res[key] = {"GBps": round(2.0 * n_bytes * reps / t_total / 1e9, 4), "cores": nt, "repetitions": reps,
+                        "seconds": round(t_total, 2)}
+        out.append(res)
+    return out
+
+
 def copy_ceiling(torch, dev, nbytes=1 << 30, iters=20):
     """Measured HBM ceiling: device-to-device copy of 1 GiB (hipMemcpyAsync
     through torch), median over iters, read + write bytes per second."""
@@ -486,6 +528,7 @@ def main():
         c1 = W.c1("cpu").numpy().reshape(-1)
         c1_alpha = float(np.float32(np.sqrt(2 * np.pi * np.e) * W.c1_sigma_eff() / 32.0))
         line["cpu_baseline"] = cpu_baseline(xb, alpha, seed, args.cpu_reps, c1, c1_alpha)
+        line["cpu_baseline"]["other_workloads"] = cpu_per_workload(torch, hq, W, dev, seed)
     print(json.dumps(line), flush=True)
 
 
