@@ -33,14 +33,16 @@
  *     workspace, hq_plan_set_compact_workspace), 16-byte aligned, zero-filled
  *     by the caller once before its first use.  One workspace must not be used by two calls that can run
  *     concurrently (e.g. on two streams).
- *   - No call waits on another work-group's progress; encode is two
- *     stream-ordered launches (pack per chunk, then placement, which sums the
- *     bit counts of the chunks before its own) up to 8192 chunks of 32 tiles,
- *     and three above (the bit counts of blocks of 1024 chunks between them;
- *     placement then adds the totals of the blocks before its own and its own
- *     block's counts), four above 65536 chunks (the block totals turned into
- *     prefixes by a launch of their own).  Encode
- *     and decode allocate nothing and can be captured in a HIP graph.
+ *   - No call waits on another work-group's progress; encode is one launch
+ *     for at most 32 tiles (one chunk: its offset is the stream's start, so
+ *     the packing launch writes the stream itself), two stream-ordered
+ *     launches (pack per chunk, then placement, which sums the bit counts of
+ *     the chunks before its own) up to 8192 chunks of 32 tiles, and three
+ *     above (the bit counts of blocks of 1024 chunks between them; placement
+ *     then adds the totals of the blocks before its own and its own block's
+ *     counts), four above 65536 chunks (the block totals turned into prefixes
+ *     by a launch of their own).  Encode and decode allocate nothing and can
+ *     be captured in a HIP graph.
  *   - Tensors are row-major; every 128 consecutive elements form one tile
  *     (weights: tiles along rows; KV [B, H, S, 128]: one tile per vector).
  *   - Stream layout: record of tile t at bits [offsets[t], offsets[t+1]):

@@ -40,6 +40,7 @@ struct EncArgs {
   const uint32_t* eloc;
   const uint64_t* blockpre;
   int block_totals;
+  int direct;  // one chunk: encode_k writes the stream itself (set by the launcher)
 };
 
 struct DecArgs {

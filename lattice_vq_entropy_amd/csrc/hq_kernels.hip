@@ -343,6 +343,44 @@ __device__ __forceinline__ uint32_t pack_chunk(const EncArgs& a, uint32_t chunk,
   return base;  // >= 256: every chunk holds a tile
 }
 
+// Placement (step 3): chunks per work-group (one per wave), and the chunk
+// count up to which each work-group sums the counts before its own.
+constexpr uint32_t kSelfScanChunks = 8192;
+constexpr uint32_t kPlaceChunks = 4;
+
+// Stream words of one chunk from its bits in LDS, by the whole work-group:
+// the chunk's bits go to stream bits [E, E + A) with a funnel shift, stream
+// word first + i (i < nw) = (s[i] : s[i - 1]) >> (32 - sh), s[-1] holding the
+// 32 stream bits before the chunk, in aligned 16-byte groups: thread q writes
+// stream words g .. g + 3 with g = first - al + 4 q, i.e. i = li .. li + 3,
+// li = 4 q - al, from s[li - 1 .. li + 3] (li - 1 >= -4: s has 4 words before
+// it; li + 3 <= nw + 2 <= 2963).  The last chunk also writes its partial last
+// word; the others leave it to the chunk after them.
+__device__ __forceinline__ void put_chunk_words(uint32_t* words, uint64_t cap_words, const uint32_t* s, uint64_t E,
+                                                uint32_t A, bool last, uint32_t tid) {
+  const uint64_t E1 = E + A, first = E >> 5;
+  const uint32_t sh = (uint32_t)(E & 31);
+  const uint64_t endw = last ? (E1 + 31) >> 5 : E1 >> 5;
+  const uint64_t stop = endw < cap_words ? endw : cap_words;
+  const uint32_t nw = stop > first ? (uint32_t)(stop - first) : 0u;
+  const uint32_t al = (uint32_t)(first & 3u);
+  for (uint32_t q = tid; 4u * q < nw + al; q += 256u) {
+    const int32_t li = (int32_t)(4u * q) - (int32_t)al;
+    const uint32_t* src = s + li - 1;
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = sh ? __builtin_amdgcn_alignbit(src[e + 1], src[e], 32 - sh) : src[e + 1];
+    uint32_t* dst = words + (first - al) + 4u * q;
+    if (li >= 0 && li + 3 < (int32_t)nw) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (li + e >= 0 && li + e < (int32_t)nw) dst[e] = o[e];
+    }
+  }
+}
+
 // Whole uint4 blocks of a chunk's staging: its used words and at least one
 // zero word after them.  A chunk is staged when one more block still fits its
 // slot (slot_words, a multiple of 4: place_k's loads reach one block past the
@@ -354,12 +392,16 @@ __device__ __forceinline__ bool is_staged(uint32_t A, uint32_t slot_words) { ret
 // blockIdx.x: its records in LDS (pack_chunk), then its bits to its staging
 // slot when they fit, its bit count to agg, its last 32 bits to tailw, and per
 // tile the chunk-local bit offset and k.  No work-group waits on another.
-// LEN_ONLY: the chunk's bit count only.
+// direct (a tensor of one chunk): the chunk's stream offset is the stream's
+// start, so the work-group writes the stream words, offsets and k itself and
+// steps 2 and 3 are not launched.  LEN_ONLY: the chunk's bit count only.
 template <int L, bool DITHER, int IN, bool LEN_ONLY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IN == 1 ? 8 : 1))) void encode_k(EncArgs a) {
   constexpr bool BF16 = IN == 1, PRE = IN == 2;
-  __shared__ __align__(16) uint32_t s_stage[LEN_ONLY ? 4 : kSlotWords];
+  // s_buf[3]: the 32 stream bits before the chunk (direct mode); then the chunk's bits
+  __shared__ __align__(16) uint32_t s_buf[LEN_ONLY ? 8 : 4 + kSlotWords];
   __shared__ uint32_t s_len[kChunkTiles], s_lo[kChunkTiles], s_k[kChunkTiles];
+  uint32_t* const s_stage = s_buf + 4;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t chunk = blockIdx.x;
@@ -389,6 +431,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IN == 1 ? 8
     }
   } else {
     const uint32_t A = pack_chunk<L, DITHER, IN, true>(a, chunk, s_stage, s_len, s_lo, s_k);
+    if (a.direct) {
+      // the only chunk: its stream offset is B, so its words, offsets and k
+      // go out from here and no placement launch follows
+      const uint64_t E = a.base ? *a.base : 0ull, E1 = E + A;
+      if (tid == 0) {  // appending: the existing bits below B in its last word
+        uint32_t t2 = 0u;
+        if ((E & 31) && (E >> 5) < a.cap_words) t2 = a.words[E >> 5] << (32u - (uint32_t)(E & 31));
+        s_buf[3] = t2;
+      }
+      __syncthreads();
+      if (tid == 0 && (E1 + 31) / 32 > a.cap_words) set_status(a.ws, 4);
+      if (tid < kChunkTiles) {
+        const uint64_t t = t_first + tid;
+        if (t < a.n_tiles) {
+          a.offsets[t] = E + s_lo[tid];
+          a.kout[t] = (uint8_t)s_k[tid];
+          if (t == a.n_tiles - 1) a.offsets[a.n_tiles] = E1;
+        }
+      }
+      put_chunk_words(a.words, a.cap_words, s_stage, E, A, true, tid);
+      return;
+    }
     const uint32_t n4 = staged_blocks(A);
     if (is_staged(A, a.slot_words)) {
       uint4* dst = reinterpret_cast<uint4*>(a.stage + (uint64_t)chunk * a.slot_words);
@@ -470,44 +534,6 @@ __global__ __launch_bounds__(1024) void blockscan_k(uint64_t* T, uint32_t nb) {
     if (i < nb) T[i] = run;
     __syncthreads();  // every thread has read s_w and s_carry
     if (tid == 1023) s_carry = run + t;
-  }
-}
-
-// Placement (step 3): chunks per work-group (one per wave), and the chunk
-// count up to which each work-group sums the counts before its own.
-constexpr uint32_t kSelfScanChunks = 8192;
-constexpr uint32_t kPlaceChunks = 4;
-
-// Stream words of one chunk from its bits in LDS, by the whole work-group:
-// the chunk's bits go to stream bits [E, E + A) with a funnel shift, stream
-// word first + i (i < nw) = (s[i] : s[i - 1]) >> (32 - sh), s[-1] holding the
-// 32 stream bits before the chunk, in aligned 16-byte groups: thread q writes
-// stream words g .. g + 3 with g = first - al + 4 q, i.e. i = li .. li + 3,
-// li = 4 q - al, from s[li - 1 .. li + 3] (li - 1 >= -4: s has 4 words before
-// it; li + 3 <= nw + 2 <= 2963).  The last chunk also writes its partial last
-// word; the others leave it to the chunk after them.
-__device__ __forceinline__ void put_chunk_words(uint32_t* words, uint64_t cap_words, const uint32_t* s, uint64_t E,
-                                                uint32_t A, bool last, uint32_t tid) {
-  const uint64_t E1 = E + A, first = E >> 5;
-  const uint32_t sh = (uint32_t)(E & 31);
-  const uint64_t endw = last ? (E1 + 31) >> 5 : E1 >> 5;
-  const uint64_t stop = endw < cap_words ? endw : cap_words;
-  const uint32_t nw = stop > first ? (uint32_t)(stop - first) : 0u;
-  const uint32_t al = (uint32_t)(first & 3u);
-  for (uint32_t q = tid; 4u * q < nw + al; q += 256u) {
-    const int32_t li = (int32_t)(4u * q) - (int32_t)al;
-    const uint32_t* src = s + li - 1;
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = sh ? __builtin_amdgcn_alignbit(src[e + 1], src[e], 32 - sh) : src[e + 1];
-    uint32_t* dst = words + (first - al) + 4u * q;
-    if (li >= 0 && li + 3 < (int32_t)nw) {
-      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (li + e >= 0 && li + e < (int32_t)nw) dst[e] = o[e];
-    }
   }
 }
 
@@ -1269,7 +1295,9 @@ static hipError_t launch_encode_t(EncArgs a, bool len_only, hipStream_t st) {
                        (const unsigned long long*)a.partials, a.n_chunks, &a.ws->bits);
     return hipGetLastError();
   }
+  a.direct = a.n_chunks == 1;  // one chunk: encode_k writes the stream itself
   hipLaunchKernelGGL((encode_k<L, DITHER, IN, false>), grid, dim3(256), 0, st, a);
+  if (a.direct) return hipGetLastError();
   const bool self_scan = a.n_chunks <= kSelfScanChunks;
   // step 2 (two-level): Eloc (u32 per chunk, padded to a multiple of 4) at
   // the start of the E region, the block prefixes (u64) after it

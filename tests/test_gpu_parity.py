@@ -191,12 +191,13 @@ def test_offset_paths_at_the_boundary(hq, orc):
     assert hq.status_sync(ws) == hq.ERR_CAPACITY
 
 
-@pytest.mark.parametrize("n_tiles,big", [(97, False), (3000, False), (8193 * 32, True)])
+@pytest.mark.parametrize("n_tiles,big", [(1, False), (32, False), (97, False), (3000, False), (8193 * 32, True)])
 def test_words_outside_the_stream_are_untouched(hq, orc, n_tiles, big):
     """The placement writes exactly the stream's words: with a buffer filled
     with a sentinel, the words past ceil(total / 32) keep it, and with
     cap_words below the need (an HQ_ERR_CAPACITY) so do the words past
-    cap_words; both for the summing placement and (8193 chunks) the scan."""
+    cap_words; for a single chunk (written by the encode launch itself), the
+    summing placement and (8193 chunks) the scan."""
     g = torch.Generator().manual_seed(n_tiles)
     x = (torch.randn(n_tiles, 128, generator=g) * 0.03).to(torch.bfloat16).cuda()
     plan = hq.Plan(3, 4.0, SEED).set_alpha(0.004)
@@ -209,7 +210,7 @@ def test_words_outside_the_stream_are_untouched(hq, orc, n_tiles, big):
     need = enc.used_words()
     assert bool((words[need:] == sentinel).all())
     ref = words[:need].clone()
-    for cap in (need - 1, need - 37, need // 2 + 3):
+    for cap in sorted({max(0, c) for c in (need - 1, need - 37, need // 2 + 3)}):
         words.fill_(sentinel)
         hq.encode(plan, x, ws, out=(words, offsets, k), cap_words=cap)
         assert hq.status_sync(ws) == hq.ERR_CAPACITY
