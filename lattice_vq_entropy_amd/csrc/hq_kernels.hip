@@ -1976,69 +1976,77 @@ hipError_t launch_gemm(int lat, const GemmArgs& g, hipStream_t st) {
 // ===========================================================================
 // Dense rotation (the Haar matrix): y_i = fl32(t_i * scale) with t_i the fp32
 // fma chain over j = 0..127 of M[i][j] x_j, in index order, for every tile.
-// Persistent work-groups: the matrix (as Mt[j][i], 64 KB) is loaded into LDS
-// once; per chunk of 32 tiles the inputs go to LDS transposed (Xt[j][t]) and
-// thread (coordinates 4c..4c+3, tiles 4g..4g+3) keeps 16 chains, reading one
-// float4 of each per step.
+// Persistent work-groups of 512 threads, one per CU: the matrix (as Mt[j][i],
+// 64 KB) is loaded into LDS once; per round of kRotTiles = 128 tiles the
+// inputs go to LDS transposed (Xt[j][t], 64 KB), and thread (coordinates
+// 4c..4c+3, tiles 8g..8g+7) keeps 32 chains.  Per step it reads one float4 of
+// Mt (32 distinct per half-wave) and two of Xt (the same for a half-wave: a
+// broadcast): 48 bytes of LDS per 32 fma, so the vector ALUs, not the LDS,
+// bound it.
 // ===========================================================================
-__global__ __launch_bounds__(256) void rot_k(RotArgs a) {
-  __shared__ __align__(16) float s_m[kTile * kTile];  // Mt[128][128] (64 KB: gfx950 has 160 KB per CU)
-  __shared__ __align__(16) float s_x[kTile * 32];     // Xt[128][32]
+constexpr uint32_t kRotTiles = 128;
+__global__ __launch_bounds__(512) void rot_k(RotArgs a) {
+  __shared__ __align__(16) float s_m[kTile * kTile];      // Mt[128][128]
+  __shared__ __align__(16) float s_x[kTile * kRotTiles];  // Xt[128][128]
   const uint32_t tid = threadIdx.x;
-  for (uint32_t i = tid; i < kTile * kTile / 4; i += 256u)
+  for (uint32_t i = tid; i < kTile * kTile / 4; i += 512u)
     reinterpret_cast<float4*>(s_m)[i] = reinterpret_cast<const float4*>(a.mt)[i];
-  const uint64_t n_chunks = (a.n_tiles + 31) / 32;
-  const uint32_t c4 = 4u * (tid & 31u), g4 = 4u * (tid >> 5);
-  for (uint64_t ch = blockIdx.x; ch < n_chunks; ch += gridDim.x) {
-    // inputs: thread -> tile tid / 8, coordinates 16 (tid % 8) .. + 15
+  const uint64_t n_rounds = (a.n_tiles + kRotTiles - 1) / kRotTiles;
+  const uint32_t c4 = 4u * (tid & 31u), g8 = 8u * (tid >> 5);
+  for (uint64_t rd = blockIdx.x; rd < n_rounds; rd += gridDim.x) {
+    // inputs: thread -> tile tid / 4, coordinates 32 (tid % 4) .. + 31
     {
-      const uint32_t tt = tid >> 3, j0 = 16u * (tid & 7u);
-      const uint64_t t = ch * 32u + tt;
-      float xv[16];
+      const uint32_t tt = tid >> 2, j0 = 32u * (tid & 3u);
+      const uint64_t t = rd * kRotTiles + tt;
+      float xv[32];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) xv[e] = 0.0f;
+      for (int e = 0; e < 32; ++e) xv[e] = 0.0f;
       if (t < a.n_tiles) {
         if (a.in_bf16) {
           const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + t * kTile + j0);
-          const uint4 w0 = p[0], w1 = p[1];
-          const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            xv[2 * e] = __builtin_bit_cast(float, ww[e] << 16);
-            xv[2 * e + 1] = __builtin_bit_cast(float, ww[e] & 0xFFFF0000u);
+          for (int h = 0; h < 4; ++h) {
+            const uint4 w = p[h];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              xv[8 * h + 2 * e] = __builtin_bit_cast(float, ww[e] << 16);
+              xv[8 * h + 2 * e + 1] = __builtin_bit_cast(float, ww[e] & 0xFFFF0000u);
+            }
           }
         } else {
           const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + t * kTile + j0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 8; ++e) {
             const float4 f = p[e];
             xv[4 * e] = f.x; xv[4 * e + 1] = f.y; xv[4 * e + 2] = f.z; xv[4 * e + 3] = f.w;
           }
         }
       }
-      __syncthreads();  // (the matrix is in; the previous chunk's inputs are consumed)
+      __syncthreads();  // (the matrix is in; the previous round's inputs are consumed)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s_x[(j0 + e) * 32u + tt] = xv[e];
+      for (int e = 0; e < 32; ++e) s_x[(j0 + e) * kRotTiles + tt] = xv[e];
     }
     __syncthreads();
-    float acc[4][4];
+    float acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[i][k] = 0.0f;
-#pragma unroll 4
+      for (int k = 0; k < 8; ++k) acc[i][k] = 0.0f;
+#pragma unroll 2
     for (uint32_t j = 0; j < kTile; ++j) {
       const float4 m = *reinterpret_cast<const float4*>(s_m + j * kTile + c4);
-      const float4 x = *reinterpret_cast<const float4*>(s_x + j * 32u + g4);
-      const float mv[4] = {m.x, m.y, m.z, m.w}, xw[4] = {x.x, x.y, x.z, x.w};
+      const float4 x0 = *reinterpret_cast<const float4*>(s_x + j * kRotTiles + g8);
+      const float4 x1 = *reinterpret_cast<const float4*>(s_x + j * kRotTiles + g8 + 4u);
+      const float mv[4] = {m.x, m.y, m.z, m.w}, xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[i][k] = __builtin_fmaf(mv[i], xw[k], acc[i][k]);
+        for (int k = 0; k < 8; ++k) acc[i][k] = __builtin_fmaf(mv[i], xw[k], acc[i][k]);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint64_t t = ch * 32u + g4 + (uint32_t)k;
+    for (int k = 0; k < 8; ++k) {
+      const uint64_t t = rd * kRotTiles + g8 + (uint32_t)k;
       if (t >= a.n_tiles) continue;
       const float o0 = acc[0][k] * a.scale, o1 = acc[1][k] * a.scale, o2 = acc[2][k] * a.scale,
                   o3 = acc[3][k] * a.scale;
@@ -2057,9 +2065,9 @@ __global__ __launch_bounds__(256) void rot_k(RotArgs a) {
 }
 
 hipError_t launch_rot(const RotArgs& a, hipStream_t st) {
-  const uint64_t n_chunks = (a.n_tiles + 31) / 32;
-  const uint32_t grid = (uint32_t)(n_chunks < 512 ? n_chunks : 512);  // two work-groups per CU (LDS)
-  hipLaunchKernelGGL(rot_k, dim3(grid), dim3(256), 0, st, a);
+  const uint64_t n_rounds = (a.n_tiles + kRotTiles - 1) / kRotTiles;
+  const uint32_t grid = (uint32_t)(n_rounds < 256 ? n_rounds : 256);  // one work-group per CU (128 KB of LDS)
+  hipLaunchKernelGGL(rot_k, dim3(grid), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
