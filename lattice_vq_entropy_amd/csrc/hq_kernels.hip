@@ -844,7 +844,7 @@ __device__ __forceinline__ uint32_t unary_starts_general(const uint32_t* s, uint
 // Parse the lane's 8 symbols of one tile record held in LDS (record at local
 // bit base, length Lb, Rice parameter k) and return the dequantised
 // real-space lattice coordinates.  Returns false when the record is corrupt
-// (the verdict is uniform over the 16 lanes of the tile).  ust: 16 words of
+// (the outcome is uniform over the 16 lanes of the tile).  ust: 16 words of
 // LDS per tile.
 template <int L>
 __device__ __forceinline__ bool parse_lane(const uint32_t* s, uint32_t base, uint32_t Lb, uint32_t k, int v, int r,
