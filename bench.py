@@ -502,10 +502,11 @@ def main():
         },
         "encode": {"ms": round(enc_ms, 5), "GBps_bf16_in": round(bf16_bytes / (enc_ms * 1e-3) / 1e9, 1),
                    "GBps_algorithmic": round(enc_gbs, 1), "hbm_frac": round(enc_gbs / HBM_PEAK_GBS, 4),
-                   "kernels": "encode_k + place_k (+ blocksum_k above 8192 chunks)"},
+                   "kernels": "encode_k + place_k (+ blocksum_k above 8192 chunks)",
+                   "traffic_bytes": (traffic_for("encode") or {}).get("total_bytes")},
         "decode": {"ms": round(dec_ms, 5), "GBps_bf16_in": round(bf16_bytes / (dec_ms * 1e-3) / 1e9, 1),
                    "GBps_algorithmic": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                   "kernels": "decode_k"},
+                   "kernels": "decode_k", "traffic_bytes": (traffic_for("decode") or {}).get("total_bytes")},
         "roofline": {
             "kernel": dominant,
             "bound": "hbm",
@@ -515,6 +516,12 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (traffic_for(dominant) or {}).get("total_bytes"),
             "algorithmic_bytes_per_launch": int(alg_bytes),
+            "traffic_GBps": (round(traffic_for(dominant)["total_bytes"] / ((enc_ms if dominant == "encode" else dec_ms)
+                                                                          * 1e-3) / 1e9, 1)
+                             if traffic_for(dominant) else None),
+            "method_minimum_bytes_per_launch": int(bf16_bytes + payload_bytes),
+            "method_minimum_frac": round((bf16_bytes + payload_bytes) / ((enc_ms if dominant == "encode" else dec_ms)
+                                                                         * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "measured_copy_GBps": ceiling["GBps"],
             "frac_of_measured_copy": round(achieved / ceiling["GBps"], 4),
         },
