@@ -110,3 +110,35 @@ def test_mixed_launch_sizes_on_one_workspace(hq, orc):
         st, ow, oo, ok = orc.encode(2, SEED, 0.002, host_input(x))
         assert st == 0
         assert same(got, (ow, oo, ok)), f"launch {i} ({r}x{c}) differs from the oracle"
+
+
+def test_graph_of_single_chunk_encodes_and_appends(hq, orc):
+    """Encodes of at most 32 tiles are one launch: a graph of an encode of 20
+    tiles followed by two appends of 12 and 3 tiles (the appends start inside
+    a word of the existing stream), replayed over three inputs, equals the
+    oracle's encode of the 35 tiles every time."""
+    plan = hq.Plan(1, 4.0, SEED).set_alpha(0.004)
+    g = torch.Generator().manual_seed(77)
+    xs = [(torch.randn(35, 128, generator=g) * 0.03).to(torch.bfloat16) for _ in range(3)]
+    xin = xs[0].clone().cuda()
+    words, offsets, k = hq.alloc_stream(plan, 35)
+    ws = plan.workspace(20)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(gr, stream=side):
+            enc = hq.encode(plan, xin[:20], ws, out=(words, offsets, k), stream=side)
+            enc = hq.append(plan, enc, xin[20:32], ws, stream=side)
+            enc = hq.append(plan, enc, xin[32:], ws, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        i = rep % 3
+        xin.copy_(xs[i].cuda())
+        gr.replay()
+        got = stream_of(enc)
+        st, ow, oo, ok = orc.encode(1, SEED, 0.004, host_input(xs[i]))
+        assert st == 0
+        assert same(got, (ow, oo, ok)), f"replay {rep} (input {i}) differs from the oracle"
+    assert hq.status_sync(ws) == hq.OK
