@@ -48,18 +48,23 @@ def say(label, what):
 
 
 def whole_stream(hq, orc, lat, x2d: torch.Tensor, bps, dithered=False, tile_base=0, out_dtype=torch.bfloat16,
-                 label=""):
+                 label="", rot=0, compact=False):
     """Calibrate, encode and decode x on the GPU and in the oracle; compare
-    everything bit for bit.  Returns (plan, Encoded, workspace)."""
+    everything bit for bit.  rot: the Haar rotation instead of the RHT;
+    compact: a compact workspace.  Returns (plan, Encoded, workspace)."""
     n = x2d.numel() // 128
     plan = hq.Plan(lat, bps, SEED)
+    if rot:
+        plan.set_rotation(rot)
+    if compact:
+        plan.set_compact_workspace()
     ws = plan.workspace(n)
     say(label, f"{n} tiles: GPU calibration")
     a_gpu, r_gpu = plan.calibrate(x2d, ws, dithered=dithered, tile_base=tile_base)
     xh = host_bits(x2d)
     say(label, f"oracle calibration on {THREADS} threads")
     with orc.threads(THREADS):
-        st, a_orc, r_orc, _ = orc.calibrate(lat, SEED, bps, xh, dithered=dithered, tile_base=tile_base)
+        st, a_orc, r_orc, _ = orc.calibrate(lat, SEED, bps, xh, dithered=dithered, tile_base=tile_base, rot=rot)
     assert st == 0
     assert np.float32(a_gpu) == np.float32(a_orc), (a_gpu, a_orc)
     assert r_gpu == r_orc, (r_gpu, r_orc)
@@ -80,9 +85,10 @@ def whole_stream(hq, orc, lat, x2d: torch.Tensor, bps, dithered=False, tile_base
     del y
     say(label, "oracle encode + decode")
     with orc.threads(THREADS):
-        st, ow, oo, ok = orc.encode(lat, SEED, a_orc, xh, dithered=dithered, tile_base=tile_base)
+        st, ow, oo, ok = orc.encode(lat, SEED, a_orc, xh, dithered=dithered, tile_base=tile_base, rot=rot)
         assert st == 0
-        st, oy = orc.decode(lat, SEED, a_orc, ow, oo, ok, dithered=dithered, tile_base=tile_base, out_dtype=code)
+        st, oy = orc.decode(lat, SEED, a_orc, ow, oo, ok, dithered=dithered, tile_base=tile_base, out_dtype=code,
+                            rot=rot)
         assert st == 0
     assert np.array_equal(offsets, oo), "offsets"
     assert np.array_equal(kk, ok), "Rice parameters"
@@ -137,6 +143,25 @@ def test_kv_8x8x32768_d4_dithered(hq, orc, which):
     whole_stream(hq, orc, 2, t, 2.0, dithered=True, tile_base=0, label=f"KV 8x8x32768 {which} D4 2")
     del k, v, t
     torch.cuda.empty_cache()
+
+
+def test_kv_8x8x32768_k_haar(hq, orc):
+    """The K tensor of one layer with the Haar rotation instead of the RHT
+    (D4, 2 bps, dither): alpha, offsets, k, words and reconstruction of the
+    whole stream equal the oracle's."""
+    from lattice_vq_entropy_amd import workloads as W
+    k, v, q = W.c3("cuda")
+    del v, q
+    whole_stream(hq, orc, 2, k, 2.0, dithered=True, tile_base=0, label="KV 8x8x32768 K D4 2 Haar", rot=1)
+    del k
+    torch.cuda.empty_cache()
+
+
+def test_weight_4096x4096_e8_compact_workspace(hq, orc):
+    """The headline weight (E8, 4 bps) with a compact workspace: the same
+    whole-stream equality (no chunk there exceeds its rate-sized slot)."""
+    from lattice_vq_entropy_amd import workloads as W
+    whole_stream(hq, orc, 3, W.c2("cuda"), 4.0, label="4096x4096 E8 4 compact", compact=True)
 
 
 def test_kv_8x8x32768_bias(hq):
