@@ -178,3 +178,29 @@ def test_compact_equals_full_slots_and_noalloc(hq):
     assert_mixed(b[1], 0.5)
     for p, q, r in zip(a, b, c):
         assert np.array_equal(p, q) and np.array_equal(p, r)
+
+
+def test_reencoded_chunks_respect_the_capacity(hq):
+    """Re-encoded chunks write no word at or past cap_words: with the buffer
+    filled with a sentinel and cap_words below the stream's need, the encode
+    reports HQ_ERR_CAPACITY and every word from cap_words on keeps the
+    sentinel; with cap_words equal to the need, the words past it do."""
+    x = rows_input(24, 1024, 324).cuda()  # 192 tiles, 6 chunks
+    plan = hq.Plan(3, 0.5, SEED).set_compact_workspace().set_alpha(0.0021)
+    n = x.numel() // 128
+    ws = plan.workspace(n)
+    ref = hq.encode(plan, x, ws)
+    assert hq.status_sync(ws) == hq.OK
+    need = ref.used_words()
+    assert_mixed(stream_of(ref)[1], 0.5)
+    sentinel = -0x21524111
+    words, offsets, k = hq.alloc_stream(plan, n)
+    for cap in (need - 1, need // 2, need // 3 + 5):
+        words.fill_(sentinel)
+        hq.encode(plan, x, ws, out=(words, offsets, k), cap_words=cap)
+        assert hq.status_sync(ws) == hq.ERR_CAPACITY
+        assert bool((words[cap:] == sentinel).all()), f"words past cap_words = {cap} written"
+    words.fill_(sentinel)
+    hq.encode(plan, x, ws, out=(words, offsets, k), cap_words=need)
+    assert hq.status_sync(ws) == hq.OK
+    assert torch.equal(words[:need], ref.words[:need]) and bool((words[need:] == sentinel).all())
